@@ -1,0 +1,109 @@
+"""Greedy acceptance (oracle side).
+
+Greedy verification, as the single-RTX-3090 DFlash note runs it (section
+"Architecture": greedy verify only; section "Next steps": sampling is not yet
+supported), accepts a draft token exactly when it equals the target model's
+argmax at the draft's parent.  Over a token tree the step keeps the longest
+root path whose drafts are all accepted, then appends one bonus token: the
+target's argmax at the last node of that path.  The note's DDTree verifier
+reads budget+1 logits rows for this (section "Key breakthroughs", the
+verify-logits buffer fix).
+
+Conventions the pages leave open, read here as:
+
+* ties in a row's maximum go to the lowest token index;
+* among equally deep accepted nodes the one with the smallest node index
+  wins (the generators keep sibling tokens distinct, so with real trees the
+  accepted path is unique);
+* ``a`` (the accept length returned) counts accepted drafts, so ``a + 1``
+  tokens are committed; node 0's draft id is the already committed token and
+  is ignored.
+"""
+import numpy as np
+
+
+def argmax_first(row) -> int:
+    """Lowest index holding the maximum of a 1-D row (compared exactly)."""
+    row = np.asarray(row, dtype=np.float64)
+    m = row.max()
+    return int(np.flatnonzero(row == m)[0])
+
+
+def _depths(parent):
+    n = len(parent)
+    depth = [0] * n
+    for i in range(1, n):
+        depth[i] = depth[parent[i]] + 1
+    return depth
+
+
+def _result(best, am, draft, parent, n):
+    path = []
+    j = best
+    while j >= 0:
+        path.append(j)
+        j = int(parent[j]) if j > 0 else -1
+    path.reverse()
+    a = len(path) - 1
+    tokens = [int(draft[path[j]]) for j in range(1, a + 1)] + [int(am[path[a]])]
+    path_out = np.full(n, -1, dtype=np.int32)
+    tok_out = np.full(n, -1, dtype=np.int32)
+    path_out[:a + 1] = path
+    tok_out[:a + 1] = tokens
+    return a, path_out, tok_out
+
+
+def accept_walk(am, draft, parent):
+    """Forward walk in node order: node i is accepted iff its parent is and
+    ``draft[i] == am[parent[i]]``.  Returns ``(a, path, tokens)`` with ``path``
+    and ``tokens`` padded to N with -1."""
+    parent = [int(p) for p in parent]
+    n = len(parent)
+    acc = [False] * n
+    acc[0] = True
+    for i in range(1, n):
+        p = parent[i]
+        acc[i] = acc[p] and int(draft[i]) == int(am[p])
+    depth = _depths(parent)
+    best = 0
+    for i in range(1, n):
+        if acc[i] and depth[i] > depth[best]:
+            best = i
+    return _result(best, am, draft, parent, n)
+
+
+def accept_bruteforce(am, draft, parent):
+    """Independent check of ``accept_walk``: enumerate every root-to-node path,
+    keep those whose every edge is accepted, take the longest (ties: the
+    smallest end node)."""
+    parent = [int(p) for p in parent]
+    n = len(parent)
+    best, best_len = 0, 0
+    for end in range(n):
+        chain = []
+        j = end
+        while j >= 0:
+            chain.append(j)
+            j = parent[j] if j > 0 else -1
+        chain.reverse()
+        ok = all(int(draft[c]) == int(am[p]) for p, c in zip(chain[:-1], chain[1:]))
+        if ok and len(chain) - 1 > best_len:
+            best, best_len = end, len(chain) - 1
+    return _result(best, am, draft, parent, n)
+
+
+def greedy_accept(logits64, draft_ids, parent):
+    """Whole batch.  ``logits64``: float64 ``[B, N, V]`` (exactly widened).
+
+    Returns ``am [B, N]``, ``accept_len [B]``, ``path [B, N]``, ``tokens [B, N]``.
+    """
+    B, N, _ = logits64.shape
+    am = np.empty((B, N), dtype=np.int32)
+    acc = np.empty(B, dtype=np.int32)
+    path = np.empty((B, N), dtype=np.int32)
+    tok = np.empty((B, N), dtype=np.int32)
+    for b in range(B):
+        for i in range(N):
+            am[b, i] = argmax_first(logits64[b, i])
+        acc[b], path[b], tok[b] = accept_walk(am[b], draft_ids[b], parent[b])
+    return am, acc, path, tok
