@@ -1,0 +1,271 @@
+"""Benchmark of one verify step on one MI355X.
+
+A step is the whole verify path for one layer over one batch of seeded
+synthetic inputs already resident in HBM: ``sv_verify_attn`` (tree/chain
+masked GQA attention over the KV cache), ``sv_greedy_accept`` (vocab argmax +
+acceptance walk) and ``sv_kv_compact`` (in-place compaction).  Inputs rotate
+over enough device copies (>= 1 GiB) that the 256 MB Infinity Cache cannot
+serve the KV cache from one step to the next.
+
+Prints one JSON line.  ``value`` is verified draft tokens per second
+(sum over sequences of N - 1 draft rows, per step time).  ``roofline``
+reports the verify-attention call (split kernel + merge kernel), timed with
+HIP events on the launch stream around a graph replay of `steps` calls
+against the 8 TB/s HBM peak, using the algorithmic bytes of the call: every KV
+row of the key range read once, plus q, out and lse.  ``cpu_baseline`` times
+the fp64 CPU oracle on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "verified draft tokens/s per verify step + achieved HBM GB/s (% of MI355X peak)"
+WORKLOADS = {"C1": "C1", "C2": "C2", "C3": "C3", "C4": "C4", "C5": "C5"}
+DEFAULT_CONFIG = "C2"        # chain verify, GQA 24/4, head dim 256, 4096 cached tokens
+
+
+def kv_bytes_per_position(cfg):
+    D = cfg.head_dim
+    if cfg.kv_dtype == "f32":
+        return 2 * D * 4
+    if cfg.kv_dtype == "bf16":
+        return 2 * D * 2
+    return 2 * (D // 2 + (D // 32) * 2)          # 4-bit codes + fp16 scales, K and V
+
+
+def attn_algorithmic_bytes(cfg, ctx_lens):
+    qb = 4 if cfg.q_dtype == "f32" else 2
+    rows = int(np.sum(ctx_lens + cfg.n_nodes))
+    kv = rows * cfg.n_kv_heads * kv_bytes_per_position(cfg)
+    q_out = 2 * cfg.batch * cfg.n_nodes * cfg.n_q_heads * cfg.head_dim * qb
+    lse = cfg.batch * cfg.n_nodes * cfg.n_q_heads * 4
+    return kv + q_out + lse
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "draft_token_verification_sv_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, per_launch_bytes):
+    """HBM bytes per attention call from the committed rocprofv3 counter runs,
+    if they were taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "attn_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(workload)
+    if not ent or ent.get("source_hash") != source_hash():
+        return None
+    return ent.get("bytes_per_call")
+
+
+def cpu_baseline(cfg_key, seconds):
+    """The oracle (unchanged) on a sample of the same workload: whole verify
+    steps on the host cores, repeated for about `seconds`."""
+    import oracle
+    import workloads
+    cfg = workloads.CONFIGS[cfg_key]
+    case = workloads.make_case(cfg, seed=1)
+    lg = case.logits.astype(np.float64) if cfg.logits_dtype == "f32" else oracle.widen_bf16(case.logits)
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.verify_attention(case)
+        am, acc, path, tok = oracle.greedy_accept(lg, case.draft_ids, case.parent)
+        arrs = [case.k[None], case.v[None]]
+        if case.k_scale is not None:
+            arrs += [case.k_scale[None], case.v_scale[None]]
+        oracle.compact_cache(arrs, ctx_lens=case.ctx_lens, path=path, accept_len=acc,
+                             page_table=case.page_table if cfg.paged else None, page_size=cfg.page_size)
+        steps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    drafts = cfg.batch * (cfg.n_nodes - 1)
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    return {"value": drafts * steps / dt, "unit": "verified draft tokens/s", "cores": int(blas),
+            "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{steps} whole verify steps of the {cfg.name} workload (attention, argmax + walk, "
+                      f"compaction) in {dt:.1f} s, fp64 numpy"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate-bytes", type=float, default=1.1 * 2 ** 30)
+    ap.add_argument("--target-wgs", type=int, default=0, help="attention grid target (0: library default)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the verify path shards by sequence or KV head with no exchange, see the design notes",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    import draft_token_verification_sv_amd as sv
+
+    if args.target_wgs:
+        sv.set_option(sv.SV_OPT_ATTN_TARGET_WGS, args.target_wgs)
+    cfg = workloads.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    case = workloads.make_case(cfg, seed=1)
+
+    def up(x, kind):
+        x = np.ascontiguousarray(x)
+        if kind == "bf16":
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        if kind == "u16":
+            return torch.from_numpy(x.view(np.int16)).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    qk = "bf16" if cfg.q_dtype == "bf16" else "f32"
+    base = {
+        "q": up(case.q, qk),
+        "logits": up(case.logits, "bf16" if cfg.logits_dtype == "bf16" else "f32"),
+    }
+    if cfg.kv_dtype == "q4":
+        base.update(k=up(case.k, "u8"), v=up(case.v, "u8"), ks=up(case.k_scale, "u16"), vs=up(case.v_scale, "u16"))
+    else:
+        kk = "bf16" if cfg.kv_dtype == "bf16" else "f32"
+        base.update(k=up(case.k, kk), v=up(case.v, kk))
+    ctx = up(case.ctx_lens.astype(np.int32), "i32")
+    parent = up(case.parent.astype(np.int32), "i32")
+    drafts = up(case.draft_ids.astype(np.int32), "i32")
+    pt = up(case.page_table.astype(np.int32), "i32") if cfg.paged else None
+    max_ctx = int(case.ctx_lens.max())
+    per_copy = sum(t.numel() * t.element_size() for t in base.values())
+    n_copies = max(1, int(np.ceil(args.rotate_bytes / per_copy)))
+    copies = [base] + [{k: t.clone() for k, t in base.items()} for _ in range(n_copies - 1)]
+
+    B, N, Hq, D = cfg.batch, cfg.n_nodes, cfg.n_q_heads, cfg.head_dim
+    kvs = [sv.KVCache(k=c["k"], v=c["v"], k_scale=c.get("ks"), v_scale=c.get("vs"), page_table=pt)
+           for c in copies]
+    outs = [torch.empty_like(base["q"]) for _ in range(2)]
+    lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev)
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    path = torch.empty((B, N), dtype=torch.int32, device=dev)
+    tok = torch.empty((B, N), dtype=torch.int32, device=dev)
+    new_lens = torch.empty(B, dtype=torch.int32, device=dev)
+    ws_a = torch.empty(sv.verify_attn_workspace_size(kvs[0], B, N, Hq, max_ctx), dtype=torch.uint8, device=dev)
+    ws_g = torch.zeros(sv.greedy_accept_workspace_size(B, N, cfg.vocab), dtype=torch.uint8, device=dev)
+
+    def attn(i):
+        c, kv = copies[i % n_copies], kvs[i % n_copies]
+        sv.verify_attn(kv, c["q"], ctx, parent, max_ctx, out=outs[i & 1], lse=lse, workspace=ws_a)
+
+    def accept(i):
+        sv.greedy_accept(copies[i % n_copies]["logits"], drafts, parent, workspace=ws_g,
+                         outputs=(acc, path, tok, None))
+
+    def compact(i):
+        sv.kv_compact(kvs[i % n_copies], ctx, max_ctx, path, acc, new_lens=new_lens)
+
+    def step(i):
+        attn(i)
+        accept(i)
+        compact(i)
+
+    # warm-up: eager steps (first launches, code objects, caches)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # The timed work is replayed from HIP graphs (the launch path a serving loop
+    # uses); each graph holds exactly `steps` consecutive calls over the rotation.
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(args.steps):
+                fn(args.warmup + i)
+        torch.cuda.synchronize()
+        return g
+
+    def timed(g):
+        s = torch.cuda.current_stream(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g.replay()                       # untimed replay (graph upload)
+        torch.cuda.synchronize()
+        e0.record(s)
+        g.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    g_step = capture(step)
+    total_ms = timed(g_step)
+    g_attn = capture(attn)
+    attn_total_ms = timed(g_attn)
+    g_acc = capture(accept)
+    accept_us = timed(g_acc) / args.steps * 1e3
+    g_cmp = capture(compact)
+    compact_us = timed(g_cmp) / args.steps * 1e3
+    attn_ms = np.array([attn_total_ms / args.steps])
+
+    ms_per_step = total_ms / args.steps
+    drafts_per_step = B * (N - 1)
+    value = drafts_per_step / (ms_per_step / 1e3)
+    attn_bytes = attn_algorithmic_bytes(cfg, case.ctx_lens)
+    attn_us = float(np.mean(attn_ms) * 1e3)
+    achieved = attn_bytes / (attn_us * 1e-6) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "verified draft tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.q_dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": B, "n_q_heads": Hq, "n_kv_heads": cfg.n_kv_heads,
+                   "head_dim": D, "n_nodes": N, "tree": cfg.tree, "kv": cfg.kv_dtype,
+                   "kv_layout": "paged16" if cfg.paged else "contiguous",
+                   "ctx": int(cfg.ctx) if not cfg.ctx_hi else [int(cfg.ctx), int(cfg.ctx_hi)],
+                   "vocab": cfg.vocab, "rotation_copies": n_copies},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(cfg.name, attn_bytes),
+                     "kernel": "sv_verify_attn (split + merge kernels)",
+                     "algorithmic_bytes": int(attn_bytes)},
+        "breakdown_us": {"verify_attn": round(attn_us, 2), "greedy_accept": round(accept_us, 2),
+                         "kv_compact": round(compact_us, 2)},
+        "accepted_tokens_per_step": None,
+    }
+    a_host = acc.cpu().numpy()
+    rec["accepted_tokens_per_step"] = int(np.sum(a_host + 1))
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

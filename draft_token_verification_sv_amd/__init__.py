@@ -1,0 +1,290 @@
+"""Python binding of the gfx950 verify-step library (``libsv.so``).
+
+Argument marshalling only: every step of the verify path runs in the HIP
+kernels behind the C ABI of ``include/sv.h``.  PyTorch supplies device memory
+and the current stream.  Importing this package loads the library and raises
+if it has not been built; there is no fallback implementation.
+
+    kv = KVCache.contiguous(k, v)                 # [B, Hkv, cap, D] bf16/fp32
+    out, lse = verify_attn(kv, q, ctx_lens, parent, max_ctx)
+    acc, path, tokens, am = greedy_accept(logits, draft_ids, parent)
+    new_lens = kv_compact(kv, ctx_lens, max_ctx, path, acc)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "SV_F32", "SV_BF16", "SV_Q4", "SVError", "KVCache", "lib", "library_path",
+    "verify_attn", "verify_attn_workspace_size", "greedy_accept", "greedy_accept_workspace_size",
+    "kv_compact", "set_option", "SV_OPT_ATTN_TARGET_WGS", "SV_OPT_ARGMAX_CHUNK",
+]
+
+SV_F32, SV_BF16, SV_Q4 = 0, 1, 2
+SV_OPT_ATTN_TARGET_WGS, SV_OPT_ARGMAX_CHUNK = 1, 2
+
+library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsv.so")
+if not os.path.exists(library_path):
+    raise ImportError(
+        f"{library_path} is missing: build it with `python draft_token_verification_sv_amd/build.py` "
+        "(there is no CPU fallback)")
+lib = ctypes.CDLL(library_path)
+
+
+class _KvDesc(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("capacity", ctypes.c_int64),
+        ("n_seqs", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p),
+        ("layer_stride", ctypes.c_int64),
+        ("scale_layer_stride", ctypes.c_int64),
+    ]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+lib.sv_verify_attn_workspace_size.restype = ctypes.c_size_t
+lib.sv_verify_attn_workspace_size.argtypes = [ctypes.POINTER(_KvDesc), _I, _I, _I, _I]
+lib.sv_verify_attn.restype = _I
+lib.sv_verify_attn.argtypes = [ctypes.POINTER(_KvDesc), _I, _I, _I, _P, _I, _P, _I, _P,
+                               ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]
+lib.sv_greedy_accept_workspace_size.restype = ctypes.c_size_t
+lib.sv_greedy_accept_workspace_size.argtypes = [_I, _I, _I]
+lib.sv_greedy_accept.restype = _I
+lib.sv_greedy_accept.argtypes = [_I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+lib.sv_kv_compact.restype = _I
+lib.sv_kv_compact.argtypes = [ctypes.POINTER(_KvDesc), _I, _I, _I, _P, _I, _P, _P, _P, _P]
+lib.sv_error_string.restype = ctypes.c_char_p
+lib.sv_error_string.argtypes = [_I]
+lib.sv_last_hip_error.restype = _I
+lib.sv_set_option.restype = _I
+lib.sv_set_option.argtypes = [_I, _I]
+
+
+class SVError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        msg = lib.sv_error_string(code).decode()
+        if code == -4:
+            msg += f" (hipError {lib.sv_last_hip_error()})"
+        super().__init__(f"{where}: {msg} [{code}]")
+        self.code = code
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != 0:
+        raise SVError(rc, where)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SV_F32
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+@dataclass
+class KVCache:
+    """Device KV cache views (no copies).
+
+    Contiguous: ``k``/``v`` are ``[B, Hkv, cap, D]`` (fp32/bf16) or
+    ``[B, Hkv, cap, D/2]`` uint8 4-bit codes with ``k_scale``/``v_scale``
+    ``[B, Hkv, cap, D/32]`` (fp16, as int16/uint16/float16).  Paged: the same
+    with the leading two axes ``[pages, Hkv, page_size, ...]`` and a
+    ``page_table`` int32 ``[B, max_pages]``.  An extra leading layer axis makes
+    a multi-layer cache (``kv_compact`` walks every layer; attention reads
+    layer ``layer``).
+    """
+    k: torch.Tensor
+    v: torch.Tensor
+    k_scale: Optional[torch.Tensor] = None
+    v_scale: Optional[torch.Tensor] = None
+    page_table: Optional[torch.Tensor] = None
+    head_dim: int = 0
+
+    @property
+    def q4(self) -> bool:
+        return self.k.dtype == torch.uint8
+
+    @property
+    def n_layers(self) -> int:
+        return self.k.shape[0] if self.k.dim() == 5 else 1
+
+    def desc(self, layer: int = 0) -> _KvDesc:
+        k, v = self.k, self.v
+        for t in (k, v, self.k_scale, self.v_scale, self.page_table):
+            if t is not None and not t.is_contiguous():
+                raise ValueError("KV tensors must be contiguous")
+        multi = k.dim() == 5
+        kl = k[layer] if multi else k
+        vl = v[layer] if multi else v
+        d = _KvDesc()
+        if self.q4:
+            if self.k_scale is None or self.v_scale is None:
+                raise ValueError("4-bit cache needs k_scale and v_scale")
+            d.dtype = SV_Q4
+            d.head_dim = kl.shape[-1] * 2
+            ks = self.k_scale[layer] if multi else self.k_scale
+            vs = self.v_scale[layer] if multi else self.v_scale
+            d.k_scale, d.v_scale = ks.data_ptr(), vs.data_ptr()
+            d.scale_layer_stride = (self.k_scale.stride(0) * self.k_scale.element_size()) if multi else 0
+        else:
+            d.dtype = _dtype_code(kl)
+            d.head_dim = kl.shape[-1]
+            d.k_scale = d.v_scale = None
+            d.scale_layer_stride = 0
+        if self.head_dim and self.head_dim != d.head_dim:
+            raise ValueError("head_dim mismatch")
+        d.n_kv_heads = kl.shape[1]
+        d.k, d.v = kl.data_ptr(), vl.data_ptr()
+        d.layer_stride = (k.stride(0) * k.element_size()) if multi else 0
+        if self.page_table is None:
+            d.page_size = 0
+            d.capacity = kl.shape[2]
+            d.n_seqs = kl.shape[0]
+            d.max_pages_per_seq = 0
+            d.page_table = None
+        else:
+            if self.page_table.dtype != torch.int32:
+                raise TypeError("page_table must be int32")
+            d.page_size = kl.shape[2]
+            d.capacity = kl.shape[0]
+            d.n_seqs = 0
+            d.max_pages_per_seq = self.page_table.shape[1]
+            d.page_table = self.page_table.data_ptr()
+        return d
+
+    @classmethod
+    def contiguous(cls, k, v, k_scale=None, v_scale=None):
+        return cls(k=k, v=v, k_scale=k_scale, v_scale=v_scale)
+
+    @classmethod
+    def paged(cls, k, v, page_table, k_scale=None, v_scale=None):
+        return cls(k=k, v=v, k_scale=k_scale, v_scale=v_scale, page_table=page_table)
+
+
+_ws_cache: dict = {}
+
+
+def _workspace(kind: str, dev: torch.device, nbytes: int, zero: bool) -> torch.Tensor:
+    key = (kind, dev)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        size = max(nbytes, 256)
+        buf = (torch.zeros if zero else torch.empty)(size, dtype=torch.uint8, device=dev)
+        _ws_cache[key] = buf
+    return buf
+
+
+def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.int32 or not t.is_contiguous() or not t.is_cuda:
+        raise TypeError(f"{name} must be a contiguous int32 device tensor")
+    return t
+
+
+def verify_attn_workspace_size(kv: KVCache, batch: int, n_nodes: int, n_q_heads: int, max_ctx: int) -> int:
+    d = kv.desc()
+    return int(lib.sv_verify_attn_workspace_size(ctypes.byref(d), batch, n_nodes, n_q_heads, max_ctx))
+
+
+def verify_attn(kv: KVCache, q: torch.Tensor, ctx_lens: torch.Tensor, parent: torch.Tensor,
+                max_ctx: int, sm_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                workspace: Optional[torch.Tensor] = None, layer: int = 0):
+    """Masked GQA attention of the verify rows.  ``q`` ``[B, N, Hq, D]``."""
+    if q.dim() != 4 or not q.is_contiguous() or not q.is_cuda:
+        raise ValueError("q must be a contiguous [B, N, Hq, D] device tensor")
+    B, N, Hq, D = q.shape
+    _i32(ctx_lens, "ctx_lens")
+    _i32(parent, "parent")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, N, Hq), dtype=torch.float32, device=q.device)
+    d = kv.desc(layer)
+    need = int(lib.sv_verify_attn_workspace_size(ctypes.byref(d), B, N, Hq, int(max_ctx)))
+    if workspace is None:
+        workspace = _workspace("attn", q.device, need, zero=False)
+    rc = lib.sv_verify_attn(ctypes.byref(d), B, N, Hq, _ptr(ctx_lens), int(max_ctx), _ptr(q),
+                            _dtype_code(q), _ptr(parent), float(sm_scale), _ptr(out), _ptr(lse),
+                            _ptr(workspace), workspace.numel() * workspace.element_size(),
+                            _stream(q.device))
+    _check(rc, "sv_verify_attn")
+    return out, lse
+
+
+def greedy_accept_workspace_size(batch: int, n_nodes: int, vocab: int) -> int:
+    return int(lib.sv_greedy_accept_workspace_size(batch, n_nodes, vocab))
+
+
+def greedy_accept(logits: torch.Tensor, draft_ids: torch.Tensor, parent: torch.Tensor,
+                  want_argmax: bool = True, workspace: Optional[torch.Tensor] = None, outputs=None):
+    """Greedy acceptance.  ``logits`` ``[B, N, V]`` fp32/bf16.
+
+    Returns ``(accept_len [B], path [B, N], tokens [B, N], argmax [B, N] or None)``.
+    """
+    if logits.dim() != 3 or not logits.is_contiguous() or not logits.is_cuda:
+        raise ValueError("logits must be a contiguous [B, N, V] device tensor")
+    B, N, V = logits.shape
+    _i32(draft_ids, "draft_ids")
+    _i32(parent, "parent")
+    dev = logits.device
+    if outputs is None:
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        path = torch.empty((B, N), dtype=torch.int32, device=dev)
+        tok = torch.empty((B, N), dtype=torch.int32, device=dev)
+        am = torch.empty((B, N), dtype=torch.int32, device=dev) if want_argmax else None
+    else:
+        acc, path, tok, am = outputs
+    need = int(lib.sv_greedy_accept_workspace_size(B, N, V))
+    if workspace is None:
+        workspace = _workspace("accept", dev, need, zero=True)
+    rc = lib.sv_greedy_accept(B, N, V, _ptr(logits), _dtype_code(logits), _ptr(draft_ids), _ptr(parent),
+                              _ptr(acc), _ptr(path), _ptr(tok), _ptr(am), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(rc, "sv_greedy_accept")
+    return acc, path, tok, am
+
+
+def kv_compact(kv: KVCache, ctx_lens: torch.Tensor, max_ctx: int, path: torch.Tensor,
+               accept_len: torch.Tensor, n_layers: Optional[int] = None,
+               new_lens: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """In-place compaction of the accepted rows (every layer of ``kv``)."""
+    _i32(ctx_lens, "ctx_lens")
+    _i32(path, "path")
+    _i32(accept_len, "accept_len")
+    B, N = path.shape
+    if new_lens is None:
+        new_lens = torch.empty(B, dtype=torch.int32, device=path.device)
+    d = kv.desc(0)
+    L = kv.n_layers if n_layers is None else n_layers
+    rc = lib.sv_kv_compact(ctypes.byref(d), L, B, N, _ptr(ctx_lens), int(max_ctx), _ptr(path),
+                           _ptr(accept_len), _ptr(new_lens), _stream(path.device))
+    _check(rc, "sv_kv_compact")
+    return new_lens
+
+
+def set_option(option: int, value: int) -> int:
+    return int(lib.sv_set_option(option, value))

@@ -1,0 +1,273 @@
+// Vector-ALU verify attention (fp32 arithmetic) and the split merge.
+//
+// The VALU kernel serves packed row blocks of fewer than 16 rows with bf16
+// queries (single-row decode, small GQA groups) and every fp32-query call.  It
+// stages each KV tile in LDS as fp32 (4-bit rows dequantised as d * (n - 8)),
+// keeps up to 16 query rows in LDS, and gives each row 16 threads: the
+// threads of a row split the tile's positions for the scores and the head
+// dimension for the output accumulation.  The tree mask is the ancestor-set
+// mask built in LDS from the parent array [single-RTX-3090 DFlash note,
+// "From autoregressive to DDTree"; causal mask aligned to the end of the keys,
+// xdnf.cn notes section 5.3].  Partials use the same layout as the matrix-core
+// kernel.
+//
+// The merge combines the splits of every row with the log-sum-exp rule
+//   M = max_s m_s,  out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
+//   lse = ln 2 * (M + log2 sum_s 2^(m_s - M) l_s)
+// (m in log2 units), and writes the output in the query dtype.
+#include "device_common.h"
+
+namespace sv {
+namespace {
+
+constexpr int kRowsV = 16;
+
+template <int KVT>
+__device__ __forceinline__ void load_row_chunk_f32(float *dst, const uint8_t *base, const uint8_t *sbase,
+                                                   int64_t ri, int chunk, int D) {
+    // one 16-byte chunk of codes / values of row ri, widened to fp32 into dst
+    if constexpr (KVT == SV_F32) {
+        const f32x4 v = *(const f32x4 *)(base + ri * (D * 4) + chunk * 16);
+        dst[0] = v[0]; dst[1] = v[1]; dst[2] = v[2]; dst[3] = v[3];
+    } else if constexpr (KVT == SV_BF16) {
+        const u32x4 v = *(const u32x4 *)(base + ri * (D * 2) + chunk * 16);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            dst[2 * w] = bf16_bits_to_f32(v[w] & 0xFFFFu);
+            dst[2 * w + 1] = bf16_bits_to_f32(v[w] >> 16);
+        }
+    } else {
+        // a 16-byte chunk of codes is one 32-value block
+        const u32x4 v = *(const u32x4 *)(base + ri * (D / 2) + chunk * 16);
+        const float d = fp16_bits_to_f32(*(const uint16_t *)(sbase + ri * ((D / 32) * 2) + chunk * 2));
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                dst[8 * w + t] = (float)(int)((v[w] >> (4 * t)) & 15u) * d - 8.f * d;
+    }
+}
+
+template <int D, int KVT, bool QF32>
+__global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
+    constexpr int T = kValuTileElems / D;          // 32, 64 or 128 positions per tile
+    constexpr int DP = D + 1;                      // padded K row (bank spread)
+    constexpr int VPC = (KVT == SV_F32) ? 4 : (KVT == SV_BF16 ? 8 : 32);  // values per chunk
+    constexpr int CPR = D / VPC;                   // chunks per row
+    __shared__ float Ks[T * DP];
+    __shared__ float Vs[T * D];
+    __shared__ float Qs[kRowsV * D];
+    __shared__ float Ps[kRowsV * T];
+    __shared__ int par_s[64];
+    __shared__ uint64_t anc_s[64];
+
+    const int id = blockIdx.x;
+    const int xcd = id & 7, k8 = id >> 3;
+    const int rb = k8 % p.n_rowblocks;
+    const int u = (k8 / p.n_rowblocks) * 8 + xcd;
+    if (u >= p.B * p.Hkv * p.n_splits) return;
+    const int s = u % p.n_splits;
+    const int bh = u / p.n_splits;
+    const int kvh = bh % p.Hkv, b = bh / p.Hkv;
+
+    const int N = p.N, G = p.G, R = p.R;
+    const int ctx = clamp_ctx(p.ctx_lens[b], p.max_ctx);
+    const int L = ctx + N;
+    const int p0 = s * p.split_len;
+    if (p0 >= L) return;
+    const int p1 = min(p0 + p.split_len, L);
+
+    const int tid = threadIdx.x;
+    const int r = tid >> 4, j = tid & 15;           // row in block, thread in row
+    const int rglob = rb * kRowsV + r;
+    const bool row_ok = r < p.rows_per_block && rglob < R;
+
+    if (tid < N) par_s[tid] = p.parent[(int64_t)b * N + tid];
+    __syncthreads();
+    if (tid < N) anc_s[tid] = ancestor_bits(par_s, tid);
+
+    // query rows -> LDS (fp32)
+    for (int e = tid; e < kRowsV * D; e += 256) {
+        const int rr = e / D, d = e % D;
+        const int rg = rb * kRowsV + rr;
+        float val = 0.f;
+        if (rr < p.rows_per_block && rg < R) {
+            const int n = rg / G, g = rg % G;
+            const int64_t qi = (((int64_t)b * N + n) * p.Hq + (int64_t)kvh * G + g) * D + d;
+            val = QF32 ? ((const float *)p.q)[qi] : bf16_bits_to_f32(((const uint16_t *)p.q)[qi]);
+        }
+        Qs[e] = val;
+    }
+    __syncthreads();
+    const uint64_t anc = row_ok ? anc_s[rglob / G] : 0ull;
+
+    float o[D / 16];
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) o[k] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const uint8_t *kb = (const uint8_t *)p.kv.k, *vb = (const uint8_t *)p.kv.v;
+    const uint8_t *ksb = (const uint8_t *)p.kv.ks, *vsb = (const uint8_t *)p.kv.vs;
+
+#pragma unroll 1
+    for (int tp = p0; tp < p1; tp += T) {
+        // stage K and V rows [tp, tp + T) as fp32
+        for (int c = tid; c < T * CPR; c += 256) {
+            const int row = c / CPR, ch = c % CPR;
+            const int pos = tp + row;
+            float kv8[VPC], vv8[VPC];
+            bool ok = false;
+            if (pos < p1) {
+                const int64_t ri = kv_row_index(p.kv, b, p.Hkv, kvh, pos);
+                if (ri >= 0) {
+                    load_row_chunk_f32<KVT>(kv8, kb, ksb, ri, ch, D);
+                    load_row_chunk_f32<KVT>(vv8, vb, vsb, ri, ch, D);
+                    ok = true;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < VPC; ++e) {
+                Ks[row * DP + ch * VPC + e] = ok ? kv8[e] : 0.f;
+                Vs[row * D + ch * VPC + e] = ok ? vv8[e] : 0.f;
+            }
+        }
+        __syncthreads();
+
+        // scores for this thread's positions j, j+16, ...
+        float sc[T / 16];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < T / 16; ++i) {
+            const int pt = j + 16 * i;
+            const int pos = tp + pt;
+            float acc = 0.f;
+#pragma unroll 8
+            for (int d = 0; d < D; ++d) acc = __builtin_fmaf(Qs[r * D + d], Ks[pt * DP + d], acc);
+            const int rel = pos - ctx;          // draft index (negative: cache row)
+            bool vis = row_ok && pos < p1;
+            if (rel >= 0) vis = vis && (((anc >> (rel & 63)) & 1ull) != 0ull);
+            sc[i] = vis ? acc * p.scale_log2 : -INFINITY;
+            tmax = fmaxf(tmax, sc[i]);
+        }
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, m, 64));
+        const float m_new = fmaxf(m_run, tmax);
+        const float mu = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - mu);
+        float lt = 0.f;
+#pragma unroll
+        for (int i = 0; i < T / 16; ++i) {
+            const float pr = exp2f(sc[i] - mu);
+            Ps[r * T + j + 16 * i] = pr;
+            lt += pr;
+        }
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) lt += __shfl_xor(lt, m, 64);
+        l_run = l_run * alpha + lt;
+        m_run = m_new;
+        __syncthreads();
+
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k) {
+            const int d = j + 16 * k;
+            float acc = o[k] * alpha;
+#pragma unroll 8
+            for (int pt = 0; pt < T; ++pt) acc = __builtin_fmaf(Ps[r * T + pt], Vs[pt * D + d], acc);
+            o[k] = acc;
+        }
+        __syncthreads();
+    }
+
+    if (!row_ok) return;
+    const int64_t part = ((int64_t)b * p.Hkv + kvh) * p.n_splits + s;
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) p.part_o[(part * R + rglob) * D + j + 16 * k] = o[k];
+    if (j == 0) {
+        p.part_ml[(part * R + rglob) * 2 + 0] = m_run;
+        p.part_ml[(part * R + rglob) * 2 + 1] = l_run;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
+    constexpr int RPB = 256 / D;
+    const int row = blockIdx.x * RPB + (int)threadIdx.x / D;
+    const int d = threadIdx.x % D;
+    const int rows = p.B * p.N * p.Hq;
+    if (row >= rows) return;
+    const int h = row % p.Hq;
+    const int n = (row / p.Hq) % p.N;
+    const int b = row / (p.Hq * p.N);
+    const int kvh = h / p.G, g = h % p.G;
+    const int r = n * p.G + g;
+    const int ctx = clamp_ctx(p.ctx_lens[b], p.max_ctx);
+    const int L = ctx + p.N;
+    const int ns = min(p.n_splits, (L + p.split_len - 1) / p.split_len);
+    const int64_t base = ((int64_t)b * p.Hkv + kvh) * p.n_splits;
+
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, p.part_ml[((base + s) * p.R + r) * 2]);
+    float acc = 0.f, lsum = 0.f;
+    for (int s = 0; s < ns; ++s) {
+        const int64_t pr = (base + s) * p.R + r;
+        const float ms = p.part_ml[pr * 2];
+        const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+        lsum += w * p.part_ml[pr * 2 + 1];
+        acc += w * p.part_o[pr * D + d];
+    }
+    const float v = acc / lsum;
+    const int64_t oi = (((int64_t)b * p.N + n) * p.Hq + h) * D + d;
+    if (p.q_f32) ((float *)p.out)[oi] = v;
+    else ((uint16_t *)p.out)[oi] = (uint16_t)f32_to_bf16_bits(v);
+    if (d == 0 && p.lse != nullptr)
+        p.lse[((int64_t)b * p.N + n) * p.Hq + h] = (M + log2f(lsum)) * 0.69314718055994530942f;
+}
+
+template <int D, int KVT>
+hipError_t launch_valu_t(const AttnParams &p, hipStream_t st) {
+    const int units = p.B * p.Hkv * p.n_splits;
+    const int grid = ((units + 7) / 8) * 8 * p.n_rowblocks;
+    if (p.q_f32)
+        hipLaunchKernelGGL((attn_valu_kernel<D, KVT, true>), dim3(grid), dim3(256), 0, st, p);
+    else
+        hipLaunchKernelGGL((attn_valu_kernel<D, KVT, false>), dim3(grid), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_valu_d(const AttnParams &p, int dtype, hipStream_t st) {
+    if (dtype == SV_F32) return launch_valu_t<D, SV_F32>(p, st);
+    if (dtype == SV_BF16) return launch_valu_t<D, SV_BF16>(p, st);
+    if (dtype == SV_Q4) return launch_valu_t<D, SV_Q4>(p, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_attn_valu(const AttnParams &p, int dtype, int D, hipStream_t st) {
+    switch (D) {
+        case 64: return launch_valu_d<64>(p, dtype, st);
+        case 128: return launch_valu_d<128>(p, dtype, st);
+        case 256: return launch_valu_d<256>(p, dtype, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_merge(const AttnParams &p, int D, hipStream_t st) {
+    const int rows = p.B * p.N * p.Hq;
+    switch (D) {
+        case 64:
+            hipLaunchKernelGGL(attn_merge_kernel<64>, dim3((rows + 3) / 4), dim3(256), 0, st, p);
+            break;
+        case 128:
+            hipLaunchKernelGGL(attn_merge_kernel<128>, dim3((rows + 1) / 2), dim3(256), 0, st, p);
+            break;
+        case 256:
+            hipLaunchKernelGGL(attn_merge_kernel<256>, dim3(rows), dim3(256), 0, st, p);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,82 @@
+// Device helpers shared by the gfx950 kernels: number formats, the tree mask,
+// KV row addressing, wavefront reductions.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "sv_internal.h"
+
+namespace sv {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+    return __uint_as_float(b16 << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    __bf16 h = (__bf16)f;
+    return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float fp16_bits_to_f32(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// Low (sel=0) or high (sel=1) 16-bit halves of a and b packed as (a_half, b_half).
+__device__ __forceinline__ uint32_t pack_lo_halves(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi_halves(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// Ancestor-or-self bit set of every node of one tree, built from the parent
+// array in LDS.  `par` holds parent[0..n-1]; a parent that is not an earlier
+// node ends the walk (no out-of-range access, bounded by n steps).
+__device__ __forceinline__ uint64_t ancestor_bits(const int *par, int i) {
+    uint64_t a = 1ull << i;
+    int j = i;
+#pragma unroll 1
+    for (int step = 0; step < 64 && j > 0; ++step) {
+        const int pj = par[j];
+        if (pj < 0 || pj >= j) break;
+        a |= 1ull << pj;
+        j = pj;
+    }
+    return a;
+}
+
+// Row number of KV row (b, h, pos) in the cache arrays (rows of any width); -1
+// when the page id is outside the pool (the row is then read as zeros and
+// never written).
+__device__ __forceinline__ int64_t kv_row_index(const KvView &kv, int b, int Hkv, int h, int pos) {
+    if (kv.page_table == nullptr) {
+        return ((int64_t)b * Hkv + h) * kv.capacity + pos;
+    }
+    const int ps = kv.page_size;
+    const int page = kv.page_table[(int64_t)b * kv.max_pages + pos / ps];
+    if (page < 0 || page >= kv.capacity) return -1;
+    return ((int64_t)page * Hkv + h) * ps + (pos % ps);
+}
+
+__device__ __forceinline__ int clamp_ctx(int c, int max_ctx) {
+    return c < 0 ? 0 : (c > max_ctx ? max_ctx : c);
+}
+
+// XOR lane exchange within a wavefront of 64
+__device__ __forceinline__ float xor_shfl(float v, int m) {
+    return __shfl_xor(v, m, 64);
+}
+
+}  // namespace sv

@@ -1,0 +1,324 @@
+// Host side of the C ABI declared in include/sv.h: argument validation, launch
+// planning and error mapping.  Nothing here allocates device memory or
+// synchronises; every kernel goes to the caller's stream.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "sv_internal.h"
+
+namespace sv {
+namespace {
+
+thread_local int g_last_hip_error = 0;
+int g_attn_target_wgs = 0;     // 0: choose by batch (see plan_attn)
+int g_argmax_chunk = 4096;
+
+int hip_fail(hipError_t e) {
+    g_last_hip_error = (int)e;
+    return SV_EHIP;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t m) { return ceil_div(a, m) * m; }
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Validates the cache descriptor against a call touching positions
+// [0, max_ctx + n_nodes) of sequences [0, batch).
+int check_kv(const sv_kv_cache *kv, int batch, int n_nodes, int max_ctx) {
+    if (kv == nullptr) return SV_EINVAL;
+    if (kv->dtype != SV_F32 && kv->dtype != SV_BF16 && kv->dtype != SV_Q4) return SV_EINVAL;
+    if (kv->n_kv_heads < 1) return SV_EINVAL;
+    if (kv->head_dim != 64 && kv->head_dim != 128 && kv->head_dim != 256) return SV_EINVAL;
+    if (kv->k == nullptr || kv->v == nullptr) return SV_EINVAL;
+    if (!aligned(kv->k, 16) || !aligned(kv->v, 16)) return SV_EINVAL;
+    if (kv->dtype == SV_Q4) {
+        if (kv->k_scale == nullptr || kv->v_scale == nullptr) return SV_EINVAL;
+        if (!aligned(kv->k_scale, 4) || !aligned(kv->v_scale, 4)) return SV_EINVAL;
+    }
+    if (kv->capacity < 1) return SV_EINVAL;
+    const int64_t need = (int64_t)max_ctx + n_nodes;
+    if (kv->page_size == 0) {
+        if (kv->page_table != nullptr) return SV_EINVAL;
+        if (kv->n_seqs < batch) return SV_EINVAL;
+        if (kv->capacity < need) return SV_EINVAL;
+    } else {
+        if (kv->page_size < 0 || kv->page_size % 8 != 0 || kv->page_size > (1 << 20)) return SV_EINVAL;
+        if (kv->page_table == nullptr) return SV_EINVAL;
+        if (kv->max_pages_per_seq < 1) return SV_EINVAL;
+        if ((int64_t)kv->max_pages_per_seq * kv->page_size < need) return SV_EINVAL;
+    }
+    return SV_OK;
+}
+
+KvView view_of(const sv_kv_cache *kv) {
+    KvView v;
+    v.k = kv->k;
+    v.v = kv->v;
+    v.ks = kv->k_scale;
+    v.vs = kv->v_scale;
+    v.page_table = kv->page_size ? kv->page_table : nullptr;
+    v.capacity = kv->capacity;
+    v.page_size = kv->page_size;
+    v.max_pages = kv->max_pages_per_seq;
+    return v;
+}
+
+struct AttnPlan {
+    bool mfma;
+    int nt, pg;
+    int rows_per_block, n_rowblocks;
+    int n_splits, split_len;
+    size_t ws_bytes;
+};
+
+// Launch plan for sv_verify_attn.  Work units are (sequence, KV head, row
+// block); each is split along the key positions so that the grid holds about
+// `target` workgroups (one per CU for a single sequence; several per CU for a
+// batch, whose sequence lengths are known only on the device, so that the
+// shorter sequences' empty splits leave the longer ones room).  Row blocks
+// are added while the split partials would exceed ~15% of the KV bytes.
+AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int Hkv, int max_ctx) {
+    AttnPlan pl{};
+    const int G = Hq / Hkv;
+    const int R = G * N;
+    const int64_t L = (int64_t)max_ctx + N;
+    pl.mfma = (q_dtype == SV_BF16) && (kv_dtype == SV_BF16 || kv_dtype == SV_Q4) && R >= 16;
+    const int target = g_attn_target_wgs > 0 ? g_attn_target_wgs : (B > 1 ? 2048 : 256);
+    const double pos_bytes = kv_dtype == SV_F32 ? D * 8.0 : (kv_dtype == SV_BF16 ? D * 4.0 : D * 1.125);
+
+    auto splits_for = [&](int units, int &split_len, int &n_splits) {
+        const int64_t want = std::max<int64_t>(1, target / std::max(units, 1));
+        split_len = (int)round_up(std::max<int64_t>(ceil_div(L, want), 8), 8);
+        n_splits = (int)ceil_div(L, split_len);
+    };
+
+    if (pl.mfma) {
+        const int T = kMfmaTileElems / D;
+        const int RT = (R + 15) / 16;
+        if (RT == 1) {
+            pl.pg = std::min(4, T / 32);
+            pl.nt = 1;
+            pl.rows_per_block = 16;
+            pl.n_rowblocks = 1;
+            splits_for(B * Hkv, pl.split_len, pl.n_splits);
+        } else {
+            pl.pg = 1;
+            int nrb = (RT + 7) / 8;            // at most 2 row tiles per wave
+            for (;;) {
+                const int tpb = (RT + nrb - 1) / nrb;
+                splits_for(B * Hkv * nrb, pl.split_len, pl.n_splits);
+                const double part = (double)pl.n_splits * R * (D + 2) * 4.0;
+                const double kvb = (double)L * pos_bytes;
+                if (part <= 0.15 * kvb || tpb <= 2) break;
+                ++nrb;
+            }
+            const int tpb = (RT + nrb - 1) / nrb;
+            pl.n_rowblocks = (RT + tpb - 1) / tpb;
+            pl.rows_per_block = tpb * 16;
+            pl.nt = (tpb + 3) / 4;
+            splits_for(B * Hkv * pl.n_rowblocks, pl.split_len, pl.n_splits);
+        }
+    } else {
+        pl.nt = 1;
+        pl.pg = 1;
+        pl.rows_per_block = 16;
+        pl.n_rowblocks = (R + 15) / 16;
+        splits_for(B * Hkv * pl.n_rowblocks, pl.split_len, pl.n_splits);
+    }
+    const size_t o_bytes = (size_t)B * Hkv * pl.n_splits * R * D * 4;
+    const size_t ml_bytes = (size_t)B * Hkv * pl.n_splits * R * 2 * 4;
+    pl.ws_bytes = (size_t)round_up((int64_t)o_bytes, 256) + (size_t)round_up((int64_t)ml_bytes, 256);
+    return pl;
+}
+
+int check_attn_shape(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads, int max_ctx) {
+    if (batch < 1 || n_nodes < 1 || n_nodes > 64 || n_q_heads < 1 || max_ctx < 0) return SV_EINVAL;
+    if (max_ctx > (1 << 30)) return SV_EINVAL;
+    if (kv == nullptr || kv->n_kv_heads < 1 || n_q_heads % kv->n_kv_heads != 0) return SV_EINVAL;
+    const int64_t rows = (int64_t)(n_q_heads / kv->n_kv_heads) * n_nodes;
+    if (rows > 4096) return SV_EUNSUPPORTED;
+    return check_kv(kv, batch, n_nodes, max_ctx);
+}
+
+}  // namespace
+}  // namespace sv
+
+using namespace sv;
+
+extern "C" {
+
+const char *sv_error_string(int code) {
+    switch (code) {
+        case SV_OK: return "ok";
+        case SV_EINVAL: return "invalid argument";
+        case SV_EUNSUPPORTED: return "unsupported combination";
+        case SV_EWORKSPACE: return "workspace missing or too small";
+        case SV_EHIP: return "HIP error";
+    }
+    return "unknown error code";
+}
+
+int sv_last_hip_error(void) { return g_last_hip_error; }
+
+int sv_set_option(int option, int value) {
+    int prev;
+    switch (option) {
+        case SV_OPT_ATTN_TARGET_WGS:
+            if (value < 0) return SV_EINVAL;
+            prev = g_attn_target_wgs;
+            g_attn_target_wgs = value;
+            return prev;
+        case SV_OPT_ARGMAX_CHUNK:
+            if (value <= 0 || value % 8 != 0) return SV_EINVAL;
+            prev = g_argmax_chunk;
+            g_argmax_chunk = value;
+            return prev;
+    }
+    return SV_EINVAL;
+}
+
+size_t sv_verify_attn_workspace_size(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
+                                     int max_ctx) {
+    if (check_attn_shape(kv, batch, n_nodes, n_q_heads, max_ctx) != SV_OK) return 0;
+    const AttnPlan pl = plan_attn(kv->dtype, SV_BF16, kv->head_dim, batch, n_nodes, n_q_heads,
+                                  kv->n_kv_heads, max_ctx);
+    const AttnPlan pf = plan_attn(kv->dtype, SV_F32, kv->head_dim, batch, n_nodes, n_q_heads,
+                                  kv->n_kv_heads, max_ctx);
+    return std::max(pl.ws_bytes, pf.ws_bytes);
+}
+
+int sv_verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
+                   const int32_t *ctx_lens, int max_ctx,
+                   const void *q, int q_dtype, const int32_t *parent, float sm_scale,
+                   void *out, float *lse,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = check_attn_shape(kv, batch, n_nodes, n_q_heads, max_ctx);
+    if (rc != SV_OK) return rc;
+    if (q == nullptr || out == nullptr || ctx_lens == nullptr || parent == nullptr) return SV_EINVAL;
+    if (q_dtype != SV_F32 && q_dtype != SV_BF16) return SV_EINVAL;
+    if (!aligned(q, 16) || !aligned(out, 16)) return SV_EINVAL;
+    if (!isfinite(sm_scale)) return SV_EINVAL;
+    if (q_dtype == SV_BF16 && kv->dtype == SV_F32) return SV_EUNSUPPORTED;
+    const int D = kv->head_dim;
+    const AttnPlan pl = plan_attn(kv->dtype, q_dtype, D, batch, n_nodes, n_q_heads, kv->n_kv_heads, max_ctx);
+    if (workspace == nullptr || workspace_bytes < pl.ws_bytes) return SV_EWORKSPACE;
+    if (!aligned(workspace, 16)) return SV_EINVAL;
+
+    AttnParams p{};
+    p.kv = view_of(kv);
+    p.q = q;
+    p.ctx_lens = ctx_lens;
+    p.parent = parent;
+    p.part_o = (float *)workspace;
+    const size_t o_bytes = (size_t)batch * kv->n_kv_heads * pl.n_splits * (n_q_heads / kv->n_kv_heads) *
+                           n_nodes * D * 4;
+    p.part_ml = (float *)((char *)workspace + round_up((int64_t)o_bytes, 256));
+    p.out = out;
+    p.lse = lse;
+    p.B = batch;
+    p.N = n_nodes;
+    p.Hq = n_q_heads;
+    p.Hkv = kv->n_kv_heads;
+    p.G = n_q_heads / kv->n_kv_heads;
+    p.R = p.G * n_nodes;
+    p.max_ctx = max_ctx;
+    p.n_splits = pl.n_splits;
+    p.split_len = pl.split_len;
+    p.rows_per_block = pl.rows_per_block;
+    p.n_rowblocks = pl.n_rowblocks;
+    p.n_units = batch * kv->n_kv_heads * pl.n_splits * pl.n_rowblocks;
+    const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)D);
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.q_f32 = q_dtype == SV_F32;
+
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = pl.mfma ? launch_attn_mfma(p, kv->dtype, D, pl.nt, pl.pg, st)
+                           : launch_attn_valu(p, kv->dtype, D, st);
+    if (e != hipSuccess) return hip_fail(e);
+    e = launch_attn_merge(p, D, st);
+    if (e != hipSuccess) return hip_fail(e);
+    return SV_OK;
+}
+
+size_t sv_greedy_accept_workspace_size(int batch, int n_nodes, int vocab) {
+    if (batch < 1 || n_nodes < 1 || n_nodes > 64 || vocab < 1) return 0;
+    const int64_t chunks = ceil_div(vocab, g_argmax_chunk);
+    const int64_t keys = (int64_t)batch * n_nodes * chunks * 8;
+    return (size_t)(round_up(keys, 256) + round_up((int64_t)batch * 4, 256));
+}
+
+int sv_greedy_accept(int batch, int n_nodes, int vocab,
+                     const void *logits, int logits_dtype,
+                     const int32_t *draft_ids, const int32_t *parent,
+                     int32_t *accept_len, int32_t *path, int32_t *tokens, int32_t *argmax,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+    if (batch < 1 || n_nodes < 1 || n_nodes > 64 || vocab < 1) return SV_EINVAL;
+    if (logits == nullptr || draft_ids == nullptr || parent == nullptr || accept_len == nullptr ||
+        path == nullptr || tokens == nullptr)
+        return SV_EINVAL;
+    if (logits_dtype != SV_F32 && logits_dtype != SV_BF16) return SV_EINVAL;
+    const int64_t chunks = ceil_div(vocab, g_argmax_chunk);
+    if ((int64_t)batch * n_nodes * chunks > (int64_t)INT32_MAX) return SV_EUNSUPPORTED;
+    const size_t need = sv_greedy_accept_workspace_size(batch, n_nodes, vocab);
+    if (workspace == nullptr || workspace_bytes < need) return SV_EWORKSPACE;
+    if (!aligned(workspace, 16)) return SV_EINVAL;
+    AcceptParams p{};
+    p.logits = logits;
+    p.draft = draft_ids;
+    p.parent = parent;
+    p.accept_len = accept_len;
+    p.path = path;
+    p.tokens = tokens;
+    p.argmax = argmax;
+    p.keys = (unsigned long long *)workspace;
+    p.counters = (unsigned int *)((char *)workspace + round_up((int64_t)batch * n_nodes * chunks * 8, 256));
+    p.B = batch;
+    p.N = n_nodes;
+    p.V = vocab;
+    p.chunk = g_argmax_chunk;
+    p.n_chunks = (int)chunks;
+    p.logits_f32 = logits_dtype == SV_F32;
+    const hipError_t e = launch_accept(p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return SV_OK;
+}
+
+int sv_kv_compact(const sv_kv_cache *kv, int n_layers, int batch, int n_nodes,
+                  const int32_t *ctx_lens, int max_ctx,
+                  const int32_t *path, const int32_t *accept_len,
+                  int32_t *new_lens, void *stream) {
+    if (n_layers < 1 || batch < 1 || n_nodes < 1 || n_nodes > 64 || max_ctx < 0) return SV_EINVAL;
+    if (max_ctx > (1 << 30)) return SV_EINVAL;
+    const int rc = check_kv(kv, batch, n_nodes, max_ctx);
+    if (rc != SV_OK) return rc;
+    if (ctx_lens == nullptr || path == nullptr || accept_len == nullptr) return SV_EINVAL;
+    if (n_layers > 1 && (kv->layer_stride == 0 ||
+                         (kv->dtype == SV_Q4 && kv->scale_layer_stride == 0)))
+        return SV_EINVAL;
+    if (kv->layer_stride % 16 != 0 || kv->scale_layer_stride % 4 != 0) return SV_EINVAL;
+    if ((int64_t)batch * n_layers * kv->n_kv_heads * 2 > (int64_t)INT32_MAX) return SV_EUNSUPPORTED;
+    CompactParams p{};
+    p.kv = view_of(kv);
+    p.layer_stride = kv->layer_stride;
+    p.scale_layer_stride = kv->scale_layer_stride;
+    p.ctx_lens = ctx_lens;
+    p.path = path;
+    p.accept_len = accept_len;
+    p.new_lens = new_lens;
+    p.B = batch;
+    p.N = n_nodes;
+    p.Hkv = kv->n_kv_heads;
+    p.D = kv->head_dim;
+    p.n_layers = n_layers;
+    p.max_ctx = max_ctx;
+    p.dtype = kv->dtype;
+    const hipError_t e = launch_compact(p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return SV_OK;
+}
+
+}  // extern "C"

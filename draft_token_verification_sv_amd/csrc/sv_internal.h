@@ -1,0 +1,72 @@
+// Internal launch parameters shared by the host API (sv_api.cpp) and the HIP
+// kernels.  Plain C++ structs passed by value as kernel arguments.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/sv.h"
+
+namespace sv {
+
+// Where one layer of the KV cache lives (see sv_kv_cache in sv.h).
+struct KvView {
+    const void *k, *v;            // codes / values, layer 0 of this call
+    const void *ks, *vs;          // 4-bit scales or nullptr
+    const int32_t *page_table;    // nullptr: contiguous
+    int64_t capacity;             // positions per (seq, head) or pages in the pool
+    int32_t page_size;            // 0: contiguous
+    int32_t max_pages;            // page-table row length
+};
+
+struct AttnParams {
+    KvView kv;
+    const void *q;                // [B][N][Hq][D]
+    const int32_t *ctx_lens;      // [B]
+    const int32_t *parent;        // [B][N]
+    float *part_o;                // [B][Hkv][S][R][D]  (unnormalised, scaled to 2^-m)
+    float *part_ml;               // [B][Hkv][S][R][2]  (m in log2 units, l)
+    void *out;                    // [B][N][Hq][D]
+    float *lse;                   // [B][N][Hq] or nullptr
+    int B, N, Hq, Hkv, G, R;      // R = G * N packed rows per (b, kv head)
+    int max_ctx;
+    int n_splits, split_len;      // positions per split (multiple of the kernel tile)
+    int rows_per_block, n_rowblocks;
+    int n_units;                  // B * Hkv * n_splits * n_rowblocks
+    float scale_log2;             // sm_scale * log2(e)
+    int q_f32;                    // 1: q/out are fp32, 0: bf16
+};
+
+struct AcceptParams {
+    const void *logits;           // [B][N][V]
+    const int32_t *draft;         // [B][N]
+    const int32_t *parent;        // [B][N]
+    int32_t *accept_len, *path, *tokens, *argmax;
+    unsigned long long *keys;     // [B][N][chunks] packed (value, index) maxima
+    unsigned int *counters;       // [B]   (zero between calls)
+    int B, N, V, chunk, n_chunks;
+    int logits_f32;
+};
+
+struct CompactParams {
+    KvView kv;
+    int64_t layer_stride, scale_layer_stride;   // bytes
+    const int32_t *ctx_lens, *path, *accept_len;
+    int32_t *new_lens;
+    int B, N, Hkv, D, n_layers, max_ctx, dtype;
+};
+
+// Kernel-side tile sizes (positions staged per iteration) -----------------
+constexpr int kMfmaTileElems = 16384;          // T * D bf16 elements per K (or V) tile
+constexpr int kValuTileElems = 8192;           // T * D fp32 elements per K (or V) tile
+
+// launchers (return the hipError_t of the launch) -------------------------
+hipError_t launch_attn_mfma(const AttnParams &p, int dtype, int D, int nt, int pg, hipStream_t s);
+hipError_t launch_attn_valu(const AttnParams &p, int dtype, int D, hipStream_t s);
+hipError_t launch_attn_merge(const AttnParams &p, int D, hipStream_t s);
+hipError_t launch_accept(const AcceptParams &p, hipStream_t s);
+hipError_t launch_compact(const CompactParams &p, hipStream_t s);
+
+}  // namespace sv

@@ -1,0 +1,212 @@
+/*
+ * sv.h -- the verify step of speculative decoding on one AMD MI355X (gfx950).
+ *
+ * Three calls verify a draft (a chain or a token tree) against the target
+ * model, for one layer's KV cache at a time:
+ *
+ *   sv_verify_attn    tree- or chain-masked GQA attention of the N verify rows
+ *                     over the KV cache (contiguous, paged or 4-bit);
+ *   sv_greedy_accept  per-row argmax of the target logits, greedy acceptance of
+ *                     the longest root path whose drafts equal their parent's
+ *                     argmax, plus the bonus token;
+ *   sv_kv_compact     in-place compaction of the accepted rows' KV so that only
+ *                     the accepted path remains.
+ *
+ * Sources (web pages on speculative decoding; citations name page and section):
+ *   [DFN]  "Making Qwen3.5-27B token generation 6x faster on one RTX 3090"
+ *          (blog.xiaohack.org): greedy verify of 16-row DFlash blocks
+ *          ("Architecture"), DDTree verification of budget+1 rows ("From
+ *          autoregressive to DDTree", "Key breakthroughs"), compaction after
+ *          a sibling branch is accepted ("Key breakthroughs"), flash attention
+ *          reading a 4-bit KV cache at 128K context ("128K context in 24 GB").
+ *   [XDN]  xdnf.cn notes on Qwen3.8-27B speculative decoding: 16-token KV pages
+ *          (section 2); the draft block's causal mask must be aligned to the
+ *          end of the keys (section 5.3).
+ *   [KWK]  kwkr.cn RTX-4080 notes: rolling back rejected draft KV (section 3.3).
+ *
+ * Conventions used by every call
+ * ------------------------------
+ *  - Pointers named "device" point to GPU memory owned by the caller; the
+ *    library keeps no pointer after a call returns.  Host pointers are read
+ *    during the call only.
+ *  - N (n_nodes) is the number of verify rows INCLUDING the root: row 0 is the
+ *    last committed token, rows 1..N-1 are drafts.  1 <= N <= 64.
+ *  - parent[b][i] (device int32 [batch][N]): parent[b][0] = -1 and
+ *    0 <= parent[b][i] < i for i >= 1 (a chain has parent[i] = i - 1).  An
+ *    entry that breaks this rule is treated as the end of the node's path
+ *    (never read out of bounds, result unspecified).
+ *  - ctx_lens[b] (device int32 [batch]) counts the cached tokens before the
+ *    verify block.  The N verify rows' K/V are already in the cache at logical
+ *    positions ctx .. ctx+N-1 in node order (written by the caller, quantised
+ *    for a 4-bit cache).  Values above max_ctx are clamped to max_ctx, negative
+ *    ones to 0.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream); outputs are valid once the stream has been synchronised.  The
+ *    library never synchronises and never allocates device memory.
+ *  - Return codes: SV_OK, or a negative SV_E* code; on SV_EHIP the HIP error is
+ *    available from sv_last_hip_error() (per thread).  Argument errors are
+ *    detected on the host before anything is launched.
+ */
+#ifndef SV_H
+#define SV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SV_OK            0
+#define SV_EINVAL       -1   /* bad argument (null pointer, size, dtype, layout) */
+#define SV_EUNSUPPORTED -2   /* valid but not implemented combination            */
+#define SV_EWORKSPACE   -3   /* workspace missing or smaller than required      */
+#define SV_EHIP         -4   /* a HIP call or kernel launch failed              */
+
+#define SV_F32  0            /* IEEE binary32                                     */
+#define SV_BF16 1            /* bfloat16                                          */
+#define SV_Q4   2            /* 4-bit KV blocks: see sv_kv_cache                  */
+
+/*
+ * KV cache descriptor (one layer is read by sv_verify_attn; sv_kv_compact walks
+ * n_layers layers spaced layer_stride bytes apart).
+ *
+ * Row = one (sequence, KV head, position): head_dim values.
+ *   SV_F32 / SV_BF16: k, v hold the values, head_dim per row.
+ *   SV_Q4 [DFN "128K context in 24 GB"]: k, v hold 4-bit codes, head_dim/2
+ *     bytes per row; value 2t of a row is the low nibble of byte t, value 2t+1
+ *     the high nibble.  k_scale, v_scale hold one IEEE-half scale per 32
+ *     consecutive values (head_dim/32 per row).  Value i of a row is
+ *     scale[i/32] * (code_i - 8).
+ * Layout (page_size == 0, contiguous): row (b, h, p) is row number
+ *     (b * n_kv_heads + h) * capacity + p   of each array.
+ * Layout (page_size > 0, paged) [XDN section 2]: page_table[b][p / page_size]
+ *     names the physical page of logical position p of sequence b; row
+ *     (b, h, p) is row number (page * n_kv_heads + h) * page_size + p % page_size.
+ *     Page ids outside [0, capacity) are read as zero rows and never written.
+ */
+typedef struct sv_kv_cache {
+    int32_t dtype;              /* SV_F32, SV_BF16 or SV_Q4                         */
+    int32_t n_kv_heads;         /* >= 1                                             */
+    int32_t head_dim;           /* 64, 128 or 256                                   */
+    int32_t page_size;          /* 0: contiguous; else tokens per page (multiple of 8) */
+    int64_t capacity;           /* contiguous: positions per (seq, head); paged: pages in the pool */
+    int32_t n_seqs;             /* contiguous: sequences held (>= batch); paged: unused */
+    int32_t max_pages_per_seq;  /* paged: row length of page_table                  */
+    void *k;                    /* device, layer 0                                  */
+    void *v;                    /* device, layer 0                                  */
+    void *k_scale;              /* device, SV_Q4 only (else NULL)                   */
+    void *v_scale;              /* device, SV_Q4 only (else NULL)                   */
+    const int32_t *page_table;  /* device int32 [batch][max_pages_per_seq], paged only */
+    int64_t layer_stride;       /* bytes between layers in k and v                  */
+    int64_t scale_layer_stride; /* bytes between layers in k_scale and v_scale      */
+} sv_kv_cache;
+
+/*
+ * sv_verify_attn -- masked GQA attention of the verify rows.
+ *
+ * For sequence b, query head h (KV head h / (n_q_heads / n_kv_heads)) and
+ * verify row i, with keys/values at logical positions j in [0, ctx + N):
+ *   visible(i, j)  = j < ctx, or j - ctx is node i or one of its ancestors
+ *                    (for a chain: row i sees ctx + 0..i, the causal mask
+ *                    aligned to the end of the keys [XDN section 5.3]; for a
+ *                    DDTree the ancestor mask [DFN "From autoregressive to
+ *                    DDTree"]);
+ *   out[b][i][h]   = sum_j softmax_visible(sm_scale * q . k_j) v_j;
+ *   lse[b][i][h]   = ln sum_visible exp(sm_scale * q . k_j).
+ *
+ * q    device [batch][N][n_q_heads][head_dim], q_dtype SV_F32 or SV_BF16.
+ * out  device, same shape and dtype as q (bf16 rounded to nearest even).
+ * lse  device float [batch][N][n_q_heads], or NULL.
+ * sm_scale  <= 0 selects 1/sqrt(head_dim).
+ * max_ctx   host int >= every ctx_lens[b]; sizes the launch.  The cache must
+ *           hold max_ctx + N positions per sequence (contiguous: capacity;
+ *           paged: max_pages_per_seq * page_size).
+ * workspace device scratch of at least sv_verify_attn_workspace_size() bytes
+ *           (any contents; 256-byte aligned).  One workspace serves one
+ *           stream at a time.
+ * Supported: q SV_BF16 with KV SV_BF16 or SV_Q4 (bf16 matrix cores when
+ * (n_q_heads/n_kv_heads) * N >= 16 rows, vector ALU otherwise); q SV_F32 with
+ * KV SV_F32, SV_BF16 or SV_Q4 (vector ALU, fp32 arithmetic).
+ */
+size_t sv_verify_attn_workspace_size(const sv_kv_cache *kv, int batch, int n_nodes,
+                                     int n_q_heads, int max_ctx);
+int sv_verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
+                   const int32_t *ctx_lens, int max_ctx,
+                   const void *q, int q_dtype, const int32_t *parent, float sm_scale,
+                   void *out, float *lse,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sv_greedy_accept -- greedy acceptance [DFN "Architecture": greedy verify;
+ * "From autoregressive to DDTree": longest accepted root path].
+ *
+ * logits    device [batch][N][vocab], SV_F32 or SV_BF16 (finite values).  Row i
+ *           holds the target's logits after node i (N = budget + 1 rows for a
+ *           DDTree [DFN "Key breakthroughs"]).
+ * draft_ids device int32 [batch][N]; entry 0 (the committed token) is ignored.
+ * am[b][i]  = lowest index of the maximum of row (b, i), compared in fp32.
+ * Node i is accepted iff its parent is accepted and draft_ids[b][i] ==
+ * am[b][parent[b][i]] (node 0 always).  The deepest accepted node wins, ties
+ * to the smallest node index; path = its root path (node 0 first).
+ * Outputs (device int32):
+ *   accept_len [batch]     a = accepted drafts (0 .. N-1); a + 1 tokens commit;
+ *   path       [batch][N]  path[0..a] node indices, then -1;
+ *   tokens     [batch][N]  draft ids of path[1..a], then the bonus am[path[a]],
+ *                          then -1;
+ *   argmax     [batch][N]  am, or NULL.
+ * workspace device scratch of sv_greedy_accept_workspace_size() bytes.  It must
+ *           be zero-filled before its first use; every completed call leaves
+ *           all of it zero-filled again (whatever the shape of the next call).  One workspace serves one stream at a
+ *           time (concurrent calls sharing it race).
+ */
+size_t sv_greedy_accept_workspace_size(int batch, int n_nodes, int vocab);
+int sv_greedy_accept(int batch, int n_nodes, int vocab,
+                     const void *logits, int logits_dtype,
+                     const int32_t *draft_ids, const int32_t *parent,
+                     int32_t *accept_len, int32_t *path, int32_t *tokens, int32_t *argmax,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sv_kv_compact -- keep only the accepted rows [DFN "Key breakthroughs";
+ * KWK section 3.3].  In place, for every layer l < n_layers, KV head, K and V
+ * (and the 4-bit scale rows):
+ *     row ctx + j  <-  row ctx + path[b][j]      for j = 0 .. accept_len[b],
+ * with every source read before any destination is written.  Rows where
+ * path[j] == j are not touched (a chain moves nothing); rows past
+ * ctx + accept_len are left as they were.
+ * new_lens  device int32 [batch] = ctx + accept_len + 1, or NULL.
+ * path / accept_len are sv_greedy_accept's outputs (device).  Entries that are
+ * out of range (accept_len outside [0, N-1], path[j] outside [j, N-1]) skip the
+ * affected rows.
+ */
+int sv_kv_compact(const sv_kv_cache *kv, int n_layers, int batch, int n_nodes,
+                  const int32_t *ctx_lens, int max_ctx,
+                  const int32_t *path, const int32_t *accept_len,
+                  int32_t *new_lens, void *stream);
+
+/* Static text for a return code. */
+const char *sv_error_string(int code);
+/* The hipError_t of this thread's last SV_EHIP return (0 if none). */
+int sv_last_hip_error(void);
+
+/*
+ * Launch tuning (for benchmarks and sweeps; the defaults need no setting).
+ *   SV_OPT_ATTN_TARGET_WGS  workgroups the attention launch aims for; 0 (the
+ *                           default) = 256 for one sequence, 2048 for a batch
+ *   SV_OPT_ARGMAX_CHUNK     logits elements per argmax workgroup, a positive
+ *                           multiple of 8 (default 4096)
+ * Returns the previous value, or SV_EINVAL for an unknown option or a value
+ * out of range.  A workspace sized under one setting may be too small under
+ * another (the call then returns SV_EWORKSPACE).
+ * Process-wide; not synchronised with calls in flight on other threads.
+ */
+#define SV_OPT_ATTN_TARGET_WGS 1
+#define SV_OPT_ARGMAX_CHUNK    2
+int sv_set_option(int option, int value);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SV_H */

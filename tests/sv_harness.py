@@ -1,0 +1,139 @@
+"""Shared helpers for the GPU tests: move a ``workloads.Case`` to the device,
+run the library through its binding, compare with the oracle."""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_tensor(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(device).view(torch.bfloat16)
+    if dtype == "u8":
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to(device)
+    if dtype == "u16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(device)
+    if dtype == "i32":
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(device)
+    raise ValueError(dtype)
+
+
+class DeviceCase:
+    """Device copies of a case's arrays plus the binding's KVCache view."""
+
+    def __init__(self, case, device="cuda"):
+        import draft_token_verification_sv_amd as sv
+        cfg = case.cfg
+        self.case = case
+        self.q = dev_tensor(case.q, cfg.q_dtype, device)
+        if cfg.kv_dtype == "q4":
+            self.k = dev_tensor(case.k, "u8", device)
+            self.v = dev_tensor(case.v, "u8", device)
+            self.ks = dev_tensor(case.k_scale, "u16", device)
+            self.vs = dev_tensor(case.v_scale, "u16", device)
+        else:
+            self.k = dev_tensor(case.k, cfg.kv_dtype, device)
+            self.v = dev_tensor(case.v, cfg.kv_dtype, device)
+            self.ks = self.vs = None
+        self.pt = dev_tensor(case.page_table, "i32", device) if cfg.paged else None
+        self.kv = sv.KVCache(k=self.k, v=self.v, k_scale=self.ks, v_scale=self.vs, page_table=self.pt)
+        self.ctx = dev_tensor(case.ctx_lens, "i32", device)
+        self.parent = dev_tensor(case.parent, "i32", device)
+        self.logits = dev_tensor(case.logits, cfg.logits_dtype, device)
+        self.drafts = dev_tensor(case.draft_ids, "i32", device)
+        self.max_ctx = int(case.ctx_lens.max())
+
+    def attn(self, **kw):
+        import draft_token_verification_sv_amd as sv
+        return sv.verify_attn(self.kv, self.q, self.ctx, self.parent, self.max_ctx, **kw)
+
+    def accept(self, **kw):
+        import draft_token_verification_sv_amd as sv
+        return sv.greedy_accept(self.logits, self.drafts, self.parent, **kw)
+
+    def cache_arrays_host(self):
+        """Host copies of the cache arrays in the storage form of the case."""
+        def back(t, like):
+            if t.dtype == torch.bfloat16:
+                t = t.view(torch.int16)
+            a = t.cpu().numpy()
+            return a.view(like.dtype) if a.dtype != like.dtype else a
+        arrs = [back(self.k, self.case.k), back(self.v, self.case.v)]
+        if self.ks is not None:
+            arrs += [back(self.ks, self.case.k_scale), back(self.vs, self.case.v_scale)]
+        return arrs
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def check_attention(case, out, lse, *, heads=None, batch=None, ref=None):
+    """Attention gate of the case's dtype plus the supplementary diagnostics.
+    Returns (max_abs, rel_fro, lse_err)."""
+    cfg = case.cfg
+    if ref is None:
+        ref = oracle.verify_attention(case, heads=heads, batch=batch)
+    ro, rl = ref
+    go, gl = to_f64(out), to_f64(lse)
+    sel = ~np.isnan(ro[..., 0])
+    diff = np.abs(go[sel] - ro[sel])
+    max_abs = float(diff.max())
+    rel = float(np.linalg.norm(go[sel] - ro[sel]) / max(np.linalg.norm(ro[sel]), 1e-30))
+    lse_err = float(np.abs(gl[sel] - rl[sel]).max())
+    bf16 = cfg.q_dtype == "bf16" or cfg.kv_dtype != "f32"
+    if cfg.q_dtype == "f32" and cfg.kv_dtype == "f32":
+        assert max_abs <= 1e-4, (max_abs, cfg.name)
+        assert lse_err <= 1e-5, (lse_err, cfg.name)
+    else:
+        assert max_abs <= 2e-2, (max_abs, cfg.name)
+        lse_tol = 2e-2
+        if cfg.kv_dtype == "q4" and cfg.q_dtype == "bf16":
+            # the matrix-core path rounds dequantised 4-bit keys to bf16
+            # (relative error <= 2^-8 per value), so a score can move by up to
+            # 2^-8 * scale * sum_d |q_d k_d|; peaked rows reach scores ~30
+            lse_tol += 2.0 ** -8 * score_abs_bound(case, heads=heads, batch=batch)
+        assert lse_err <= lse_tol, (lse_err, lse_tol, cfg.name)
+        if bf16:
+            assert rel <= 1e-2, (rel, cfg.name)
+    assert np.all(np.isfinite(go[sel]))
+    return max_abs, rel, lse_err
+
+
+def score_abs_bound(case, heads=None, batch=None):
+    """max over rows and keys of scale * sum_d |q_d| |k_d| (exact inputs)."""
+    from oracle.attention import logical_rows
+    from oracle.formats import widen
+    cfg = case.cfg
+    G = cfg.n_q_heads // cfg.n_kv_heads
+    scale = 1.0 / np.sqrt(cfg.head_dim)
+    lay = (lambda a: a) if case.kv_layers == 1 else (lambda a: a[0])
+    best = 0.0
+    for b in (range(cfg.batch) if batch is None else batch):
+        L = int(case.ctx_lens[b]) + cfg.n_nodes
+        qa = np.abs(widen(case.q[b], cfg.q_dtype))
+        for g in range(cfg.n_kv_heads):
+            hs = [h for h in range(g * G, (g + 1) * G) if heads is None or h in heads]
+            if not hs:
+                continue
+            K = np.abs(logical_rows(lay(case.k), None if case.k_scale is None else lay(case.k_scale),
+                                    b=b, head=g, length=L, dtype=cfg.kv_dtype,
+                                    page_table=case.page_table if cfg.paged else None,
+                                    page_size=cfg.page_size))
+            for h in hs:
+                best = max(best, float((qa[:, h, :] @ K.T).max()) * scale)
+    return best
+
+
+def oracle_accept(case):
+    lg = case.logits.astype(np.float64) if case.cfg.logits_dtype == "f32" else oracle.widen_bf16(case.logits)
+    return oracle.greedy_accept(lg, case.draft_ids, case.parent)

@@ -1,0 +1,136 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every entry point
+include/sv.h declares, sizes workspaces, and rejects bad arguments before
+launching anything.  Every call made here returns during host-side argument
+validation."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "draft_token_verification_sv_amd", "libsv.so")
+HEADER = os.path.join(ROOT, "include", "sv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "sv_build", os.path.join(ROOT, "draft_token_verification_sv_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
+    L = ctypes.CDLL(LIB)
+    L.sv_error_string.restype = ctypes.c_char_p
+    L.sv_verify_attn_workspace_size.restype = ctypes.c_size_t
+    L.sv_greedy_accept_workspace_size.restype = ctypes.c_size_t
+    return L
+
+
+class KV(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("capacity", ctypes.c_int64), ("n_seqs", ctypes.c_int32),
+                ("max_pages_per_seq", ctypes.c_int32), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p), ("page_table", ctypes.c_void_p),
+                ("layer_stride", ctypes.c_int64), ("scale_layer_stride", ctypes.c_int64)]
+
+
+FAKE = 0x7F0000000000        # aligned, never dereferenced by the host checks
+
+
+def kv(**kw):
+    d = KV(dtype=1, n_kv_heads=4, head_dim=256, page_size=0, capacity=4200, n_seqs=1,
+           max_pages_per_seq=0, k=FAKE, v=FAKE + 0x100000, k_scale=None, v_scale=None,
+           page_table=None, layer_stride=0, scale_layer_stride=0)
+    for k_, v_ in kw.items():
+        setattr(d, k_, v_)
+    return d
+
+
+def test_exports_every_declared_symbol(lib):
+    with open(HEADER) as f:
+        text = f.read()
+    names = set(re.findall(r"\b(sv_[a-z_]+)\s*\(", text))
+    assert {"sv_verify_attn", "sv_greedy_accept", "sv_kv_compact"} <= names
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+
+
+def test_error_strings(lib):
+    for code, text in [(0, b"ok"), (-1, b"invalid argument"), (-3, b"workspace missing or too small")]:
+        assert lib.sv_error_string(code) == text
+    assert lib.sv_last_hip_error() == 0
+
+
+def _attn(lib, d, B=1, N=8, Hq=24, max_ctx=4096, q=FAKE, qd=1, ws=FAKE, wsb=1 << 40):
+    return lib.sv_verify_attn(ctypes.byref(d) if d is not None else None, B, N, Hq,
+                              ctypes.c_void_p(FAKE), max_ctx, ctypes.c_void_p(q), qd,
+                              ctypes.c_void_p(FAKE), ctypes.c_float(0.0), ctypes.c_void_p(FAKE),
+                              None, ctypes.c_void_p(ws), ctypes.c_size_t(wsb), None)
+
+
+def test_attention_argument_checks(lib):
+    assert _attn(lib, None) == -1
+    assert _attn(lib, kv(head_dim=96)) == -1
+    assert _attn(lib, kv(dtype=7)) == -1
+    assert _attn(lib, kv(), Hq=25) == -1                   # Hq % Hkv
+    assert _attn(lib, kv(), N=0) == -1
+    assert _attn(lib, kv(), N=65) == -1
+    assert _attn(lib, kv(capacity=4100)) == -1             # ctx + N over capacity
+    assert _attn(lib, kv(n_seqs=0)) == -1
+    assert _attn(lib, kv(k=FAKE + 8)) == -1                # misaligned
+    assert _attn(lib, kv(), q=0) == -1
+    assert _attn(lib, kv(), qd=2) == -1
+    assert _attn(lib, kv(dtype=2)) == -1                   # 4-bit without scales
+    assert _attn(lib, kv(dtype=0), qd=1) == -2             # bf16 q over an fp32 cache
+    assert _attn(lib, kv(page_size=12, page_table=FAKE, max_pages_per_seq=400)) == -1
+    assert _attn(lib, kv(page_size=16, page_table=FAKE, max_pages_per_seq=256)) == -1   # 4096 < ctx+N
+    assert _attn(lib, kv(), ws=0) == -3
+    assert _attn(lib, kv(), wsb=1024) == -3
+
+
+def test_attention_workspace_size(lib):
+    d = kv()
+    n = lib.sv_verify_attn_workspace_size(ctypes.byref(d), 1, 8, 24, 4096)
+    # partials (O and m,l) of 48 rows x 256 dims per (KV head, split): at least one split per head
+    assert n >= 4 * 48 * (256 + 2) * 4 and n % 256 == 0
+    assert lib.sv_verify_attn_workspace_size(ctypes.byref(d), 1, 8, 25, 4096) == 0
+    big = lib.sv_verify_attn_workspace_size(ctypes.byref(kv(capacity=200000)), 1, 8, 24, 131072)
+    assert big >= n
+
+
+def test_accept_checks_and_workspace(lib):
+    n = lib.sv_greedy_accept_workspace_size(1, 8, 151936)
+    chunks = -(-151936 // 4096)
+    assert n == -(-(8 * chunks * 8) // 256) * 256 + 256
+    P = ctypes.c_void_p(FAKE)
+
+    def call(B=1, N=8, V=151936, ld=1, ws=FAKE, wsb=1 << 30):
+        return lib.sv_greedy_accept(B, N, V, P, ld, P, P, P, P, P, None, ctypes.c_void_p(ws),
+                                    ctypes.c_size_t(wsb), None)
+    assert call(N=0) == -1 and call(N=65) == -1 and call(V=0) == -1 and call(ld=2) == -1
+    assert call(ws=0) == -3 and call(wsb=16) == -3
+    assert lib.sv_greedy_accept(1, 8, 100, None, 1, P, P, P, P, P, None, P, ctypes.c_size_t(1 << 20), None) == -1
+
+
+def test_compact_checks(lib):
+    P = ctypes.c_void_p(FAKE)
+
+    def call(d, L=1, B=1, N=8, max_ctx=4096):
+        return lib.sv_kv_compact(ctypes.byref(d), L, B, N, P, max_ctx, P, P, None, None)
+    assert call(kv(), L=0) == -1
+    assert call(kv(), L=3) == -1                            # several layers need a layer stride
+    assert call(kv(layer_stride=24)) == -1                  # stride not a multiple of 16
+    assert call(kv(), N=70) == -1
+    assert call(kv(capacity=10)) == -1
+
+
+def test_options(lib):
+    prev = lib.sv_set_option(1, 300)
+    assert prev == 0
+    assert lib.sv_set_option(1, 0) == 300
+    assert lib.sv_set_option(2, 12) == -1                   # not a multiple of 8
+    assert lib.sv_set_option(2, 4096) == 4096
+    assert lib.sv_set_option(9, 1) == -1

@@ -1,0 +1,286 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Attention within the gates (max-abs 2e-2 for bf16 / 4-bit inputs, 1e-4 for
+fp32) plus the supplementary checks (relative Frobenius error, lse error);
+argmax, accept length, path, tokens and compacted caches bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from sv_harness import DeviceCase, check_attention, oracle_accept, say
+
+pytestmark = pytest.mark.gpu
+
+C = workloads.CONFIGS
+
+
+@pytest.fixture(scope="module")
+def sv():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import draft_token_verification_sv_amd as m
+    return m
+
+
+def _small(name, **kw):
+    return workloads.small_variant(C[name], **kw)
+
+
+ATTN_CASES = [
+    # (label, config, make_case kwargs)
+    ("C1 tiny fp32 chain", C["C1"], {}),
+    ("C2 ctx333", _small("C2", ctx=333), {}),
+    ("C2 ctx1000 peaked", _small("C2", ctx=1000), {"variant": "peaked"}),
+    ("C3 tree22 ctx500", _small("C3", ctx=500), {}),
+    ("C3 tree23 ctx700 peaked", _small("C3", ctx=700, n_nodes=23), {"variant": "peaked"}),
+    ("C3 tree22 ctx16 peaked", _small("C3", ctx=16), {"variant": "peaked"}),
+    ("C3 tree22 ctx0", _small("C3", ctx=0), {"variant": "peaked"}),
+    ("C4 q4 ctx700", _small("C4", ctx=700), {}),
+    ("C4 q4 ctx130 peaked", _small("C4", ctx=130), {"variant": "peaked"}),
+    ("C5 paged b8", _small("C5", ctx=40, ctx_hi=900), {}),
+    ("C5 paged b8 peaked", _small("C5", ctx=3, ctx_hi=200), {"variant": "peaked"}),
+]
+
+
+@pytest.mark.parametrize("label,cfg,kw", ATTN_CASES, ids=[c[0] for c in ATTN_CASES])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_attention_small(sv, label, cfg, kw, seed):
+    say(f"[attn] {label} seed={seed}")
+    case = workloads.make_case(cfg, seed=1000 * seed + 17, capacity_pad=5, **kw)
+    dc = DeviceCase(case)
+    out, lse = dc.attn()
+    torch.cuda.synchronize()
+    ma, rel, le = check_attention(case, out, lse)
+    say(f"    max_abs={ma:.3g} rel={rel:.3g} lse={le:.3g}")
+
+
+VARIANT_SHAPES = [
+    # (label, Hq, Hkv, D, N, q, kv, paged, ctx, tree)
+    ("decode N=1 G=6 bf16 (VALU)", 24, 4, 256, 1, "bf16", "bf16", False, 777, "chain"),
+    ("decode N=1 G=4 paged (VALU)", 32, 8, 128, 1, "bf16", "bf16", True, 300, "chain"),
+    ("N=64 max rows tree D128", 4, 2, 128, 64, "bf16", "bf16", False, 200, "ddtree"),
+    ("N=3 G=8 -> 24 rows D64", 8, 1, 64, 3, "bf16", "bf16", False, 513, "chain"),
+    ("R=16 exactly D256", 8, 2, 256, 4, "bf16", "bf16", False, 129, "chain"),
+    ("R=16 D256 q4", 8, 2, 256, 4, "bf16", "q4", False, 129, "chain"),
+    ("fp32 q bf16 kv", 4, 2, 128, 5, "f32", "bf16", False, 150, "ddtree"),
+    ("fp32 q q4 kv paged", 4, 2, 256, 6, "f32", "q4", True, 90, "ddtree"),
+    ("fp32 tree D256 rows>16", 12, 2, 256, 8, "f32", "f32", False, 64, "ddtree"),
+    ("bf16 q4 paged tree", 12, 2, 64, 9, "bf16", "q4", True, 100, "ddtree"),
+    ("many row blocks", 32, 1, 128, 12, "bf16", "bf16", False, 40, "ddtree"),
+]
+
+
+@pytest.mark.parametrize("shape", VARIANT_SHAPES, ids=[s[0] for s in VARIANT_SHAPES])
+def test_attention_shapes(sv, shape):
+    label, Hq, Hkv, D, N, qd, kvd, paged, ctx, tree = shape
+    say(f"[attn-shape] {label}")
+    cfg = workloads.Config(label, 2, Hq, Hkv, D, N, qd, kvd, "f32", 50, ctx, ctx_hi=ctx + 37,
+                           tree=tree, paged=paged, q_std=0.5, kv_std=0.5,
+                           draft_rule="tree" if tree == "ddtree" else "geometric")
+    case = workloads.make_case(cfg, seed=5, capacity_pad=3, variant="peaked")
+    dc = DeviceCase(case)
+    out, lse = dc.attn()
+    torch.cuda.synchronize()
+    ma, rel, le = check_attention(case, out, lse)
+    say(f"    max_abs={ma:.3g} rel={rel:.3g} lse={le:.3g}")
+
+
+@pytest.mark.parametrize("target", [1, 5, 64, 300, 5000])
+def test_attention_split_count_independent(sv, target):
+    """Any number of splits gives the same answer (to fp tolerance)."""
+    say(f"[attn-splits] target_wgs={target}")
+    cfg = _small("C3", ctx=900)
+    case = workloads.make_case(cfg, seed=3, variant="peaked")
+    dc = DeviceCase(case)
+    prev = sv.set_option(sv.SV_OPT_ATTN_TARGET_WGS, target)
+    try:
+        out, lse = dc.attn()
+        torch.cuda.synchronize()
+    finally:
+        sv.set_option(sv.SV_OPT_ATTN_TARGET_WGS, prev)
+    check_attention(case, out, lse)
+
+
+FULL = [("C2", None, None), ("C3", None, None), ("C4", [0, 7, 23], None), ("C5", None, [0, 3, 7])]
+
+
+@pytest.mark.parametrize("name,heads,batch", FULL, ids=[f[0] for f in FULL])
+def test_attention_full_size_sampled(sv, name, heads, batch):
+    """The configurations at their full sizes, in the launch configuration the
+    benchmark times (library defaults), against the oracle on all rows (C2,
+    C3) or sampled heads / sequences (C4: 131072 cached tokens, C5: batch of 8)."""
+    cfg = C[name]
+    say(f"[attn-full] {cfg.name} heads={heads} batch={batch}")
+    case = workloads.make_case(cfg, seed=1)
+    dc = DeviceCase(case)
+    out, lse = dc.attn()
+    torch.cuda.synchronize()
+    ma, rel, le = check_attention(case, out, lse, heads=heads, batch=batch)
+    say(f"    max_abs={ma:.3g} rel={rel:.3g} lse={le:.3g}")
+    out2, lse2 = dc.attn()
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+def test_attention_repeatable(sv):
+    case = workloads.make_case(_small("C2", ctx=600), seed=9)
+    dc = DeviceCase(case)
+    o1, l1 = dc.attn()
+    o2, l2 = dc.attn()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ---------------------------------------------------------------------------
+# greedy acceptance
+# ---------------------------------------------------------------------------
+
+ACCEPT_CASES = [
+    ("C1", C["C1"], {}),
+    ("C2 full vocab", _small("C2", ctx=8, vocab=151936), {}),
+    ("C2 perfect", _small("C2", ctx=8, vocab=151936), {"variant": "perfect"}),
+    ("C3 tree22", _small("C3", ctx=8, vocab=151936), {}),
+    ("C3 tree23 rescue", _small("C3", ctx=8, vocab=151936, n_nodes=23), {"force_first_mismatch": True}),
+    ("C4 block16", _small("C4", ctx=8, vocab=151936), {}),
+    ("C5 batch8", _small("C5", ctx=8, ctx_hi=20, vocab=151936), {}),
+    ("odd vocab f32", workloads.Config("oddv", 3, 2, 1, 64, 7, "f32", "f32", "f32", 4099, 8,
+                                       tree="ddtree", draft_rule="tree"), {}),
+    ("odd vocab bf16", workloads.Config("oddb", 2, 2, 1, 64, 64, "bf16", "bf16", "bf16", 12345, 8,
+                                        tree="ddtree", draft_rule="tree"), {}),
+]
+
+
+@pytest.mark.parametrize("label,cfg,kw", ACCEPT_CASES, ids=[c[0] for c in ACCEPT_CASES])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_greedy_accept(sv, label, cfg, kw, seed):
+    say(f"[accept] {label} seed={seed}")
+    case = workloads.make_case(cfg, seed=77 + seed, **kw)
+    dc = DeviceCase(case)
+    acc, path, tok, am = dc.accept()
+    torch.cuda.synchronize()
+    r_am, r_acc, r_path, r_tok = oracle_accept(case)
+    np.testing.assert_array_equal(am.cpu().numpy(), r_am)
+    np.testing.assert_array_equal(acc.cpu().numpy(), r_acc)
+    np.testing.assert_array_equal(path.cpu().numpy(), r_path)
+    np.testing.assert_array_equal(tok.cpu().numpy(), r_tok)
+    # the planted maxima are what both found
+    np.testing.assert_array_equal(r_am, case.target)
+
+
+def test_argmax_natural_and_planted_ties(sv):
+    """Unplanted bf16 N(0,2) rows (frequent natural ties) plus planted ties that
+    straddle lanes, waves and workgroup chunks: lowest index wins."""
+    rng = np.random.default_rng(4)
+    B, N, V = 2, 40, 151936
+    x = rng.standard_normal((B, N, V)).astype(np.float32) * np.float32(np.sqrt(2))
+    bits = workloads.bf16_bits(x)
+    w = oracle.widen_bf16(bits)
+    plants = [(0, 0, [7, 8]), (0, 1, [4095, 4096]), (0, 2, [63, 64, 65]), (0, 3, [V - 1, 1]),
+              (1, 5, [2047, 2048, 6000]), (1, 6, [0, V - 1]), (1, 7, [8191, 8192])]
+    for b, i, idx in plants:
+        top = np.float32(w[b, i].max() + 1.0)
+        bits[b, i, idx] = workloads.bf16_bits(np.array([top], np.float32))[0]
+    parent = np.stack([workloads.ddtree_parent(rng, N) for _ in range(B)])
+    lg = oracle.widen_bf16(bits)
+    r_am = np.array([[oracle.argmax_first(lg[b, i]) for i in range(N)] for b in range(B)])
+    drafts = np.stack([workloads.drafts_from_targets(rng, parent[b], r_am[b], V, rng.random(N) < 0.7)
+                       for b in range(B)])
+    import draft_token_verification_sv_amd as m
+    from sv_harness import dev_tensor
+    acc, path, tok, am = m.greedy_accept(dev_tensor(bits, "bf16"), dev_tensor(drafts, "i32"),
+                                         dev_tensor(parent, "i32"))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(am.cpu().numpy(), r_am)
+    _, r_acc, r_path, r_tok = oracle.greedy_accept(lg, drafts, parent)
+    np.testing.assert_array_equal(acc.cpu().numpy(), r_acc)
+    np.testing.assert_array_equal(path.cpu().numpy(), r_path)
+    np.testing.assert_array_equal(tok.cpu().numpy(), r_tok)
+
+
+def test_accept_repeated_calls_and_chunk_sizes(sv):
+    """The workspace counters return to zero: many calls in a row, different
+    shapes and chunk sizes, stay exact."""
+    for k, (chunk, cfg) in enumerate([(4096, _small("C3", ctx=8, vocab=151936)),
+                                      (8, _small("C2", ctx=8, vocab=1000)),
+                                      (1024, _small("C5", ctx=8, ctx_hi=9, vocab=151936)),
+                                      (65536, _small("C3", ctx=8, vocab=70000))]):
+        prev = sv.set_option(sv.SV_OPT_ARGMAX_CHUNK, chunk)
+        try:
+            for rep in range(3):
+                case = workloads.make_case(cfg, seed=300 + 10 * k + rep)
+                dc = DeviceCase(case)
+                acc, path, tok, am = dc.accept(workspace=None)
+                torch.cuda.synchronize()
+                r_am, r_acc, r_path, r_tok = oracle_accept(case)
+                np.testing.assert_array_equal(am.cpu().numpy(), r_am)
+                np.testing.assert_array_equal(path.cpu().numpy(), r_path)
+                np.testing.assert_array_equal(tok.cpu().numpy(), r_tok)
+        finally:
+            sv.set_option(sv.SV_OPT_ARGMAX_CHUNK, prev)
+
+
+# ---------------------------------------------------------------------------
+# compaction
+# ---------------------------------------------------------------------------
+
+COMPACT_CASES = [
+    ("C2 chain bf16 3 layers", _small("C2", ctx=50), 3, {}),
+    ("C3 tree bf16", _small("C3", ctx=60), 2, {}),
+    ("C3 tree rescue", _small("C3", ctx=61, n_nodes=23), 1, {"force_first_mismatch": True}),
+    ("C4 q4 chain", _small("C4", ctx=70), 2, {}),
+    ("C5 paged", _small("C5", ctx=30, ctx_hi=100), 2, {}),
+    ("C1 f32", C["C1"], 1, {}),
+    ("tree q4 paged", workloads.Config("tqp", 3, 8, 2, 128, 20, "bf16", "q4", "bf16", 300, 20, ctx_hi=70,
+                                       tree="ddtree", paged=True, draft_rule="tree"), 2, {}),
+    ("tree perfect f32", workloads.Config("tpf", 2, 4, 2, 64, 30, "f32", "f32", "f32", 200, 9,
+                                          tree="ddtree", draft_rule="tree"), 1, {"variant": "perfect"}),
+]
+
+
+@pytest.mark.parametrize("label,cfg,layers,kw", COMPACT_CASES, ids=[c[0] for c in COMPACT_CASES])
+def test_kv_compact(sv, label, cfg, layers, kw):
+    say(f"[compact] {label}")
+    case = workloads.make_case(cfg, seed=21, capacity_pad=4, n_layers=layers, **kw)
+    dc = DeviceCase(case)
+    before = dc.cache_arrays_host()
+    acc, path, tok, am = dc.accept()
+    new_lens = sv.kv_compact(dc.kv, dc.ctx, dc.max_ctx, path, acc)
+    torch.cuda.synchronize()
+    after = dc.cache_arrays_host()
+    _, r_acc, r_path, _ = oracle_accept(case)
+    np.testing.assert_array_equal(acc.cpu().numpy(), r_acc)
+    lay = (lambda a: a[None]) if layers == 1 else (lambda a: a)
+    exp, r_new, _ = oracle.compact_cache([lay(a) for a in before], ctx_lens=case.ctx_lens, path=r_path,
+                                         accept_len=r_acc,
+                                         page_table=case.page_table if cfg.paged else None,
+                                         page_size=cfg.page_size)
+    for e, g in zip(exp, after):
+        np.testing.assert_array_equal(lay(g), e)
+    np.testing.assert_array_equal(new_lens.cpu().numpy(), r_new)
+
+
+def test_verify_step_end_to_end(sv):
+    """attention -> acceptance -> compaction, twice, on a paged batch."""
+    cfg = _small("C5", ctx=40, ctx_hi=300, vocab=3001)
+    case = workloads.make_case(cfg, seed=8, capacity_pad=8)
+    dc = DeviceCase(case)
+    for step in range(2):
+        say(f"[step] {step}")
+        arrs = dc.cache_arrays_host()
+        case.k, case.v = arrs[0], arrs[1]       # the oracle reads the cache as it is now
+        out, lse = dc.attn()
+        acc, path, tok, am = dc.accept()
+        before = dc.cache_arrays_host()
+        new_lens = sv.kv_compact(dc.kv, dc.ctx, dc.max_ctx, path, acc)
+        torch.cuda.synchronize()
+        check_attention(case, out, lse)
+        r_am, r_acc, r_path, r_tok = oracle_accept(case)
+        np.testing.assert_array_equal(tok.cpu().numpy(), r_tok)
+        exp, r_new, _ = oracle.compact_cache([a[None] for a in before], ctx_lens=case.ctx_lens, path=r_path,
+                                             accept_len=r_acc, page_table=case.page_table,
+                                             page_size=cfg.page_size)
+        for e, g in zip(exp, dc.cache_arrays_host()):
+            np.testing.assert_array_equal(g[None], e)
+        np.testing.assert_array_equal(new_lens.cpu().numpy(), r_new)
