@@ -14,10 +14,14 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libsv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["sv_api.cpp", "attn_mfma.hip", "attn_valu.hip", "accept.hip", "compact.hip"]
+SOURCES = ["sv_api.cpp", "attn_dma.hip", "attn_mfma.hip", "attn_valu.hip", "accept.hip", "compact.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in VGPRs: the online softmax rescales them with
+    # vector ALU ops, and the AGPR form made the compiler copy every
+    # accumulator AGPR -> VGPR on each loop iteration
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -7,14 +7,22 @@
 // reads budget+1 logits rows, "Key breakthroughs"].
 //
 // One launch.  Workgroup (row, chunk) streams `chunk` logits of one row with
-// 16-byte loads and reduces them to a 64-bit key
+// 16-byte loads (all of a thread's loads in flight at once) and reduces them
+// to a 64-bit key
 //     (order-preserving fp32 bits << 32) | (0xFFFFFFFF - index),
-// whose maximum is the largest value at the lowest index.  The key is stored
-// to the workspace, then a per-sequence counter is incremented; the workgroup
-// that brings the counter to N * chunks (the last one of that sequence) reads
-// all keys of the sequence, runs the acceptance walk for its <= 64 nodes in
-// one wavefront, writes the outputs and sets its keys and counter back to
-// zero, so the whole workspace is zero between calls of any shape.
+// whose maximum is the largest value at the lowest index.  Completion is
+// tracked with device-scope atomics only (no cache flushes):
+//   1. atomic max of the key into keys[row]; wait for its return;
+//   2. add 1 to rows_done[row]; the workgroup that completes the row (the
+//      last of its `chunks` arrivals) sets that counter back to zero and adds
+//      1 to seqs_done[b];
+//   3. the workgroup that completes sequence b (the N-th row) takes every
+//      key of the sequence with an atomic exchange against zero, runs the
+//      acceptance walk for its <= 64 nodes in one wavefront and writes the
+//      outputs.
+// Each step is issued only after the previous atomic has returned, and all of
+// them act on the device-coherent copy, so the last workgroup sees every
+// key.  Every call leaves the keys and counters it used at zero.
 #include "device_common.h"
 
 namespace sv {
@@ -41,6 +49,10 @@ __device__ __forceinline__ unsigned long long wave_max64(unsigned long long k) {
     return k;
 }
 
+// vmcnt(0): every vector memory operation of this wave (the atomics above
+// included, their results returned) has completed
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <bool F32, bool VEC>
 __global__ __launch_bounds__(256) void argmax_accept_kernel(AcceptParams p) {
     __shared__ unsigned long long red[4];
@@ -54,66 +66,93 @@ __global__ __launch_bounds__(256) void argmax_accept_kernel(AcceptParams p) {
     const int64_t V = p.V;
     const int64_t lo = (int64_t)c * p.chunk;
     const int64_t hi = min<int64_t>(V, lo + p.chunk);
+    constexpr int EPL = F32 ? 4 : 8;                      // elements per 16-byte load
+    constexpr int UNR = 4;                                // loads in flight per thread
 
     unsigned long long best = 0ull;
-    if constexpr (F32) {
-        const float *rowp = (const float *)p.logits + (int64_t)row * V;
-        if constexpr (VEC) {
-            for (int64_t e = lo + tid * 4; e < hi; e += 256 * 4) {
-                const f32x4 v = *(const f32x4 *)(rowp + e);
+    if constexpr (VEC) {
+        // full groups of UNR loads, then the rest one load at a time
+        const void *base = F32 ? (const void *)((const float *)p.logits + (int64_t)row * V)
+                               : (const void *)((const uint16_t *)p.logits + (int64_t)row * V);
+        int64_t e = lo + (int64_t)tid * EPL;
+        for (; e + (int64_t)(UNR - 1) * 256 * EPL < hi; e += (int64_t)UNR * 256 * EPL) {
+            u32x4 v[UNR];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) best = umax64(best, make_key(v[t], (uint32_t)(e + t)));
-            }
-        } else {
-            for (int64_t e = lo + tid; e < hi; e += 256) best = umax64(best, make_key(rowp[e], (uint32_t)e));
-        }
-    } else {
-        const uint16_t *rowp = (const uint16_t *)p.logits + (int64_t)row * V;
-        if constexpr (VEC) {
-            for (int64_t e = lo + tid * 8; e < hi; e += 256 * 8) {
-                const u32x4 v = *(const u32x4 *)(rowp + e);
+            for (int k = 0; k < UNR; ++k)
+                v[k] = *(const u32x4 *)((const uint8_t *)base + (e + (int64_t)k * 256 * EPL) * (F32 ? 4 : 2));
+#pragma unroll
+            for (int k = 0; k < UNR; ++k) {
+                const uint32_t i0 = (uint32_t)(e + (int64_t)k * 256 * EPL);
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
+                    if constexpr (F32) {
+                        best = umax64(best, make_key(__uint_as_float(v[k][t]), i0 + t));
+                    } else {
+                        best = umax64(best, make_key(bf16_bits_to_f32(v[k][t] & 0xFFFFu), i0 + 2 * t));
+                        best = umax64(best, make_key(bf16_bits_to_f32(v[k][t] >> 16), i0 + 2 * t + 1));
+                    }
+                }
+            }
+        }
+        for (; e < hi; e += 256 * EPL) {
+            const u32x4 v = *(const u32x4 *)((const uint8_t *)base + e * (F32 ? 4 : 2));
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                if constexpr (F32) {
+                    best = umax64(best, make_key(__uint_as_float(v[t]), (uint32_t)(e + t)));
+                } else {
                     best = umax64(best, make_key(bf16_bits_to_f32(v[t] & 0xFFFFu), (uint32_t)(e + 2 * t)));
                     best = umax64(best, make_key(bf16_bits_to_f32(v[t] >> 16), (uint32_t)(e + 2 * t + 1)));
                 }
             }
-        } else {
-            for (int64_t e = lo + tid; e < hi; e += 256)
-                best = umax64(best, make_key(bf16_bits_to_f32(rowp[e]), (uint32_t)e));
         }
+    } else if constexpr (F32) {
+        const float *rowp = (const float *)p.logits + (int64_t)row * V;
+        for (int64_t e = lo + tid; e < hi; e += 256) best = umax64(best, make_key(rowp[e], (uint32_t)e));
+    } else {
+        const uint16_t *rowp = (const uint16_t *)p.logits + (int64_t)row * V;
+        for (int64_t e = lo + tid; e < hi; e += 256)
+            best = umax64(best, make_key(bf16_bits_to_f32(rowp[e]), (uint32_t)e));
     }
     best = wave_max64(best);
     if ((tid & 63) == 0) red[tid >> 6] = best;
     __syncthreads();
     if (tid == 0) {
         const unsigned long long k = umax64(umax64(red[0], red[1]), umax64(red[2], red[3]));
-        p.keys[(int64_t)row * p.n_chunks + c] = k;
-        __threadfence();
-        const unsigned int prev = atomicAdd(&p.counters[b], 1u);
-        last_s = (prev == (unsigned int)(p.N * p.n_chunks - 1));
+        int last = 0;
+        const unsigned long long was =
+            __hip_atomic_fetch_max(&p.keys[row], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // consuming `was` keeps the returning form of the atomic, whose
+        // result comes back only once it has been performed
+        asm volatile("" : : "v"((uint32_t)was));
+        wait_vm0();
+        const unsigned int rd =
+            __hip_atomic_fetch_add(&p.rows_done[row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (rd == (unsigned int)(p.n_chunks - 1)) {
+            __hip_atomic_store(&p.rows_done[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const unsigned int sd =
+                __hip_atomic_fetch_add(&p.seqs_done[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last = sd == (unsigned int)(p.N - 1);
+        }
+        last_s = last;
     }
     __syncthreads();
     if (!last_s) return;
 
-    // ---- last workgroup of sequence b: reduce keys, then walk ----------------
-    __threadfence();
+    // ---- the workgroup that completed sequence b: take keys, then walk --------
     const int N = p.N;
     const int wave = tid >> 6, lane = tid & 63;
-    for (int i = wave; i < N; i += 4) {
-        const unsigned long long *kp = p.keys + ((int64_t)b * N + i) * p.n_chunks;
-        unsigned long long k = 0ull;
-        for (int cc = lane; cc < p.n_chunks; cc += 64)
-            k = umax64(k, __hip_atomic_load(kp + cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        k = wave_max64(k);
-        if (lane == 0) am_s[i] = (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
-    }
-    if (tid < N) {
-        dr_s[tid] = p.draft[(int64_t)b * N + tid];
-        par_s[tid] = p.parent[(int64_t)b * N + tid];
-    }
-    __syncthreads();
     if (wave != 0) return;
+    if (lane < N) {
+        const unsigned long long k =
+            __hip_atomic_exchange(&p.keys[(int64_t)b * N + lane], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        am_s[lane] = (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+        dr_s[lane] = p.draft[(int64_t)b * N + lane];
+        par_s[lane] = p.parent[(int64_t)b * N + lane];
+    }
+    if (lane == 0) __hip_atomic_store(&p.seqs_done[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);           // the LDS writes of all lanes (one wave: no barrier)
+    __builtin_amdgcn_wave_barrier();
 
     // node `lane`: accepted iff every edge of its root path is accepted
     int acc = 0, depth = 0;
@@ -153,11 +192,6 @@ __global__ __launch_bounds__(256) void argmax_accept_kernel(AcceptParams p) {
         tok[lane] = -1;
     }
     if (p.argmax != nullptr && lane < N) p.argmax[(int64_t)b * N + lane] = am_s[lane];
-    // leave this sequence's part of the workspace zero again: its keys (a later
-    // call with another shape may place its counters there) and its counter
-    unsigned long long *kz = p.keys + (int64_t)b * N * p.n_chunks;
-    for (int e = lane; e < N * p.n_chunks; e += 64) kz[e] = 0ull;
-    if (lane == 0) __hip_atomic_store(&p.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace

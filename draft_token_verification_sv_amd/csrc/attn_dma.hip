@@ -1,0 +1,493 @@
+// Split-KV verify attention over a bf16 KV cache on gfx950: direct-to-LDS
+// multi-stage pipeline + bf16 matrix cores.
+//
+// One workgroup (4 waves) handles one (sequence, KV head, row block, split).
+// Packed query rows of a KV head are r = node * G + g: the verify rows of all
+// query heads of the GQA group [single-RTX-3090 DFlash note: 24 Q / 4 KV heads
+// of dim 256, "Why we ran this test"; 16-row blocks, "Architecture"; budget+1
+// tree rows, "Key breakthroughs"].  A wave owns up to NT tiles of 16 rows; when
+// a block has a single row tile, PG waves split each stage's positions.
+//
+// Memory pipeline.  A stage is T = 32 * PG consecutive key positions: the K
+// rows then the V rows, both in their natural [pos][d] order, 16-byte chunks
+// XOR-swizzled per row.  Stages are fetched with global_load_lds_dwordx4 (each
+// lane's 16 bytes land at M0 + 16 * lane), issued from inline assembly so the
+// compiler does not drain them before every LDS read; an S-deep ring keeps
+// S - 1 stages in flight and each wave waits on its own vmcnt for exactly the
+// stage it is about to use.  No registers stage the data and nothing is
+// transposed on the way in.
+//
+// Math per 32-position chunk (16x16x32 bf16 MFMA):
+//   S^T = K Q^T    A = K rows from LDS (one ds_read_b128 per k-step),
+//                  B = the wave's query fragments held in registers;
+//   online softmax in log2 units, per lane one row and 8 positions; the
+//   reference maximum is refreshed only when a row's maximum grows by more
+//   than 2^8 (numerator and denominator share it, so this is exact);
+//   O^T += V^T P^T  A = V^T fragments read with ds_read_b64_tr_b16 (within a
+//                  16-lane group, lane i receives element i % 4 of the 4-value
+//                  runs read by lanes 4k + i/4, k = 0..3: two such reads give a
+//                  lane 8 positions of one head-dim column straight from the
+//                  natural V layout), B = the probabilities already in place.
+// Tree mask [DFN "From autoregressive to DDTree"; chains: causal mask aligned
+// to the end of the keys, xdnf.cn notes section 5.3]: 64-bit ancestor sets in
+// LDS, applied on chunks that reach the draft rows.
+// Output: unnormalised partials (O, m, l) per row for the split merge.
+#include "attn_sched.h"
+
+#ifndef SV_SWZ_W
+#define SV_SWZ_W 16
+#endif
+
+namespace sv {
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+template <int D, int NT, int PG>
+struct DCfg {
+    static constexpr int W = D >= 128 ? SV_SWZ_W : 8;          // swizzle width (chunks)
+    static constexpr int T = 32 * PG;                 // positions per stage
+    static constexpr int ROWB = D * 2;                // bytes per K / V row
+    static constexpr int KBYTES = T * ROWB;           // K part of a stage
+    static constexpr int STAGE = 2 * KBYTES;
+    static constexpr int S_RAW = 131072 / STAGE;
+    static constexpr int S = S_RAW < 2 ? 2 : (S_RAW > 8 ? 8 : S_RAW);   // ring depth
+    static constexpr int NKB = STAGE / 1024;          // 1 KB DMA instructions per stage
+    static constexpr int LPW = NKB / 4;               // per wave
+    static constexpr int RPK = 1024 / ROWB;           // rows per DMA instruction
+    static constexpr int RG = 4 / PG;
+    static constexpr int KS = D / 32;
+    static constexpr int DT = D / 16;
+    static_assert(NKB % 8 == 0, "stage split evenly between waves and K/V");
+    static_assert(LPW * (S - 2) < 64, "vmcnt range");
+};
+
+// Chunk swizzle shared by the K (16-byte) and V (transposed 8-byte) reads.  A
+// K fragment read touches 16 rows {8a + b : a, b < 4} (+4t) at one logical
+// chunk; a V transposed read touches rows 8q + 4h + b (b < 4) at two adjacent
+// chunks.  W = 16 spreads the 16 K rows over 16 distinct 16-byte bank groups
+// and each 8-row half of the V rows over 8 distinct pairs (head dims >= 128,
+// i.e. >= 16 chunks per row); W = 8 is the 3-bit form for 8 chunks per row.
+template <int W>
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (W == 16) return ((row & 3) << 1) | (((row >> 3) & 1) << 3) | ((row >> 4) & 1);
+    return ((row & 3) << 1) | ((row >> 3) & 1);
+}
+
+// s_waitcnt vmcnt(N) with expcnt / lgkmcnt left alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int STEP, int K>
+__device__ __forceinline__ void wait_vm_dyn(int k) {
+    if constexpr (K < 0) {
+        wait_vm<0>();
+    } else {
+        if (k >= K) wait_vm<STEP * K>();
+        else wait_vm_dyn<STEP, K - 1>(k);
+    }
+}
+
+__device__ __forceinline__ void dma16(uint32_t lds_base, const void *gptr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds_base), "v"(gptr)
+                 : "memory", "m0");
+}
+
+constexpr int kMaxSplitPages = 512;
+
+template <int D, int NT, int PG, bool PAGED>
+__global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
+    using C = DCfg<D, NT, PG>;
+    constexpr int T = C::T, S = C::S;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[S * C::STAGE];
+    __shared__ int par_s[64];
+    __shared__ uint64_t anc_s[64];
+    __shared__ int pages_s[PAGED ? kMaxSplitPages : 1];
+
+    __shared__ SchedLds sched_s;
+
+    // ---- unit: (b, kv head, row block, split); row blocks of one (b, head,
+    // split) get ids 8 apart, i.e. the same XCD and L2 ---------------------
+    const int id = blockIdx.x;
+    const int xcd = id & 7, k8 = id >> 3;
+    const int rb = k8 % p.n_rowblocks;
+    AttnUnit wu;
+    if (!attn_unit(p, (k8 / p.n_rowblocks) * 8 + xcd, rb == 0, sched_s, wu)) return;
+    const int b = wu.b, kvh = wu.kvh;
+    const int N = p.N, G = p.G, R = p.R;
+    const int ctx = wu.ctx, p0 = wu.p0, p1 = wu.p1;
+    const int n_st = (p1 - p0 + T - 1) / T;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave-uniform
+    const int rg = wave % C::RG, pg = wave / C::RG;
+    const int l16 = lane & 15, qd = lane >> 4;
+
+    // ---- tree (only splits that reach the draft rows) and page ids ---------
+    const bool has_draft = p1 > ctx;
+    if (has_draft && tid < N) par_s[tid] = p.parent[(int64_t)b * N + tid];
+    int first_page = 0;
+    const int ps_shift = (p.kv.page_size > 0 && (p.kv.page_size & (p.kv.page_size - 1)) == 0)
+                             ? __builtin_ctz((unsigned)p.kv.page_size) : -1;
+    if constexpr (PAGED) {
+        first_page = p0 / p.kv.page_size;
+        const int last_page = (p1 - 1) / p.kv.page_size;
+        for (int e = tid; e <= last_page - first_page; e += 256) {
+            int pgid = p.kv.page_table[(int64_t)b * p.kv.max_pages + first_page + e];
+            pgid = pgid < 0 ? 0 : (pgid >= p.kv.capacity ? (int)p.kv.capacity - 1 : pgid);
+            pages_s[e] = pgid;
+        }
+    }
+    __syncthreads();
+    if (has_draft && tid < N) anc_s[tid] = ancestor_bits(par_s, tid);   // visible after the loop's first barrier
+
+    // ---- DMA issue: instruction j of this wave covers 1 KB of the stage ------
+    const uint8_t *kbase = (const uint8_t *)p.kv.k;
+    const uint8_t *vbase = (const uint8_t *)p.kv.v;
+    const int64_t head_row0 = ((int64_t)b * p.Hkv + kvh) * p.kv.capacity;   // contiguous
+    const uint32_t ring_u32 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)ring;
+
+    // Lane constants of DMA instruction j: row within the stage and byte offset
+    // of its (swizzled) 16-byte chunk.
+    int dma_row[C::LPW];
+    uint32_t dma_off[C::LPW];
+#pragma unroll
+    for (int j = 0; j < C::LPW; ++j) {
+        const int kbi = wave * C::LPW + j;
+        const int kb_in = kbi >= C::NKB / 2 ? kbi - C::NKB / 2 : kbi;
+        const int row = kb_in * C::RPK + (lane * 16) / C::ROWB;
+        const int chunk = ((lane * 16) % C::ROWB / 16) ^ swz<C::W>(row);
+        dma_row[j] = row;
+        dma_off[j] = (uint32_t)(row * C::ROWB + chunk * 16);
+    }
+
+    auto issue = [&](int st) {
+        const int tb = p0 + st * T;
+        const uint32_t slot = ring_u32 + (uint32_t)((st % S) * C::STAGE);
+        const bool full = tb + T <= p1;                          // uniform
+#pragma unroll
+        for (int j = 0; j < C::LPW; ++j) {
+            const int kbi = wave * C::LPW + j;                     // wave-uniform
+            const bool is_v = kbi >= C::NKB / 2;
+            const uint8_t *g;
+            if constexpr (!PAGED) {
+                if (full) {
+                    g = (is_v ? vbase : kbase) + (head_row0 + tb) * C::ROWB + dma_off[j];
+                } else {
+                    const int pos = min(tb + dma_row[j], p1 - 1);
+                    g = (is_v ? vbase : kbase) + (head_row0 + pos) * C::ROWB +
+                        (dma_off[j] - (uint32_t)(dma_row[j] * C::ROWB));
+                }
+            } else {
+                const int ps = p.kv.page_size;
+                const int pos = min(tb + dma_row[j], p1 - 1);
+                int pq, pr;
+                if (ps_shift >= 0) {
+                    pq = pos >> ps_shift;
+                    pr = pos & (ps - 1);
+                } else {
+                    pq = pos / ps;
+                    pr = pos - pq * ps;
+                }
+                const int pgid = pages_s[pq - first_page];
+                const int64_t ri = ((int64_t)pgid * p.Hkv + kvh) * ps + pr;
+                g = (is_v ? vbase : kbase) + ri * C::ROWB + (dma_off[j] - (uint32_t)(dma_row[j] * C::ROWB));
+            }
+            dma16(__builtin_amdgcn_readfirstlane(slot + (uint32_t)(kbi * 1024)), g);
+        }
+    };
+
+    // ---- pipeline prologue: the first stages go out before the query loads, so
+    // their latencies overlap ----------------------------------------------------
+    const int pro = min(S - 1, n_st);
+    for (int st = 0; st < pro; ++st) issue(st);
+
+    // ---- query fragments and accumulators ------------------------------------
+    const int row0 = rb * p.rows_per_block;
+    const int rows_here = min(p.rows_per_block, R - row0);
+    bool tile_on[NT];
+    int node_of[NT];
+    bf16x8 qf[NT][C::KS];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const int rt = rg + C::RG * i;
+        tile_on[i] = rt * 16 < rows_here;
+        const int r = row0 + rt * 16 + l16;
+        const bool ok = tile_on[i] && (rt * 16 + l16) < rows_here;
+        node_of[i] = ok ? r / G : -1;
+        if (ok) {
+            const int n = r / G, g = r % G;
+            const __bf16 *qp = (const __bf16 *)p.q +
+                               (((int64_t)b * N + n) * p.Hq + (int64_t)kvh * G + g) * D + qd * 8;
+#pragma unroll
+            for (int k = 0; k < C::KS; ++k) qf[i][k] = *(const bf16x8 *)(qp + 32 * k);
+        } else {
+#pragma unroll
+            for (int k = 0; k < C::KS; ++k) {
+                const bf16x8 z = {};
+                qf[i][k] = z;
+            }
+        }
+    }
+    f32x4 o[NT][C::DT];
+    float m_ref[NT], l_sum[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        m_ref[i] = -INFINITY;
+        l_sum[i] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) o[i][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // Lane constants of the LDS fragment reads.  K rows read by a lane are
+    // 8 * (l16 / 4) + (l16 % 4) (+ 4t); V rows 8 * qd + l16 / 4 (+ 4hh); with a
+    // chunk base that is a multiple of 32 rows their swizzle does not depend on
+    // the chunk, t or hh, so each read is a lane constant plus an immediate.
+    constexpr int W = C::W;
+    const int ksz = swz<W>(8 * (l16 >> 2) + (l16 & 3));
+    const int k_lane = (8 * (l16 >> 2) + (l16 & 3)) * C::ROWB;
+    int k_off[W / 4];                       // K chunk 4k + qd: k % (W/4) varies the XOR
+#pragma unroll
+    for (int kk = 0; kk < W / 4; ++kk) k_off[kk] = ((4 * kk + qd) ^ ksz) * 16;
+    const int vsz = swz<W>(8 * qd + (l16 >> 2));
+    const int vch = (l16 & 3) >> 1;
+    const int v_lane = (8 * qd + (l16 >> 2)) * C::ROWB + (l16 & 1) * 8;
+    int v_off[W / 2];                       // V chunk 2dt + vch: dt % (W/2) varies the XOR
+#pragma unroll
+    for (int dd = 0; dd < W / 2; ++dd) v_off[dd] = ((2 * dd + vch) ^ vsz) * 16;
+
+    // The query loads were issued after the prologue stages; waiting for them
+    // (the compiler would insert the same wait before their first use) also
+    // waits for those stages.
+    wait_vm<0>();
+
+    // ---- main loop ---------------------------------------------------------
+#pragma unroll 1
+    for (int it = 0; it < n_st; ++it) {
+        wait_vm_dyn<C::LPW, S - 2>(min(S - 2, n_st - 1 - it));   // this wave's part of stage `it` landed
+        __syncthreads();                                           // everyone's part landed; slot it-1 free
+        if (it + S - 1 < n_st) issue(it + S - 1);
+
+        const uint8_t *Kl = ring + (it % S) * C::STAGE;
+        const uint8_t *Vl = Kl + C::KBYTES;
+        const int cb = pg * 32;
+        const int abase = p0 + it * T + cb;
+        if (abase >= p1) continue;
+
+        // Every wave runs all NT tile slots: a slot without rows holds zero
+        // queries, gives finite scores and is never written back, and no
+        // branch breaks the stream of matrix instructions (the waves meet at
+        // the next barrier anyway).
+        f32x4 sacc[NT][2];
+        {
+            // K fragment (t, k) sits at k_lane + 4t rows + (k / (W/4)) * 16W bytes
+            // + a lane constant that depends only on k % (W/4)
+            const uint8_t *kp = Kl + cb * C::ROWB + k_lane;
+            bf16x8 kf[2][C::KS];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int k = 0; k < C::KS; ++k)
+                    kf[t][k] = *(const bf16x8 *)(kp + 4 * t * C::ROWB + (k / (W / 4)) * (W * 16) + k_off[k % (W / 4)]);
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < NT; ++i)
+                    sacc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][0], qf[i][0], zero, 0, 0, 0);
+#pragma unroll
+            for (int k = 1; k < C::KS; ++k)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int i = 0; i < NT; ++i)
+                        sacc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][k], qf[i][k], sacc[i][t], 0, 0, 0);
+        }
+
+        const bool need_mask = (abase + 32 > ctx) || (abase + 32 > p1);
+        bf16x8 pb[NT];
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            // raw scores; the softmax scale (log2 units) is applied inside the
+            // exponent, so the maxima below are raw too
+            float sv[8];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sv[4 * t + j] = sacc[i][t][j];
+            if (need_mask) {
+                const uint64_t anc = node_of[i] >= 0 ? anc_s[node_of[i]] : 0ull;
+                const int rel0 = abase + 8 * qd - ctx;      // draft index of value 0
+                const int lim = p1 - (abase + 8 * qd);      // values e < lim are in the split
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int rel = rel0 + e;
+                    bool vis = e < lim;
+                    if (rel >= 0) vis = vis && (((anc >> (rel & 63)) & 1ull) != 0ull);
+                    sv[e] = vis ? sv[e] : -INFINITY;
+                }
+            }
+            // lazy rescale: the reference m_ref (log2 units) moves only when some
+            // score exceeds it by more than 8; a lane's own 8 values decide
+            // whether the wave looks at row maxima at all
+            float cm = sv[0];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) cm = fmaxf(cm, sv[e]);
+            if (__any(cm * p.scale_log2 > m_ref[i] + 8.f)) {
+                cm = fmaxf(cm, xor_shfl(cm, 16));
+                cm = fmaxf(cm, xor_shfl(cm, 32));
+                const float cms = cm * p.scale_log2;
+                const bool need = cms > m_ref[i] + 8.f;
+                const float mn = need ? cms : m_ref[i];
+                const float alpha = need ? exp2f(m_ref[i] - mn) : 1.f;
+                m_ref[i] = mn;
+                l_sum[i] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt) o[i][dt] *= alpha;
+            }
+            const float mu = (m_ref[i] == -INFINITY) ? 0.f : m_ref[i];
+            float ls = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                // 2^(s * scale - m): v_exp_f32 (results below 2^-126 flush to 0)
+                const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], p.scale_log2, -mu));
+                ls += pr;
+                pb[i][e] = (__bf16)pr;
+            }
+            l_sum[i] += ls;
+        }
+
+        // O^T += V^T P^T: V^T fragments by transposed reads of the natural layout;
+        // fragment (dt, hh) sits at v_lane + 4hh rows + (dt / (W/2)) * 16W bytes +
+        // a lane constant that depends only on dt % (W/2)
+        const uint8_t *vp = Vl + cb * C::ROWB + v_lane;
+        constexpr int VB = C::DT < 8 ? C::DT : 8;                 // fragments per batch
+#pragma unroll
+        for (int d0 = 0; d0 < C::DT; d0 += VB) {
+            bf16x8 vf[VB];
+#pragma unroll
+            for (int dd = 0; dd < VB; ++dd) {
+                const int dt = d0 + dd;
+                s16x4 h[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4 *)(__attribute__((address_space(3))) uint8_t *)(
+                            vp + 4 * hh * C::ROWB + (dt / (W / 2)) * (W * 16) + v_off[dt % (W / 2)]));
+                const short __attribute__((ext_vector_type(8))) w8 = {h[0][0], h[0][1], h[0][2], h[0][3],
+                                                                      h[1][0], h[1][1], h[1][2], h[1][3]};
+                vf[dd] = __builtin_bit_cast(bf16x8, w8);
+            }
+#pragma unroll
+            for (int dd = 0; dd < VB; ++dd)
+#pragma unroll
+                for (int i = 0; i < NT; ++i)
+                    o[i][d0 + dd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dd], pb[i], o[i][d0 + dd], 0, 0, 0);
+        }
+    }
+
+    // ---- combine position groups (PG > 1) through LDS --------------------------
+    if constexpr (PG > 1) {
+        __syncthreads();
+        f32x4 *buf = (f32x4 *)ring;
+        constexpr int SLOT = C::DT + 1;
+        static_assert((PG - 1) * C::RG * NT * SLOT * 64 * 16 <= S * C::STAGE, "combine buffer");
+        if (pg > 0) {
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+                const int slot = ((pg - 1) * C::RG + rg) * NT + i;      // own slot per (group, row group)
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt) buf[(slot * SLOT + dt) * 64 + lane] = o[i][dt];
+                buf[(slot * SLOT + C::DT) * 64 + lane] = f32x4{m_ref[i], l_sum[i], 0.f, 0.f};
+            }
+        }
+        __syncthreads();
+        if (pg > 0) return;
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            float mx = m_ref[i];
+            for (int q2 = 1; q2 < PG; ++q2)
+                mx = fmaxf(mx, buf[((((q2 - 1) * C::RG + rg) * NT + i) * SLOT + C::DT) * 64 + lane][0]);
+            const float w0 = (m_ref[i] == -INFINITY) ? 0.f : exp2f(m_ref[i] - mx);
+            l_sum[i] *= w0;
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt) o[i][dt] *= w0;
+            for (int q2 = 1; q2 < PG; ++q2) {
+                const int slot = ((q2 - 1) * C::RG + rg) * NT + i;
+                const f32x4 ml = buf[(slot * SLOT + C::DT) * 64 + lane];
+                const float w = (ml[0] == -INFINITY) ? 0.f : exp2f(ml[0] - mx);
+                l_sum[i] += w * ml[1];
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt) o[i][dt] += w * buf[(slot * SLOT + dt) * 64 + lane];
+            }
+            m_ref[i] = mx;
+        }
+    }
+
+    // ---- partials of this split --------------------------------------------------
+    const int64_t part = wu.part;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        if (!tile_on[i]) continue;
+        float ls = l_sum[i];
+        ls += xor_shfl(ls, 16);
+        ls += xor_shfl(ls, 32);
+        const int rl = (rg + C::RG * i) * 16 + l16;
+        if (rl >= rows_here) continue;
+        const int r = row0 + rl;
+        float *op = p.part_o + (part * R + r) * D + qd * 4;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) *(f32x4 *)(op + 16 * dt) = o[i][dt];
+        if (qd == 0) {
+            p.part_ml[(part * R + r) * 2 + 0] = m_ref[i];
+            p.part_ml[(part * R + r) * 2 + 1] = ls;
+        }
+    }
+}
+
+template <int D, int NT, int PG, bool PAGED>
+hipError_t launch_one(const AttnParams &p, hipStream_t st) {
+    const int grid = ((p.n_units + 7) / 8) * 8 * p.n_rowblocks;
+    hipLaunchKernelGGL((attn_dma_kernel<D, NT, PG, PAGED>), dim3(grid), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+template <int D, bool PAGED>
+hipError_t launch_shape(const AttnParams &p, int nt, int pg, hipStream_t st) {
+    if (pg == 1) {
+        if (nt == 1) return launch_one<D, 1, 1, PAGED>(p, st);
+        if (nt == 2) return launch_one<D, 2, 1, PAGED>(p, st);
+        if (nt == 3) return launch_one<D, 3, 1, PAGED>(p, st);
+    } else if (nt == 1 && pg == 2) {
+        return launch_one<D, 1, 2, PAGED>(p, st);
+    } else if (nt == 1 && pg == 4 && D <= 128) {
+        return launch_one<D, 1, (D <= 128 ? 4 : 2), PAGED>(p, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int D>
+hipError_t launch_d(const AttnParams &p, int nt, int pg, hipStream_t st) {
+    return p.kv.page_table != nullptr ? launch_shape<D, true>(p, nt, pg, st)
+                                      : launch_shape<D, false>(p, nt, pg, st);
+}
+
+}  // namespace
+
+int attn_dma_max_split_pages() { return kMaxSplitPages; }
+
+hipError_t launch_attn_dma(const AttnParams &p, int D, int nt, int pg, hipStream_t st) {
+    switch (D) {
+        case 64: return launch_d<64>(p, nt, pg, st);
+        case 128: return launch_d<128>(p, nt, pg, st);
+        case 256: return launch_d<256>(p, nt, pg, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace sv

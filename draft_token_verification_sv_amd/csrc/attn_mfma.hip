@@ -29,7 +29,7 @@
 //
 // Output per workgroup: unnormalised partials (O, m, l) per row; the merge
 // kernel combines the splits.
-#include "device_common.h"
+#include "attn_sched.h"
 
 namespace sv {
 namespace {
@@ -63,24 +63,19 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnParams p) {
     uint8_t *const Kl = lds;
     uint8_t *const Vl = lds + C::LDS_K;
 
+    __shared__ SchedLds sched_s;
+
     // ---- which unit: (b, kv head, row block, split) ------------------------
     // Row blocks of one (b, kv head, split) get ids 8 apart: the dispatcher
     // deals ids round-robin to the 8 XCDs, so they share an L2.
     const int id = blockIdx.x;
     const int xcd = id & 7, k8 = id >> 3;
     const int rb = k8 % p.n_rowblocks;
-    const int u = (k8 / p.n_rowblocks) * 8 + xcd;
-    if (u >= p.B * p.Hkv * p.n_splits) return;
-    const int s = u % p.n_splits;
-    const int bh = u / p.n_splits;
-    const int kvh = bh % p.Hkv, b = bh / p.Hkv;
-
+    AttnUnit wu;
+    if (!attn_unit(p, (k8 / p.n_rowblocks) * 8 + xcd, rb == 0, sched_s, wu)) return;
+    const int b = wu.b, kvh = wu.kvh;
     const int N = p.N, G = p.G, R = p.R;
-    const int ctx = clamp_ctx(p.ctx_lens[b], p.max_ctx);
-    const int L = ctx + N;
-    const int p0 = s * p.split_len;
-    if (p0 >= L) return;
-    const int p1 = min(p0 + p.split_len, L);
+    const int ctx = wu.ctx, p0 = wu.p0, p1 = wu.p1;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int rg = wave % C::RG, pg = wave / C::RG;
@@ -378,10 +373,11 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnParams p) {
         __syncthreads();
         f32x4 *buf = (f32x4 *)lds;
         constexpr int SLOT = C::DT + 1;
+        static_assert((PG - 1) * C::RG * NT * SLOT * 64 * 16 <= C::LDS_K + C::LDS_V, "combine buffer");
         if (pg > 0) {
 #pragma unroll
             for (int i = 0; i < NT; ++i) {
-                const int slot = (pg - 1) * NT + i;
+                const int slot = ((pg - 1) * C::RG + rg) * NT + i;      // own slot per (group, row group)
 #pragma unroll
                 for (int dt = 0; dt < C::DT; ++dt) buf[(slot * SLOT + dt) * 64 + lane] = o[i][dt];
                 buf[(slot * SLOT + C::DT) * 64 + lane] = f32x4{m_ref[i], l_sum[i], 0.f, 0.f};
@@ -393,7 +389,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnParams p) {
         for (int i = 0; i < NT; ++i) {
             float mx = m_ref[i];
             for (int q2 = 1; q2 < PG; ++q2) {
-                const int slot = (q2 - 1) * NT + i;
+                const int slot = ((q2 - 1) * C::RG + rg) * NT + i;
                 mx = fmaxf(mx, buf[(slot * SLOT + C::DT) * 64 + lane][0]);
             }
             const float w0 = (m_ref[i] == -INFINITY) ? 0.f : exp2f(m_ref[i] - mx);
@@ -401,7 +397,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnParams p) {
 #pragma unroll
             for (int dt = 0; dt < C::DT; ++dt) o[i][dt] *= w0;
             for (int q2 = 1; q2 < PG; ++q2) {
-                const int slot = (q2 - 1) * NT + i;
+                const int slot = ((q2 - 1) * C::RG + rg) * NT + i;
                 const f32x4 ml = buf[(slot * SLOT + C::DT) * 64 + lane];
                 const float w = (ml[0] == -INFINITY) ? 0.f : exp2f(ml[0] - mx);
                 l_sum[i] += w * ml[1];
@@ -413,7 +409,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnParams p) {
     }
 
     // ---- write the partials of this split ---------------------------------------
-    const int64_t part = ((int64_t)b * p.Hkv + kvh) * p.n_splits + s;
+    const int64_t part = wu.part;
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
         if (!tile_on[i]) continue;
@@ -436,8 +432,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnParams p) {
 
 template <int D, bool Q4, bool PAGED, int NT, int PG>
 hipError_t launch_one(const AttnParams &p, hipStream_t st) {
-    const int units = p.B * p.Hkv * p.n_splits;
-    const int grid = ((units + 7) / 8) * 8 * p.n_rowblocks;
+    const int grid = ((p.n_units + 7) / 8) * 8 * p.n_rowblocks;
     hipLaunchKernelGGL((attn_mfma_kernel<D, Q4, PAGED, NT, PG>), dim3(grid), dim3(256), 0, st, p);
     return hipGetLastError();
 }

@@ -15,7 +15,7 @@
 //   M = max_s m_s,  out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
 //   lse = ln 2 * (M + log2 sum_s 2^(m_s - M) l_s)
 // (m in log2 units), and writes the output in the query dtype.
-#include "device_common.h"
+#include "attn_sched.h"
 
 namespace sv {
 namespace {
@@ -61,21 +61,16 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
     __shared__ int par_s[64];
     __shared__ uint64_t anc_s[64];
 
+    __shared__ SchedLds sched_s;
+
     const int id = blockIdx.x;
     const int xcd = id & 7, k8 = id >> 3;
     const int rb = k8 % p.n_rowblocks;
-    const int u = (k8 / p.n_rowblocks) * 8 + xcd;
-    if (u >= p.B * p.Hkv * p.n_splits) return;
-    const int s = u % p.n_splits;
-    const int bh = u / p.n_splits;
-    const int kvh = bh % p.Hkv, b = bh / p.Hkv;
-
+    AttnUnit wu;
+    if (!attn_unit(p, (k8 / p.n_rowblocks) * 8 + xcd, rb == 0, sched_s, wu)) return;
+    const int b = wu.b, kvh = wu.kvh;
     const int N = p.N, G = p.G, R = p.R;
-    const int ctx = clamp_ctx(p.ctx_lens[b], p.max_ctx);
-    const int L = ctx + N;
-    const int p0 = s * p.split_len;
-    if (p0 >= L) return;
-    const int p1 = min(p0 + p.split_len, L);
+    const int ctx = wu.ctx, p0 = wu.p0, p1 = wu.p1;
 
     const int tid = threadIdx.x;
     const int r = tid >> 4, j = tid & 15;           // row in block, thread in row
@@ -179,7 +174,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
     }
 
     if (!row_ok) return;
-    const int64_t part = ((int64_t)b * p.Hkv + kvh) * p.n_splits + s;
+    const int64_t part = wu.part;
 #pragma unroll
     for (int k = 0; k < D / 16; ++k) p.part_o[(part * R + rglob) * D + j + 16 * k] = o[k];
     if (j == 0) {
@@ -188,45 +183,112 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
     }
 }
 
+// Split merge: one group of D threads per output row (256 / D rows per block).
+// Pass 1 finds M = max_s m_s and the split weights 2^(m_s - M) in parallel
+// over the splits (weights kept in LDS); pass 2 accumulates the weighted
+// partial rows with several independent loads in flight per thread.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
-    constexpr int RPB = 256 / D;
-    const int row = blockIdx.x * RPB + (int)threadIdx.x / D;
-    const int d = threadIdx.x % D;
+    constexpr int RPB = 256 / D;            // rows per block
+    constexpr int WPR = D / 64;             // waves per row
+    __shared__ float w_s[RPB][kMaxSplits];
+    __shared__ float red[4];
+    const int t = threadIdx.x % D;
+    const int rib = threadIdx.x / D;
+    const int row = blockIdx.x * RPB + rib;
     const int rows = p.B * p.N * p.Hq;
-    if (row >= rows) return;
-    const int h = row % p.Hq;
-    const int n = (row / p.Hq) % p.N;
-    const int b = row / (p.Hq * p.N);
+    const bool live = row < rows;
+    const int rr = live ? row : rows - 1;
+    const int h = rr % p.Hq;
+    const int n = (rr / p.Hq) % p.N;
+    const int b = rr / (p.Hq * p.N);
     const int kvh = h / p.G, g = h % p.G;
     const int r = n * p.G + g;
-    const int ctx = clamp_ctx(p.ctx_lens[b], p.max_ctx);
-    const int L = ctx + p.N;
-    const int ns = min(p.n_splits, (L + p.split_len - 1) / p.split_len);
-    const int64_t base = ((int64_t)b * p.Hkv + kvh) * p.n_splits;
-
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, p.part_ml[((base + s) * p.R + r) * 2]);
-    float acc = 0.f, lsum = 0.f;
-    for (int s = 0; s < ns; ++s) {
-        const int64_t pr = (base + s) * p.R + r;
-        const float ms = p.part_ml[pr * 2];
-        const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-        lsum += w * p.part_ml[pr * 2 + 1];
-        acc += w * p.part_o[pr * D + d];
+    // reduction over the D threads (WPR waves) of one row
+    auto row_reduce = [&](float v, bool is_max) -> float {
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            const float o = __shfl_xor(v, m, 64);
+            v = is_max ? fmaxf(v, o) : v + o;
+        }
+        if constexpr (WPR == 1) {
+            return v;
+        } else {
+            __syncthreads();                         // red[] free again
+            if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+            __syncthreads();
+            float a = red[rib * WPR];
+#pragma unroll
+            for (int k = 1; k < WPR; ++k) a = is_max ? fmaxf(a, red[rib * WPR + k]) : a + red[rib * WPR + k];
+            return a;
+        }
+    };
+    // first partial slot and split count of (b, kvh); the static schedule
+    // knows the slots without the context length, so the (m, l) loads start
+    // together with the ctx_lens load
+    int64_t base;
+    int ns, ns_cap;
+    if (p.dyn) {
+        const int4 tb = p.seq_tab[b];
+        base = tb.x + (int64_t)kvh * tb.y;
+        ns = ns_cap = tb.y;
+    } else {
+        base = ((int64_t)b * p.Hkv + kvh) * p.n_splits;
+        ns_cap = p.n_splits;
+        const int L = clamp_ctx(p.ctx_lens[b], p.max_ctx) + p.N;
+        ns = min(p.n_splits, (L + p.split_len - 1) / p.split_len);
     }
-    const float v = acc / lsum;
-    const int64_t oi = (((int64_t)b * p.N + n) * p.Hq + h) * D + d;
+    const float2 *ml = (const float2 *)p.part_ml;
+    constexpr int MLR = kMaxSplits / D;             // splits per thread (upper bound)
+    float2 mlv[MLR];
+#pragma unroll
+    for (int k = 0; k < MLR; ++k) {
+        const int sp = t + k * D;
+        mlv[k] = sp < ns_cap ? ml[(base + sp) * p.R + r] : make_float2(-INFINITY, 0.f);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < MLR; ++k)
+        if (t + k * D < ns) mx = fmaxf(mx, mlv[k].x);
+    const float M = row_reduce(mx, true);
+    float ls = 0.f;
+#pragma unroll
+    for (int k = 0; k < MLR; ++k) {
+        const int sp = t + k * D;
+        if (sp < ns) {
+            const float w = (mlv[k].x == -INFINITY) ? 0.f : exp2f(mlv[k].x - M);
+            w_s[rib][sp] = w;
+            ls += w * mlv[k].y;
+        }
+    }
+    const float lsum = row_reduce(ls, false);
+    __syncthreads();
+
+    const float *op = p.part_o + (base * p.R + r) * D + t;
+    const int64_t sstride = (int64_t)p.R * D;
+    float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+    int sp = 0;
+    for (; sp + 4 <= ns; sp += 4) {
+        const float o0 = op[(sp + 0) * sstride], o1 = op[(sp + 1) * sstride];
+        const float o2 = op[(sp + 2) * sstride], o3 = op[(sp + 3) * sstride];
+        acc0 += w_s[rib][sp + 0] * o0;
+        acc1 += w_s[rib][sp + 1] * o1;
+        acc2 += w_s[rib][sp + 2] * o2;
+        acc3 += w_s[rib][sp + 3] * o3;
+    }
+    for (; sp < ns; ++sp) acc0 += w_s[rib][sp] * op[sp * sstride];
+    if (!live) return;
+    const float v = ((acc0 + acc1) + (acc2 + acc3)) / lsum;
+    const int64_t oi = (((int64_t)b * p.N + n) * p.Hq + h) * D + t;
     if (p.q_f32) ((float *)p.out)[oi] = v;
     else ((uint16_t *)p.out)[oi] = (uint16_t)f32_to_bf16_bits(v);
-    if (d == 0 && p.lse != nullptr)
+    if (t == 0 && p.lse != nullptr)
         p.lse[((int64_t)b * p.N + n) * p.Hq + h] = (M + log2f(lsum)) * 0.69314718055994530942f;
 }
 
 template <int D, int KVT>
 hipError_t launch_valu_t(const AttnParams &p, hipStream_t st) {
-    const int units = p.B * p.Hkv * p.n_splits;
-    const int grid = ((units + 7) / 8) * 8 * p.n_rowblocks;
+    const int grid = ((p.n_units + 7) / 8) * 8 * p.n_rowblocks;
     if (p.q_f32)
         hipLaunchKernelGGL((attn_valu_kernel<D, KVT, true>), dim3(grid), dim3(256), 0, st, p);
     else

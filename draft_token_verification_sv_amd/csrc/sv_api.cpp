@@ -7,14 +7,16 @@
 
 #include <algorithm>
 
-#include "sv_internal.h"
+#include "attn_sched.h"
 
 namespace sv {
 namespace {
 
 thread_local int g_last_hip_error = 0;
 int g_attn_target_wgs = 0;     // 0: choose by batch (see plan_attn)
-int g_argmax_chunk = 4096;
+int g_argmax_chunk = 16384;
+int g_attn_rowblocks = 0;      // 0: planner's choice
+int g_attn_posgroups = 0;      // 0: planner's choice
 
 int hip_fail(hipError_t e) {
     g_last_hip_error = (int)e;
@@ -67,48 +69,71 @@ KvView view_of(const sv_kv_cache *kv) {
     return v;
 }
 
+enum AttnKind { kValu = 0, kMfmaStaged = 1, kMfmaDma = 2 };
+
 struct AttnPlan {
-    bool mfma;
+    int kind;
     int nt, pg;
     int rows_per_block, n_rowblocks;
-    int n_splits, split_len;
-    size_t ws_bytes;
+    int n_splits, split_len;                  // static schedule
+    int dyn, units, split_q, split_min, split_max;
+    size_t o_off, ml_off, tab_off, ws_bytes;
 };
 
 // Launch plan for sv_verify_attn.  Work units are (sequence, KV head, row
-// block); each is split along the key positions so that the grid holds about
-// `target` workgroups (one per CU for a single sequence; several per CU for a
-// batch, whose sequence lengths are known only on the device, so that the
-// shorter sequences' empty splits leave the longer ones room).  Row blocks
-// are added while the split partials would exceed ~15% of the KV bytes.
-AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int Hkv, int max_ctx) {
+// block, split of the key positions); the grid holds about `target`
+// workgroups (one per CU for the pipelined kernel, whose ring fills most of
+// the LDS; two for the others).  A single sequence is split evenly on the host
+// (static schedule); a batch, whose lengths are known only on the device,
+// gets the dynamic schedule (split length chosen by the kernel from the
+// actual lengths, see attn_sched.h).  Row blocks are added while the split
+// partials would exceed ~15% of the KV bytes.
+//   bf16 queries, >= 16 packed rows:  bf16 KV -> direct-to-LDS pipelined kernel
+//                                     4-bit KV -> register-staged kernel
+//   otherwise                         vector-ALU kernel
+AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int Hkv, int max_ctx,
+                   int page_size) {
     AttnPlan pl{};
     const int G = Hq / Hkv;
     const int R = G * N;
     const int64_t L = (int64_t)max_ctx + N;
-    pl.mfma = (q_dtype == SV_BF16) && (kv_dtype == SV_BF16 || kv_dtype == SV_Q4) && R >= 16;
-    const int target = g_attn_target_wgs > 0 ? g_attn_target_wgs : (B > 1 ? 2048 : 256);
+    const bool mfma = (q_dtype == SV_BF16) && (kv_dtype == SV_BF16 || kv_dtype == SV_Q4) && R >= 16;
+    pl.kind = !mfma ? kValu : (kv_dtype == SV_BF16 ? kMfmaDma : kMfmaStaged);
+    const int target = g_attn_target_wgs > 0 ? g_attn_target_wgs : (pl.kind == kMfmaDma ? 256 : 512);
     const double pos_bytes = kv_dtype == SV_F32 ? D * 8.0 : (kv_dtype == SV_BF16 ? D * 4.0 : D * 1.125);
+    // the pipelined kernel keeps a split's page ids in LDS
+    const int64_t max_split = (pl.kind == kMfmaDma && page_size > 0)
+                                  ? (int64_t)(attn_dma_max_split_pages() - 1) * page_size
+                                  : ((int64_t)1 << 40);
 
     auto splits_for = [&](int units, int &split_len, int &n_splits) {
         const int64_t want = std::max<int64_t>(1, target / std::max(units, 1));
-        split_len = (int)round_up(std::max<int64_t>(ceil_div(L, want), 8), 8);
+        int64_t sl = round_up(std::max<int64_t>(ceil_div(L, want), 8), 8);
+        sl = std::max<int64_t>(sl, round_up(ceil_div(L, kMaxSplits), 8));   // merge keeps <= kMaxSplits weights
+        sl = std::min(sl, max_split);
+        split_len = (int)sl;
         n_splits = (int)ceil_div(L, split_len);
     };
 
-    if (pl.mfma) {
-        const int T = kMfmaTileElems / D;
+    if (mfma) {
         const int RT = (R + 15) / 16;
+        // row tiles per wave: up to 3 on the pipelined kernel, 2 on the
+        // register-staged one
+        const int max_tiles = pl.kind == kMfmaDma ? 12 : 8;
         if (RT == 1) {
-            pl.pg = std::min(4, T / 32);
+            pl.pg = pl.kind == kMfmaDma ? std::min(4, 65536 / (128 * D))
+                                        : std::min(4, (kMfmaTileElems / D) / 32);
+            if (g_attn_posgroups > 0 && pl.kind == kMfmaDma)
+                pl.pg = std::min(g_attn_posgroups, std::min(4, 65536 / (128 * D)));
             pl.nt = 1;
             pl.rows_per_block = 16;
             pl.n_rowblocks = 1;
             splits_for(B * Hkv, pl.split_len, pl.n_splits);
         } else {
             pl.pg = 1;
-            int nrb = (RT + 7) / 8;            // at most 2 row tiles per wave
-            for (;;) {
+            int nrb = (RT + max_tiles - 1) / max_tiles;
+            if (g_attn_rowblocks > 0) nrb = std::max(nrb, std::min(g_attn_rowblocks, RT));
+            for (; g_attn_rowblocks == 0;) {
                 const int tpb = (RT + nrb - 1) / nrb;
                 splits_for(B * Hkv * nrb, pl.split_len, pl.n_splits);
                 const double part = (double)pl.n_splits * R * (D + 2) * 4.0;
@@ -129,9 +154,30 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
         pl.n_rowblocks = (R + 15) / 16;
         splits_for(B * Hkv * pl.n_rowblocks, pl.split_len, pl.n_splits);
     }
-    const size_t o_bytes = (size_t)B * Hkv * pl.n_splits * R * D * 4;
-    const size_t ml_bytes = (size_t)B * Hkv * pl.n_splits * R * 2 * 4;
-    pl.ws_bytes = (size_t)round_up((int64_t)o_bytes, 256) + (size_t)round_up((int64_t)ml_bytes, 256);
+
+    int64_t units = (int64_t)B * Hkv * pl.n_splits;
+    pl.dyn = B > 1;
+    if (pl.dyn) {
+        // split lengths: multiples of the kernel's stage (8 positions for the
+        // others), at most kMaxSplits splits per sequence, page ids of a split
+        // within the pipelined kernel's LDS table
+        const int64_t q = pl.kind == kMfmaDma ? 32 * pl.pg : 8;
+        const int64_t smax = std::min(round_up(L, q), max_split / q * q);
+        const int64_t smin = std::max<int64_t>(q, round_up(ceil_div(L, kMaxSplits), q));
+        pl.split_q = (int)q;
+        pl.split_min = (int)smin;
+        pl.split_max = (int)std::max(smax, smin);    // smax < smin is rejected by the caller
+        units = std::max<int64_t>(target / pl.n_rowblocks, 2 * (int64_t)B * Hkv);
+        units = std::max<int64_t>(units, (int64_t)B * Hkv * ceil_div(L, pl.split_max));
+        if (smax < smin) pl.split_max = -1;
+    }
+    pl.units = (int)std::min<int64_t>(units, INT32_MAX / 2);
+    const size_t o_bytes = (size_t)units * R * D * 4;
+    const size_t ml_bytes = (size_t)units * R * 2 * 4;
+    pl.o_off = 0;
+    pl.ml_off = (size_t)round_up((int64_t)o_bytes, 256);
+    pl.tab_off = pl.ml_off + (size_t)round_up((int64_t)ml_bytes, 256);
+    pl.ws_bytes = pl.tab_off + (pl.dyn ? (size_t)round_up((int64_t)B * 16, 256) : 0);
     return pl;
 }
 
@@ -172,6 +218,16 @@ int sv_set_option(int option, int value) {
             prev = g_attn_target_wgs;
             g_attn_target_wgs = value;
             return prev;
+        case SV_OPT_ATTN_ROWBLOCKS:
+            if (value < 0) return SV_EINVAL;
+            prev = g_attn_rowblocks;
+            g_attn_rowblocks = value;
+            return prev;
+        case SV_OPT_ATTN_POSGROUPS:
+            if (value != 0 && value != 1 && value != 2 && value != 4) return SV_EINVAL;
+            prev = g_attn_posgroups;
+            g_attn_posgroups = value;
+            return prev;
         case SV_OPT_ARGMAX_CHUNK:
             if (value <= 0 || value % 8 != 0) return SV_EINVAL;
             prev = g_argmax_chunk;
@@ -185,9 +241,9 @@ size_t sv_verify_attn_workspace_size(const sv_kv_cache *kv, int batch, int n_nod
                                      int max_ctx) {
     if (check_attn_shape(kv, batch, n_nodes, n_q_heads, max_ctx) != SV_OK) return 0;
     const AttnPlan pl = plan_attn(kv->dtype, SV_BF16, kv->head_dim, batch, n_nodes, n_q_heads,
-                                  kv->n_kv_heads, max_ctx);
+                                  kv->n_kv_heads, max_ctx, kv->page_size);
     const AttnPlan pf = plan_attn(kv->dtype, SV_F32, kv->head_dim, batch, n_nodes, n_q_heads,
-                                  kv->n_kv_heads, max_ctx);
+                                  kv->n_kv_heads, max_ctx, kv->page_size);
     return std::max(pl.ws_bytes, pf.ws_bytes);
 }
 
@@ -204,7 +260,10 @@ int sv_verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
     if (!isfinite(sm_scale)) return SV_EINVAL;
     if (q_dtype == SV_BF16 && kv->dtype == SV_F32) return SV_EUNSUPPORTED;
     const int D = kv->head_dim;
-    const AttnPlan pl = plan_attn(kv->dtype, q_dtype, D, batch, n_nodes, n_q_heads, kv->n_kv_heads, max_ctx);
+    const AttnPlan pl = plan_attn(kv->dtype, q_dtype, D, batch, n_nodes, n_q_heads, kv->n_kv_heads, max_ctx,
+                                  kv->page_size);
+    if (pl.dyn ? (batch > kSchedMaxBatch || pl.split_max < 0) : pl.n_splits > kMaxSplits)
+        return SV_EUNSUPPORTED;
     if (workspace == nullptr || workspace_bytes < pl.ws_bytes) return SV_EWORKSPACE;
     if (!aligned(workspace, 16)) return SV_EINVAL;
 
@@ -213,10 +272,9 @@ int sv_verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
     p.q = q;
     p.ctx_lens = ctx_lens;
     p.parent = parent;
-    p.part_o = (float *)workspace;
-    const size_t o_bytes = (size_t)batch * kv->n_kv_heads * pl.n_splits * (n_q_heads / kv->n_kv_heads) *
-                           n_nodes * D * 4;
-    p.part_ml = (float *)((char *)workspace + round_up((int64_t)o_bytes, 256));
+    p.part_o = (float *)((char *)workspace + pl.o_off);
+    p.part_ml = (float *)((char *)workspace + pl.ml_off);
+    p.seq_tab = pl.dyn ? (int4 *)((char *)workspace + pl.tab_off) : nullptr;
     p.out = out;
     p.lse = lse;
     p.B = batch;
@@ -228,16 +286,23 @@ int sv_verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
     p.max_ctx = max_ctx;
     p.n_splits = pl.n_splits;
     p.split_len = pl.split_len;
+    p.dyn = pl.dyn;
+    p.units_max = pl.units;
+    p.split_q = pl.split_q;
+    p.split_min = pl.split_min;
+    p.split_max = pl.split_max;
     p.rows_per_block = pl.rows_per_block;
     p.n_rowblocks = pl.n_rowblocks;
-    p.n_units = batch * kv->n_kv_heads * pl.n_splits * pl.n_rowblocks;
+    p.n_units = pl.units;
     const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)D);
     p.scale_log2 = scale * 1.4426950408889634f;
     p.q_f32 = q_dtype == SV_F32;
 
     hipStream_t st = (hipStream_t)stream;
-    hipError_t e = pl.mfma ? launch_attn_mfma(p, kv->dtype, D, pl.nt, pl.pg, st)
-                           : launch_attn_valu(p, kv->dtype, D, st);
+    hipError_t e;
+    if (pl.kind == kMfmaDma) e = launch_attn_dma(p, D, pl.nt, pl.pg, st);
+    else if (pl.kind == kMfmaStaged) e = launch_attn_mfma(p, kv->dtype, D, pl.nt, pl.pg, st);
+    else e = launch_attn_valu(p, kv->dtype, D, st);
     if (e != hipSuccess) return hip_fail(e);
     e = launch_attn_merge(p, D, st);
     if (e != hipSuccess) return hip_fail(e);
@@ -246,9 +311,8 @@ int sv_verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
 
 size_t sv_greedy_accept_workspace_size(int batch, int n_nodes, int vocab) {
     if (batch < 1 || n_nodes < 1 || n_nodes > 64 || vocab < 1) return 0;
-    const int64_t chunks = ceil_div(vocab, g_argmax_chunk);
-    const int64_t keys = (int64_t)batch * n_nodes * chunks * 8;
-    return (size_t)(round_up(keys, 256) + round_up((int64_t)batch * 4, 256));
+    const int64_t rows = (int64_t)batch * n_nodes;
+    return (size_t)(round_up(rows * 8, 256) + round_up(rows * 4, 256) + round_up((int64_t)batch * 4, 256));
 }
 
 int sv_greedy_accept(int batch, int n_nodes, int vocab,
@@ -274,8 +338,10 @@ int sv_greedy_accept(int batch, int n_nodes, int vocab,
     p.path = path;
     p.tokens = tokens;
     p.argmax = argmax;
+    const int64_t rows = (int64_t)batch * n_nodes;
     p.keys = (unsigned long long *)workspace;
-    p.counters = (unsigned int *)((char *)workspace + round_up((int64_t)batch * n_nodes * chunks * 8, 256));
+    p.rows_done = (unsigned int *)((char *)workspace + round_up(rows * 8, 256));
+    p.seqs_done = (unsigned int *)((char *)workspace + round_up(rows * 8, 256) + round_up(rows * 4, 256));
     p.B = batch;
     p.N = n_nodes;
     p.V = vocab;

@@ -26,15 +26,19 @@ struct AttnParams {
     const void *q;                // [B][N][Hq][D]
     const int32_t *ctx_lens;      // [B]
     const int32_t *parent;        // [B][N]
-    float *part_o;                // [B][Hkv][S][R][D]  (unnormalised, scaled to 2^-m)
-    float *part_ml;               // [B][Hkv][S][R][2]  (m in log2 units, l)
+    float *part_o;                // [unit][R][D]  (unnormalised, scaled to 2^-m)
+    float *part_ml;               // [unit][R][2]  (m in log2 units, l)
     void *out;                    // [B][N][Hq][D]
     float *lse;                   // [B][N][Hq] or nullptr
     int B, N, Hq, Hkv, G, R;      // R = G * N packed rows per (b, kv head)
     int max_ctx;
-    int n_splits, split_len;      // positions per split (multiple of the kernel tile)
+    int n_splits, split_len;      // static schedule: splits per sequence, positions per split
+    int dyn;                      // 1: dynamic schedule (split length chosen on the device)
+    int units_max;                // dynamic: units the grid covers (= partial slots)
+    int split_q, split_min, split_max;   // dynamic: split length quantum and bounds
+    int4 *seq_tab;                // dynamic: [B] (first unit, splits, split length, 0)
     int rows_per_block, n_rowblocks;
-    int n_units;                  // B * Hkv * n_splits * n_rowblocks
+    int n_units;                  // units the grid covers (without row blocks)
     float scale_log2;             // sm_scale * log2(e)
     int q_f32;                    // 1: q/out are fp32, 0: bf16
 };
@@ -44,8 +48,9 @@ struct AcceptParams {
     const int32_t *draft;         // [B][N]
     const int32_t *parent;        // [B][N]
     int32_t *accept_len, *path, *tokens, *argmax;
-    unsigned long long *keys;     // [B][N][chunks] packed (value, index) maxima
-    unsigned int *counters;       // [B]   (zero between calls)
+    unsigned long long *keys;     // [B][N] packed (value, index) maxima  (zero between calls)
+    unsigned int *rows_done;      // [B][N] chunks done                  (zero between calls)
+    unsigned int *seqs_done;      // [B]    rows done                    (zero between calls)
     int B, N, V, chunk, n_chunks;
     int logits_f32;
 };
@@ -61,9 +66,12 @@ struct CompactParams {
 // Kernel-side tile sizes (positions staged per iteration) -----------------
 constexpr int kMfmaTileElems = 16384;          // T * D bf16 elements per K (or V) tile
 constexpr int kValuTileElems = 8192;           // T * D fp32 elements per K (or V) tile
+constexpr int kMaxSplits = 1024;               // splits per (sequence, KV head, row block)
 
 // launchers (return the hipError_t of the launch) -------------------------
 hipError_t launch_attn_mfma(const AttnParams &p, int dtype, int D, int nt, int pg, hipStream_t s);
+hipError_t launch_attn_dma(const AttnParams &p, int D, int nt, int pg, hipStream_t s);
+int attn_dma_max_split_pages();
 hipError_t launch_attn_valu(const AttnParams &p, int dtype, int D, hipStream_t s);
 hipError_t launch_attn_merge(const AttnParams &p, int D, hipStream_t s);
 hipError_t launch_accept(const AcceptParams &p, hipStream_t s);

@@ -125,6 +125,9 @@ typedef struct sv_kv_cache {
  * workspace device scratch of at least sv_verify_attn_workspace_size() bytes
  *           (any contents; 256-byte aligned).  One workspace serves one
  *           stream at a time.
+ * batch     at most 1024 (SV_EUNSUPPORTED beyond).  For batch > 1 the kernels
+ *           choose the key-split length on the device from ctx_lens, so the
+ *           work per workgroup follows the actual lengths rather than max_ctx.
  * Supported: q SV_BF16 with KV SV_BF16 or SV_Q4 (bf16 matrix cores when
  * (n_q_heads/n_kv_heads) * N >= 16 rows, vector ALU otherwise); q SV_F32 with
  * KV SV_F32, SV_BF16 or SV_Q4 (vector ALU, fp32 arithmetic).
@@ -193,9 +196,15 @@ int sv_last_hip_error(void);
 /*
  * Launch tuning (for benchmarks and sweeps; the defaults need no setting).
  *   SV_OPT_ATTN_TARGET_WGS  workgroups the attention launch aims for; 0 (the
- *                           default) = 256 for one sequence, 2048 for a batch
+ *                           default) = 256 on the pipelined bf16 path, 512 on
+ *                           the others
  *   SV_OPT_ARGMAX_CHUNK     logits elements per argmax workgroup, a positive
- *                           multiple of 8 (default 4096)
+ *                           multiple of 8 (default 16384)
+ *   SV_OPT_ATTN_ROWBLOCKS   packed-row blocks per (sequence, KV head) on the
+ *                           matrix-core paths; 0 (default) = planner's choice
+ *   SV_OPT_ATTN_POSGROUPS   waves sharing one 16-row tile on the pipelined bf16
+ *                           path (1, 2 or 4; each takes 32 positions of a
+ *                           stage); 0 (default) = planner's choice
  * Returns the previous value, or SV_EINVAL for an unknown option or a value
  * out of range.  A workspace sized under one setting may be too small under
  * another (the call then returns SV_EWORKSPACE).
@@ -203,6 +212,8 @@ int sv_last_hip_error(void);
  */
 #define SV_OPT_ATTN_TARGET_WGS 1
 #define SV_OPT_ARGMAX_CHUNK    2
+#define SV_OPT_ATTN_ROWBLOCKS  3
+#define SV_OPT_ATTN_POSGROUPS  4
 int sv_set_option(int option, int value);
 
 #ifdef __cplusplus

@@ -89,6 +89,8 @@ def test_attention_argument_checks(lib):
     assert _attn(lib, kv(page_size=16, page_table=FAKE, max_pages_per_seq=256)) == -1   # 4096 < ctx+N
     assert _attn(lib, kv(), ws=0) == -3
     assert _attn(lib, kv(), wsb=1024) == -3
+    assert _attn(lib, kv(n_seqs=1025), B=1025, max_ctx=64) == -2   # batch over 1024
+    assert _attn(lib, kv(n_seqs=1024), B=1024, max_ctx=64, wsb=1024) == -3
 
 
 def test_attention_workspace_size(lib):
@@ -99,12 +101,17 @@ def test_attention_workspace_size(lib):
     assert lib.sv_verify_attn_workspace_size(ctypes.byref(d), 1, 8, 25, 4096) == 0
     big = lib.sv_verify_attn_workspace_size(ctypes.byref(kv(capacity=200000)), 1, 8, 24, 131072)
     assert big >= n
+    # a batch: partial slots for at least two units per (sequence, KV head)
+    # plus the 16-byte per-sequence schedule record
+    nb = lib.sv_verify_attn_workspace_size(ctypes.byref(kv(n_seqs=64)), 64, 8, 24, 4096)
+    assert nb >= 2 * 64 * 4 * 48 * (256 + 2) * 4 + 64 * 16 and nb % 256 == 0
 
 
 def test_accept_checks_and_workspace(lib):
     n = lib.sv_greedy_accept_workspace_size(1, 8, 151936)
-    chunks = -(-151936 // 4096)
-    assert n == -(-(8 * chunks * 8) // 256) * 256 + 256
+    # one 64-bit key and one counter per row, one counter per sequence
+    assert n == 3 * 256
+    assert lib.sv_greedy_accept_workspace_size(8, 64, 151936) == 4096 + 2048 + 256
     P = ctypes.c_void_p(FAKE)
 
     def call(B=1, N=8, V=151936, ld=1, ws=FAKE, wsb=1 << 30):
@@ -132,5 +139,9 @@ def test_options(lib):
     assert prev == 0
     assert lib.sv_set_option(1, 0) == 300
     assert lib.sv_set_option(2, 12) == -1                   # not a multiple of 8
-    assert lib.sv_set_option(2, 4096) == 4096
+    assert lib.sv_set_option(2, 4096) == 16384
+    assert lib.sv_set_option(2, 16384) == 4096
+    assert lib.sv_set_option(4, 3) == -1                   # position groups: 1, 2 or 4
+    assert lib.sv_set_option(4, 2) == 0
+    assert lib.sv_set_option(4, 0) == 2
     assert lib.sv_set_option(9, 1) == -1

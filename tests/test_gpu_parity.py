@@ -103,6 +103,71 @@ def test_attention_split_count_independent(sv, target):
     check_attention(case, out, lse)
 
 
+BATCH_PATHS = [
+    # (label, Hq, Hkv, D, N, q, kv, paged)
+    ("pipelined D128 R16 paged", 16, 4, 128, 4, "bf16", "bf16", True),
+    ("pipelined D256 R48", 24, 4, 256, 8, "bf16", "bf16", False),
+    ("staged q4 D128", 16, 4, 128, 4, "bf16", "q4", False),
+    ("valu f32 D64", 4, 2, 64, 3, "f32", "f32", False),
+]
+SKEW = [0, 3100, 5, 1500, 0, 64, 777]
+
+
+def _skewed_case(path, seed=11):
+    label, Hq, Hkv, D, N, qd, kvd, paged = path
+    cfg = workloads.Config(label, len(SKEW), Hq, Hkv, D, N, qd, kvd, "f32", 50, max(SKEW),
+                           tree="ddtree", paged=paged, q_std=0.5, kv_std=0.5, draft_rule="tree")
+    case = workloads.make_case(cfg, seed=seed, capacity_pad=3)
+    # lengths far apart: the cache holds max(SKEW) + N positions for every
+    # sequence, the call sees these lengths (both sides read the same arrays)
+    case.ctx_lens = np.array(SKEW, dtype=np.int32)
+    return case
+
+
+@pytest.mark.parametrize("path", BATCH_PATHS, ids=[b[0] for b in BATCH_PATHS])
+@pytest.mark.parametrize("target", [1, 37, 256, 4096])
+def test_attention_batch_schedule(sv, path, target):
+    """A batch with very different lengths (some empty) under the dynamic split
+    schedule, for grids far below and far above the unit count."""
+    say(f"[attn-batch] {path[0]} target_wgs={target}")
+    case = _skewed_case(path)
+    dc = DeviceCase(case)
+    prev = sv.set_option(sv.SV_OPT_ATTN_TARGET_WGS, target)
+    try:
+        out, lse = dc.attn()
+        torch.cuda.synchronize()
+    finally:
+        sv.set_option(sv.SV_OPT_ATTN_TARGET_WGS, prev)
+    ma, rel, le = check_attention(case, out, lse)
+    say(f"    max_abs={ma:.3g} rel={rel:.3g} lse={le:.3g}")
+
+
+@pytest.mark.parametrize("pg", [1, 2, 4])
+def test_attention_position_groups(sv, pg):
+    say(f"[attn-pg] posgroups={pg}")
+    case = _skewed_case(BATCH_PATHS[0], seed=12)
+    dc = DeviceCase(case)
+    prev = sv.set_option(sv.SV_OPT_ATTN_POSGROUPS, pg)
+    try:
+        out, lse = dc.attn()
+        torch.cuda.synchronize()
+    finally:
+        sv.set_option(sv.SV_OPT_ATTN_POSGROUPS, prev)
+    check_attention(case, out, lse)
+
+
+def test_attention_max_batch(sv):
+    """1024 sequences (the batch limit): four per thread in the schedule."""
+    say("[attn-maxbatch] B=1024")
+    cfg = workloads.Config("max batch", 1024, 16, 4, 128, 4, "bf16", "bf16", "f32", 50, 0, ctx_hi=60,
+                           tree="ddtree", q_std=0.5, kv_std=0.5, draft_rule="tree")
+    case = workloads.make_case(cfg, seed=21)
+    dc = DeviceCase(case)
+    out, lse = dc.attn()
+    torch.cuda.synchronize()
+    check_attention(case, out, lse, batch=[0, 1, 255, 256, 511, 777, 1023])
+
+
 FULL = [("C2", None, None), ("C3", None, None), ("C4", [0, 7, 23], None), ("C5", None, [0, 3, 7])]
 
 
