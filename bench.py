@@ -118,7 +118,20 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate-bytes", type=float, default=1.1 * 2 ** 30)
     ap.add_argument("--target-wgs", type=int, default=0, help="attention grid target (0: library default)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run 5 device-to-device copies of BYTES bytes (reference kernel for "
+                         "scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(args.copy_calibration, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": args.copy_calibration, "copies": 5}), flush=True)
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "

@@ -13,20 +13,24 @@
 //            smallest split length (a multiple of split_q, within
 //            [split_min, split_max]) for which the units
 //                U(sl) = Hkv * sum_b ceil(L_b / sl)
-//            fit the grid (units_max), so the work per unit is about the
+//            fit the grid (units_max); sequence b then takes
+//            ns_b = ceil(L_b / sl) splits of about L_b / ns_b positions each
+//            (rounded up to the quantum), so the work per unit is about the
 //            average and short sequences do not leave most of the grid idle
-//            while long ones finish.  Units are numbered sequence by sequence
-//            (then KV head, then split), so unit u is also its partial slot.
-//            The unit (b, head 0, split 0) of row block 0 records
-//            (first unit, splits, split length) of sequence b for the merge.
+//            while long ones finish.  Each sequence owns a contiguous range of
+//            unit numbers (KV head major, then split); unit u is also its
+//            partial slot.  The unit (b, head 0, split 0) of row block 0
+//            records (first unit, splits, split length) of sequence b for the
+//            merge.  Reductions and scans over the batch use DPP lane moves
+//            within a wavefront and one LDS exchange between the 4 wavefronts.
 #pragma once
 
 #include "device_common.h"
 
 namespace sv {
 
-constexpr int kSchedSeqPerThread = 4;           // 256 threads: batch <= 1024
-constexpr int kSchedMaxBatch = 256 * kSchedSeqPerThread;
+constexpr int kSchedRounds = 4;                 // sequences b = 256 * round + thread
+constexpr int kSchedMaxBatch = 256 * kSchedRounds;
 
 struct AttnUnit {
     int b, kvh, s;
@@ -35,20 +39,115 @@ struct AttnUnit {
 };
 
 struct SchedLds {
-    long long red[2][4];
-    int pick[4];                  // b, first unit, splits, L of the chosen sequence
+    double tot[4];
+    uint32_t red[2][4];
+    int pick[5];                  // b, first unit, splits, L, split length of the chosen sequence
 };
 
-// Sum over the 256 threads of a block; `par` alternates the two reduction
-// slots so that one barrier per call suffices.
-__device__ __forceinline__ long long sched_block_sum(long long v, SchedLds &sm, int &par) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP moves (row
+// shifts by 1, 2, 4, 8 within rows of 16 lanes, then the row broadcasts of
+// lanes 15 and 31), no LDS traffic.
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);   // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);   // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);   // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);   // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+    return x;
+}
+
+#define SV_DPP_ADD_F64(x, ctrl, rmask)                                                            \
+    do {                                                                                       \
+        const uint64_t u_ = __builtin_bit_cast(uint64_t, x);                                   \
+        const uint32_t lo_ = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u_, ctrl, rmask, 0xf, false); \
+        const uint32_t hi_ =                                                                   \
+            (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u_ >> 32), ctrl, rmask, 0xf, false); \
+        x += __builtin_bit_cast(double, ((uint64_t)hi_ << 32) | lo_);                          \
+    } while (0)
+
+// Wavefront sum of doubles holding integers (exact below 2^53), in every lane.
+__device__ __forceinline__ double wave_sum_f64(double x) {
+    SV_DPP_ADD_F64(x, 0x111, 0xf);
+    SV_DPP_ADD_F64(x, 0x112, 0xf);
+    SV_DPP_ADD_F64(x, 0x114, 0xf);
+    SV_DPP_ADD_F64(x, 0x118, 0xf);
+    SV_DPP_ADD_F64(x, 0x142, 0xa);
+    SV_DPP_ADD_F64(x, 0x143, 0xc);
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Block (256 threads) sum of 32-bit counts; `par` alternates the two LDS slots
+// so that one barrier per call suffices.
+__device__ __forceinline__ uint32_t sched_block_sum(uint32_t v, SchedLds &sm, int &par) {
+    v = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_u32(v), 63);
     if ((threadIdx.x & 63) == 0) sm.red[par][threadIdx.x >> 6] = v;
     __syncthreads();
-    const long long r = sm.red[par][0] + sm.red[par][1] + sm.red[par][2] + sm.red[par][3];
+    const uint32_t r = sm.red[par][0] + sm.red[par][1] + sm.red[par][2] + sm.red[par][3];
     par ^= 1;
     return r;
+}
+
+// Bounds of the split-length search.  Split lengths are multiples of the
+// power of two q.  Any feasible length is >= H * tot / U; with U > B * H the
+// length H * tot / (U - B * H) is feasible (each sequence adds < 1 unit per
+// head to H * L_b / sl); split_max is feasible by the host's choice of U.  The
+// quotients are worked out in double (exact for the integers involved, rounded
+// up and padded) so that no 64-bit integer division is needed.
+__device__ __forceinline__ void split_bounds(const AttnParams &p, double tot, int &lo, int &hi) {
+    const int qm = p.split_q - 1;
+    const double U = (double)p.units_max, BH = (double)p.B * p.Hkv, HT = (double)p.Hkv * tot;
+    auto rup = [&](double x) -> int {
+        const double c = ceil(x);
+        return c >= (double)p.split_max ? p.split_max : (((int)c + qm) & ~qm);
+    };
+    lo = rup(HT / U);
+    lo = lo > p.split_min ? lo : p.split_min;
+    hi = p.split_max;
+    if (U > BH) {
+        const int s0 = rup(HT / (U - BH) + 1.0);
+        hi = s0 < hi ? s0 : hi;
+    }
+    lo = lo < p.split_max ? lo : p.split_max;
+    hi = hi > lo ? hi : lo;
+}
+
+// Smallest length in [lo, hi] whose unit count fits (hi fits); the caller's
+// units_at(sl) must return the same value in every thread that calls it.
+template <class F>
+__device__ __forceinline__ uint32_t split_search(int lo, int hi, int qm, long long umax, F units_at) {
+    if (hi > lo) {
+        if (units_at((uint32_t)lo) <= umax) {
+            hi = lo;
+        } else {
+#pragma unroll 1
+            while (hi - lo > qm + 1) {                   // U(lo) > U_max >= U(hi)
+                const int mid = lo + (((hi - lo) >> 1) & ~qm);
+                if (units_at((uint32_t)mid) <= umax) hi = mid;
+                else lo = mid;
+            }
+        }
+    }
+    return (uint32_t)hi;
+}
+
+// Records sequence b (length L, ns splits from unit `first`) as the owner of
+// unit u when u falls in its range.
+__device__ __forceinline__ void sched_pick(SchedLds &sm, int u, int b, uint32_t L, uint32_t ns, long long first,
+                                           int H, int qm) {
+    if (ns > 0 && u >= first && u < first + (long long)H * ns) {
+        sm.pick[0] = b;
+        sm.pick[1] = (int)first;
+        sm.pick[2] = (int)ns;
+        sm.pick[3] = (int)L;
+        // the sequence's own length: its ns splits made as even as the
+        // quantum allows (<= sl, so the unit count is unchanged)
+        const uint32_t even = (L + ns - 1u) / ns;
+        sm.pick[4] = (int)((even + (uint32_t)qm) & ~(uint32_t)qm);
+    }
 }
 
 // Decodes unit u.  Must be called by all 256 threads of the block (the dynamic
@@ -72,94 +171,87 @@ __device__ __forceinline__ bool attn_unit(const AttnParams &p, int u, bool recor
     }
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint32_t Lr[kSchedSeqPerThread];
-    long long tl = 0;
+    const int qm = p.split_q - 1;
+    const int H = p.Hkv;
+    const long long umax = p.units_max;
+    if (p.B <= 64) {
+        // one sequence per lane of wavefront 0: every reduction is a DPP scan,
+        // no barrier until the result is published
+        if (wave == 0) {
+            const uint32_t Lb = lane < p.B ? (uint32_t)(clamp_ctx(p.ctx_lens[lane], p.max_ctx) + p.N) : 0u;
+            const double tot = wave_sum_f64((double)Lb);
+            int lo, hi;
+            split_bounds(p, tot, lo, hi);
+            const uint32_t sl = split_search(lo, hi, qm, umax, [&](uint32_t x) -> long long {
+                const uint32_t c = wave_scan_u32((Lb + x - 1u) / x);
+                return (long long)H * (uint32_t)__builtin_amdgcn_readlane((int)c, 63);
+            });
+            const uint32_t ns = (Lb + sl - 1u) / sl;
+            const uint32_t before = wave_scan_u32(ns) - ns;
+            if (lane == 0) sm.pick[0] = -1;           // same wavefront: ordered before the pick
+            sched_pick(sm, u, lane, Lb, ns, (long long)H * before, H, qm);
+        }
+        __syncthreads();
+    } else {
+        const int rounds = (p.B + 255) >> 8;         // uniform, <= kSchedRounds
+        uint32_t Lr[kSchedRounds];
+        double tl = 0.0;
 #pragma unroll
-    for (int k = 0; k < kSchedSeqPerThread; ++k) {
-        const int b = tid * kSchedSeqPerThread + k;
-        Lr[k] = b < p.B ? (uint32_t)(clamp_ctx(p.ctx_lens[b], p.max_ctx) + p.N) : 0u;
-        tl += Lr[k];
-    }
-    if (tid == 0) sm.pick[0] = -1;
-    int par = 0;
-    const long long tot = sched_block_sum(tl, sm, par);
-
-    const long long q = p.split_q, H = p.Hkv, U = p.units_max;
-    const long long BH = (long long)p.B * H;
-    auto rup = [&](long long x) { return (x + q - 1) / q * q; };
-    // any feasible length is >= H * tot / U; with U > B * H the length
-    // H * tot / (U - B * H) is feasible (each sequence adds < 1 unit per head
-    // to H * L_b / sl); split_max is feasible by the host's choice of U
-    long long lo = rup((H * tot + U - 1) / U);
-    lo = lo > p.split_min ? lo : (long long)p.split_min;
-    long long hi = p.split_max;
-    if (U > BH) {
-        const long long s0 = rup((H * tot + (U - BH) - 1) / (U - BH));
-        hi = s0 < hi ? s0 : hi;
-    }
-    hi = hi > lo ? hi : lo;
-    auto units_at = [&](long long sl) -> long long {
-        long long c = 0;
+        for (int k = 0; k < kSchedRounds; ++k) {
+            const int b = 256 * k + tid;
+            Lr[k] = b < p.B ? (uint32_t)(clamp_ctx(p.ctx_lens[b], p.max_ctx) + p.N) : 0u;
+            tl += (double)Lr[k];
+        }
+        tl = wave_sum_f64(tl);
+        if (lane == 0) sm.tot[wave] = tl;
+        if (tid == 0) sm.pick[0] = -1;
+        __syncthreads();
+        const double tot = (sm.tot[0] + sm.tot[1]) + (sm.tot[2] + sm.tot[3]);
+        int lo, hi;
+        split_bounds(p, tot, lo, hi);
+        int par = 0;
+        const uint32_t sl = split_search(lo, hi, qm, umax, [&](uint32_t x) -> long long {
+            uint32_t c = 0;
 #pragma unroll
-        for (int k = 0; k < kSchedSeqPerThread; ++k) c += (Lr[k] + (uint32_t)sl - 1u) / (uint32_t)sl;
-        return H * sched_block_sum(c, sm, par);
-    };
-    if (hi > lo) {
-        if (units_at(lo) <= U) {
-            hi = lo;
-        } else {
-#pragma unroll 1
-            while (hi - lo > q) {                        // U(lo) > U_max >= U(hi)
-                const long long mid = lo + (hi - lo) / q / 2 * q;
-                if (units_at(mid) <= U) hi = mid;
-                else lo = mid;
+            for (int k = 0; k < kSchedRounds; ++k)
+                if (k < rounds) c += (Lr[k] + x - 1u) / x;
+            return (long long)H * sched_block_sum(c, sm, par);
+        });
+        // units of sequence b: a contiguous range, assigned round by round in
+        // thread order (any fixed order works: the merge reads the table)
+        uint32_t first = 0;
+#pragma unroll
+        for (int k = 0; k < kSchedRounds; ++k) {
+            if (k >= rounds) break;
+            const uint32_t ns = (Lr[k] + sl - 1u) / sl;
+            const uint32_t incl = wave_scan_u32(ns);
+            if (lane == 63) sm.red[par][wave] = incl;
+            __syncthreads();
+            uint32_t before = first + incl - ns;
+            uint32_t all = 0;
+#pragma unroll
+            for (int wv = 0; wv < 4; ++wv) {
+                const uint32_t t = sm.red[par][wv];
+                before += wv < wave ? t : 0u;
+                all += t;
             }
+            par ^= 1;
+            sched_pick(sm, u, 256 * k + tid, Lr[k], ns, (long long)H * before, H, qm);
+            first += all;
         }
+        __syncthreads();
     }
-    const int sl = (int)hi;
-
-    // exclusive scan of the per-thread split counts -> first unit of each sequence
-    int ns[kSchedSeqPerThread];
-    int c = 0;
-#pragma unroll
-    for (int k = 0; k < kSchedSeqPerThread; ++k) {
-        ns[k] = (int)((Lr[k] + (uint32_t)sl - 1u) / (uint32_t)sl);
-        c += ns[k];
-    }
-    int incl = c;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int t = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += t;
-    }
-    if (lane == 63) sm.red[par][wave] = incl;
-    __syncthreads();
-    long long first = incl - c;
-    for (int wv = 0; wv < wave; ++wv) first += sm.red[par][wv];
-    first *= H;
-#pragma unroll
-    for (int k = 0; k < kSchedSeqPerThread; ++k) {
-        const long long span = H * ns[k];
-        if (u >= first && u < first + span) {
-            sm.pick[0] = tid * kSchedSeqPerThread + k;
-            sm.pick[1] = (int)first;
-            sm.pick[2] = ns[k];
-            sm.pick[3] = (int)Lr[k];
-        }
-        first += span;
-    }
-    __syncthreads();
     if (sm.pick[0] < 0) return false;
     w.b = sm.pick[0];
     const int rel = u - sm.pick[1];
     w.kvh = rel / sm.pick[2];
     w.s = rel % sm.pick[2];
-    const int L = sm.pick[3];
+    const int L = sm.pick[3], slb = sm.pick[4];
     w.ctx = L - p.N;
-    w.p0 = w.s * sl;
-    w.p1 = min(w.p0 + sl, L);
+    w.p0 = w.s * slb;
+    w.p1 = min(w.p0 + slb, L);
     w.part = u;
-    if (record && rel == 0 && tid == 0) p.seq_tab[w.b] = make_int4(sm.pick[1], sm.pick[2], sl, 0);
+    if (record && rel == 0 && tid == 0) p.seq_tab[w.b] = make_int4(sm.pick[1], sm.pick[2], slb, 0);
     return true;
 }
 

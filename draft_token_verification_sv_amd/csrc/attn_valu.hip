@@ -186,7 +186,10 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
 // Split merge: one group of D threads per output row (256 / D rows per block).
 // Pass 1 finds M = max_s m_s and the split weights 2^(m_s - M) in parallel
 // over the splits (weights kept in LDS); pass 2 accumulates the weighted
-// partial rows with several independent loads in flight per thread.
+// partial rows.  The first 32 partial values of a thread are loaded before
+// pass 1, so their latency overlaps the (m, l) loads; slots past the
+// sequence's splits (not written by this call) are selected away, never
+// multiplied.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
     constexpr int RPB = 256 / D;            // rows per block
@@ -238,6 +241,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
         const int L = clamp_ctx(p.ctx_lens[b], p.max_ctx) + p.N;
         ns = min(p.n_splits, (L + p.split_len - 1) / p.split_len);
     }
+    // the first OB partial values of this thread's column go out together
+    // with the (m, l) loads; the weights are applied once they are known
+    constexpr int OB = 32;
+    const float *op = p.part_o + (base * p.R + r) * D + t;
+    const int64_t sstride = (int64_t)p.R * D;
+    float ov[OB];
+#pragma unroll
+    for (int k = 0; k < OB; ++k) ov[k] = k < ns_cap ? op[k * sstride] : 0.f;
     const float2 *ml = (const float2 *)p.part_ml;
     constexpr int MLR = kMaxSplits / D;             // splits per thread (upper bound)
     float2 mlv[MLR];
@@ -264,19 +275,26 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
     const float lsum = row_reduce(ls, false);
     __syncthreads();
 
-    const float *op = p.part_o + (base * p.R + r) * D + t;
-    const int64_t sstride = (int64_t)p.R * D;
     float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
-    int sp = 0;
-    for (; sp + 4 <= ns; sp += 4) {
-        const float o0 = op[(sp + 0) * sstride], o1 = op[(sp + 1) * sstride];
-        const float o2 = op[(sp + 2) * sstride], o3 = op[(sp + 3) * sstride];
-        acc0 += w_s[rib][sp + 0] * o0;
-        acc1 += w_s[rib][sp + 1] * o1;
-        acc2 += w_s[rib][sp + 2] * o2;
-        acc3 += w_s[rib][sp + 3] * o3;
+#pragma unroll
+    for (int k = 0; k < OB; k += 4) {
+        acc0 += k + 0 < ns ? w_s[rib][k + 0] * ov[k + 0] : 0.f;
+        acc1 += k + 1 < ns ? w_s[rib][k + 1] * ov[k + 1] : 0.f;
+        acc2 += k + 2 < ns ? w_s[rib][k + 2] * ov[k + 2] : 0.f;
+        acc3 += k + 3 < ns ? w_s[rib][k + 3] * ov[k + 3] : 0.f;
     }
-    for (; sp < ns; ++sp) acc0 += w_s[rib][sp] * op[sp * sstride];
+#pragma unroll 1
+    for (int sp = OB; sp < ns; sp += OB) {
+#pragma unroll
+        for (int k = 0; k < OB; ++k) ov[k] = sp + k < ns ? op[(sp + k) * sstride] : 0.f;
+#pragma unroll
+        for (int k = 0; k < OB; k += 4) {
+            acc0 += sp + k + 0 < ns ? w_s[rib][sp + k + 0] * ov[k + 0] : 0.f;
+            acc1 += sp + k + 1 < ns ? w_s[rib][sp + k + 1] * ov[k + 1] : 0.f;
+            acc2 += sp + k + 2 < ns ? w_s[rib][sp + k + 2] * ov[k + 2] : 0.f;
+            acc3 += sp + k + 3 < ns ? w_s[rib][sp + k + 3] * ov[k + 3] : 0.f;
+        }
+    }
     if (!live) return;
     const float v = ((acc0 + acc1) + (acc2 + acc3)) / lsum;
     const int64_t oi = (((int64_t)b * p.N + n) * p.Hq + h) * D + t;

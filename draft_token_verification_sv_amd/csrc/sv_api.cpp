@@ -133,12 +133,19 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
             pl.pg = 1;
             int nrb = (RT + max_tiles - 1) / max_tiles;
             if (g_attn_rowblocks > 0) nrb = std::max(nrb, std::min(g_attn_rowblocks, RT));
+            // More row blocks (each reads the same KV tiles, from L2 after the
+            // first) shorten the per-split work but multiply the splits, whose
+            // fp32 partials the merge reads back.  Added while the partials
+            // exceed a fraction of the KV bytes: 35% on the pipelined kernel
+            // (whose per-stage cost grows with the tiles per wave), 15% on the
+            // register-staged one (measured on the workloads of the bench).
+            const double max_part = pl.kind == kMfmaDma ? 0.35 : 0.15;
             for (; g_attn_rowblocks == 0;) {
                 const int tpb = (RT + nrb - 1) / nrb;
                 splits_for(B * Hkv * nrb, pl.split_len, pl.n_splits);
                 const double part = (double)pl.n_splits * R * (D + 2) * 4.0;
                 const double kvb = (double)L * pos_bytes;
-                if (part <= 0.15 * kvb || tpb <= 2) break;
+                if (part <= max_part * kvb || tpb <= 2) break;
                 ++nrb;
             }
             const int tpb = (RT + nrb - 1) / nrb;
@@ -161,7 +168,7 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
         // split lengths: multiples of the kernel's stage (8 positions for the
         // others), at most kMaxSplits splits per sequence, page ids of a split
         // within the pipelined kernel's LDS table
-        const int64_t q = pl.kind == kMfmaDma ? 32 * pl.pg : 8;
+        const int64_t q = pl.kind == kMfmaDma ? 32 * pl.pg : 8;    // a power of two
         const int64_t smax = std::min(round_up(L, q), max_split / q * q);
         const int64_t smin = std::max<int64_t>(q, round_up(ceil_div(L, kMaxSplits), q));
         pl.split_q = (int)q;

@@ -156,16 +156,18 @@ def test_attention_position_groups(sv, pg):
     check_attention(case, out, lse)
 
 
-def test_attention_max_batch(sv):
-    """1024 sequences (the batch limit): four per thread in the schedule."""
-    say("[attn-maxbatch] B=1024")
-    cfg = workloads.Config("max batch", 1024, 16, 4, 128, 4, "bf16", "bf16", "f32", 50, 0, ctx_hi=60,
+@pytest.mark.parametrize("B", [64, 65, 1024])
+def test_attention_large_batch(sv, B):
+    """Batch sizes at the schedule's paths: one wavefront (<= 64 sequences),
+    the whole workgroup, and 1024 sequences (the limit, four per thread)."""
+    say(f"[attn-batch] B={B}")
+    cfg = workloads.Config("large batch", B, 16, 4, 128, 4, "bf16", "bf16", "f32", 50, 0, ctx_hi=60 if B > 100 else 700,
                            tree="ddtree", q_std=0.5, kv_std=0.5, draft_rule="tree")
-    case = workloads.make_case(cfg, seed=21)
+    case = workloads.make_case(cfg, seed=21 + B)
     dc = DeviceCase(case)
     out, lse = dc.attn()
     torch.cuda.synchronize()
-    check_attention(case, out, lse, batch=[0, 1, 255, 256, 511, 777, 1023])
+    check_attention(case, out, lse, batch=sorted({0, 1, B // 4, B // 2, B - 2, B - 1}))
 
 
 FULL = [("C2", None, None), ("C3", None, None), ("C4", [0, 7, 23], None), ("C5", None, [0, 3, 7])]
