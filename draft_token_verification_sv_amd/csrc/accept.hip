@@ -7,19 +7,17 @@
 // reads budget+1 logits rows, "Key breakthroughs"].
 //
 // One launch.  Workgroup (row, chunk) streams `chunk` logits of one row with
-// 16-byte loads (all of a thread's loads in flight at once) and reduces them
-// to a 64-bit key
+// 16-byte loads (up to 8 per thread in flight at once) and reduces them to a
+// 64-bit key
 //     (order-preserving fp32 bits << 32) | (0xFFFFFFFF - index),
-// whose maximum is the largest value at the lowest index.  Completion is
-// tracked with device-scope atomics only (no cache flushes):
+// whose maximum is the largest value at the lowest index (wavefront maxima by
+// DPP lane moves).  Completion is tracked with device-scope atomics only (no
+// cache flushes):
 //   1. atomic max of the key into keys[row]; wait for its return;
-//   2. add 1 to rows_done[row]; the workgroup that completes the row (the
-//      last of its `chunks` arrivals) sets that counter back to zero and adds
-//      1 to seqs_done[b];
-//   3. the workgroup that completes sequence b (the N-th row) takes every
-//      key of the sequence with an atomic exchange against zero, runs the
-//      acceptance walk for its <= 64 nodes in one wavefront and writes the
-//      outputs.
+//   2. add 1 to done[b]; the workgroup that brings it to N * chunks (the last
+//      arrival of sequence b) sets it back to zero, takes every key of the
+//      sequence with an atomic exchange against zero, runs the acceptance walk
+//      for its <= 64 nodes in one wavefront and writes the outputs.
 // Each step is issued only after the previous atomic has returned, and all of
 // them act on the device-coherent copy, so the last workgroup sees every
 // key.  Every call leaves the keys and counters it used at zero.
@@ -39,14 +37,27 @@ __device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsig
     return a > b ? a : b;
 }
 
+// one DPP step of a 64-bit running maximum: lanes outside the move's source
+// range (and rows outside `rmask`) contribute the identity 0
+#define SV_DPP_MAX64(k, ctrl, rmask)                                                                      \
+    do {                                                                                               \
+        const uint32_t lo_ = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k), ctrl, rmask, 0xf, false); \
+        const uint32_t hi_ = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)((k) >> 32), ctrl, rmask, 0xf, false); \
+        k = umax64(k, ((unsigned long long)hi_ << 32) | lo_);                                         \
+    } while (0)
+
+// maximum over the 64 lanes (row shifts 1, 2, 4, 8, then the broadcasts of
+// lanes 15 and 31 leave the running maximum of all lanes in lane 63)
 __device__ __forceinline__ unsigned long long wave_max64(unsigned long long k) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)k, m, 64);
-        const uint32_t hi = __shfl_xor((uint32_t)(k >> 32), m, 64);
-        k = umax64(k, ((unsigned long long)hi << 32) | lo);
-    }
-    return k;
+    SV_DPP_MAX64(k, 0x111, 0xf);
+    SV_DPP_MAX64(k, 0x112, 0xf);
+    SV_DPP_MAX64(k, 0x114, 0xf);
+    SV_DPP_MAX64(k, 0x118, 0xf);
+    SV_DPP_MAX64(k, 0x142, 0xa);
+    SV_DPP_MAX64(k, 0x143, 0xc);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 63);
+    return ((unsigned long long)hi << 32) | lo;
 }
 
 // vmcnt(0): every vector memory operation of this wave (the atomics above
@@ -67,7 +78,7 @@ __global__ __launch_bounds__(256) void argmax_accept_kernel(AcceptParams p) {
     const int64_t lo = (int64_t)c * p.chunk;
     const int64_t hi = min<int64_t>(V, lo + p.chunk);
     constexpr int EPL = F32 ? 4 : 8;                      // elements per 16-byte load
-    constexpr int UNR = 4;                                // loads in flight per thread
+    constexpr int UNR = 8;                                // loads in flight per thread
 
     unsigned long long best = 0ull;
     if constexpr (VEC) {
@@ -119,30 +130,24 @@ __global__ __launch_bounds__(256) void argmax_accept_kernel(AcceptParams p) {
     __syncthreads();
     if (tid == 0) {
         const unsigned long long k = umax64(umax64(red[0], red[1]), umax64(red[2], red[3]));
-        int last = 0;
-        const unsigned long long was =
-            __hip_atomic_fetch_max(&p.keys[row], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // consuming `was` keeps the returning form of the atomic, whose
         // result comes back only once it has been performed
+        const unsigned long long was =
+            __hip_atomic_fetch_max(&p.keys[row], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         asm volatile("" : : "v"((uint32_t)was));
         wait_vm0();
-        const unsigned int rd =
-            __hip_atomic_fetch_add(&p.rows_done[row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (rd == (unsigned int)(p.n_chunks - 1)) {
-            __hip_atomic_store(&p.rows_done[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const unsigned int sd =
-                __hip_atomic_fetch_add(&p.seqs_done[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            last = sd == (unsigned int)(p.N - 1);
-        }
-        last_s = last;
+        const unsigned int done =
+            __hip_atomic_fetch_add(&p.seqs_done[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_s = done == (unsigned int)(p.N * p.n_chunks - 1);
     }
     __syncthreads();
     if (!last_s) return;
 
-    // ---- the workgroup that completed sequence b: take keys, then walk --------
+    // ---- the last arrival of sequence b: take keys, then walk -----------------
     const int N = p.N;
     const int wave = tid >> 6, lane = tid & 63;
     if (wave != 0) return;
+    if (lane == 0) __hip_atomic_store(&p.seqs_done[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (lane < N) {
         const unsigned long long k =
             __hip_atomic_exchange(&p.keys[(int64_t)b * N + lane], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -150,7 +155,6 @@ __global__ __launch_bounds__(256) void argmax_accept_kernel(AcceptParams p) {
         dr_s[lane] = p.draft[(int64_t)b * N + lane];
         par_s[lane] = p.parent[(int64_t)b * N + lane];
     }
-    if (lane == 0) __hip_atomic_store(&p.seqs_done[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0);           // the LDS writes of all lanes (one wave: no barrier)
     __builtin_amdgcn_wave_barrier();
 

@@ -43,22 +43,29 @@ namespace {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-template <int D, int NT, int PG>
+template <int D, int NT, int PG, bool Q4>
 struct DCfg {
     static constexpr int W = D >= 128 ? SV_SWZ_W : 8;          // swizzle width (chunks)
-    static constexpr int T = 32 * PG;                 // positions per stage
-    static constexpr int ROWB = D * 2;                // bytes per K / V row
-    static constexpr int KBYTES = T * ROWB;           // K part of a stage
-    static constexpr int STAGE = 2 * KBYTES;
+    // positions per stage: 32 per position group for bf16; for the 4-bit
+    // cache 32768 / D, so a stage is 36 whole 1 KB loads (9 per wave)
+    static constexpr int T = Q4 ? 32768 / D : 32 * PG;
+    static constexpr int ROWB = D * 2;                // bytes per bf16 K / V row
+    static constexpr int CROWB = D / 2;               // 4-bit codes per row
+    static constexpr int SROWB = D / 16;              // fp16 scales per row
+    static constexpr int KBYTES = Q4 ? T * CROWB : T * ROWB;   // K part of a stage
+    static constexpr int STAGE = Q4 ? 2 * T * (CROWB + SROWB) : 2 * KBYTES;
     static constexpr int S_RAW = 131072 / STAGE;
-    static constexpr int S = S_RAW < 2 ? 2 : (S_RAW > 8 ? 8 : S_RAW);   // ring depth
+    static constexpr int S = Q4 ? 3 : (S_RAW < 2 ? 2 : (S_RAW > 8 ? 8 : S_RAW));   // ring depth
     static constexpr int NKB = STAGE / 1024;          // 1 KB DMA instructions per stage
     static constexpr int LPW = NKB / 4;               // per wave
-    static constexpr int RPK = 1024 / ROWB;           // rows per DMA instruction
+    static constexpr int RPK = 1024 / ROWB;           // rows per DMA instruction (bf16)
     static constexpr int RG = 4 / PG;
     static constexpr int KS = D / 32;
     static constexpr int DT = D / 16;
-    static_assert(NKB % 8 == 0, "stage split evenly between waves and K/V");
+    static constexpr int CH = Q4 ? T / 32 : 1;        // 32-position chunks per stage, in turn
+    static constexpr int STAGING = Q4 ? 2 * 32 * ROWB : 0;   // dequantised K and V of one chunk
+    static_assert(Q4 ? (NKB % 4 == 0) : (NKB % 8 == 0), "stage split evenly between waves (and K/V)");
+    static_assert(!Q4 || (D == 256 && PG == 1), "4-bit stages: head dim 256, one position group");
     static_assert(LPW * (S - 2) < 64, "vmcnt range");
 };
 
@@ -100,11 +107,12 @@ __device__ __forceinline__ void dma16(uint32_t lds_base, const void *gptr) {
 
 constexpr int kMaxSplitPages = 512;
 
-template <int D, int NT, int PG, bool PAGED>
+template <int D, int NT, int PG, bool PAGED, bool Q4>
 __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
-    using C = DCfg<D, NT, PG>;
+    using C = DCfg<D, NT, PG, Q4>;
     constexpr int T = C::T, S = C::S;
     __shared__ __attribute__((aligned(1024))) uint8_t ring[S * C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t staging[Q4 ? C::STAGING : 16];
     __shared__ int par_s[64];
     __shared__ uint64_t anc_s[64];
     __shared__ int pages_s[PAGED ? kMaxSplitPages : 1];
@@ -149,21 +157,37 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
     // ---- DMA issue: instruction j of this wave covers 1 KB of the stage ------
     const uint8_t *kbase = (const uint8_t *)p.kv.k;
     const uint8_t *vbase = (const uint8_t *)p.kv.v;
+    const uint8_t *ksbase = (const uint8_t *)p.kv.ks;
+    const uint8_t *vsbase = (const uint8_t *)p.kv.vs;
     const int64_t head_row0 = ((int64_t)b * p.Hkv + kvh) * p.kv.capacity;   // contiguous
     const uint32_t ring_u32 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)ring;
 
-    // Lane constants of DMA instruction j: row within the stage and byte offset
-    // of its (swizzled) 16-byte chunk.
+    // Lane constants of DMA instruction j: row within the stage, byte offset of
+    // the lane's 16 bytes within that row, and (4-bit cache) the array it reads:
+    // a 4-bit stage is [K codes][V codes][K scales][V scales], rows in order.
+    // bf16 rows are swizzled in 16-byte chunks as they land.
     int dma_row[C::LPW];
     uint32_t dma_off[C::LPW];
+    int dma_arr[C::LPW];
 #pragma unroll
     for (int j = 0; j < C::LPW; ++j) {
         const int kbi = wave * C::LPW + j;
-        const int kb_in = kbi >= C::NKB / 2 ? kbi - C::NKB / 2 : kbi;
-        const int row = kb_in * C::RPK + (lane * 16) / C::ROWB;
-        const int chunk = ((lane * 16) % C::ROWB / 16) ^ swz<C::W>(row);
-        dma_row[j] = row;
-        dma_off[j] = (uint32_t)(row * C::ROWB + chunk * 16);
+        if constexpr (Q4) {
+            constexpr int KCI = C::T * C::CROWB / 1024, KSI = C::T * C::SROWB / 1024;
+            const int arr = kbi < KCI ? 0 : (kbi < 2 * KCI ? 1 : (kbi < 2 * KCI + KSI ? 2 : 3));
+            const int start = arr == 0 ? 0 : (arr == 1 ? KCI : (arr == 2 ? 2 * KCI : 2 * KCI + KSI));
+            const int rb_ = arr < 2 ? C::CROWB : C::SROWB;
+            dma_arr[j] = arr;
+            dma_row[j] = ((kbi - start) * 1024 + lane * 16) / rb_;
+            dma_off[j] = (uint32_t)((lane * 16) % rb_);
+        } else {
+            const int kb_in = kbi >= C::NKB / 2 ? kbi - C::NKB / 2 : kbi;
+            const int row = kb_in * C::RPK + (lane * 16) / C::ROWB;
+            const int chunk = ((lane * 16) % C::ROWB / 16) ^ swz<C::W>(row);
+            dma_arr[j] = kbi >= C::NKB / 2;
+            dma_row[j] = row;
+            dma_off[j] = (uint32_t)(row * C::ROWB + chunk * 16);
+        }
     }
 
     auto issue = [&](int st) {
@@ -173,30 +197,47 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
 #pragma unroll
         for (int j = 0; j < C::LPW; ++j) {
             const int kbi = wave * C::LPW + j;                     // wave-uniform
-            const bool is_v = kbi >= C::NKB / 2;
             const uint8_t *g;
-            if constexpr (!PAGED) {
-                if (full) {
-                    g = (is_v ? vbase : kbase) + (head_row0 + tb) * C::ROWB + dma_off[j];
+            if constexpr (Q4) {
+                const int arr = dma_arr[j];
+                const uint8_t *gb = arr == 0 ? kbase : (arr == 1 ? vbase : (arr == 2 ? ksbase : vsbase));
+                const int rb_ = arr < 2 ? C::CROWB : C::SROWB;
+                const int pos = full ? tb + dma_row[j] : min(tb + dma_row[j], p1 - 1);
+                int64_t ri;
+                if constexpr (!PAGED) {
+                    ri = head_row0 + pos;
                 } else {
-                    const int pos = min(tb + dma_row[j], p1 - 1);
-                    g = (is_v ? vbase : kbase) + (head_row0 + pos) * C::ROWB +
-                        (dma_off[j] - (uint32_t)(dma_row[j] * C::ROWB));
+                    const int ps = p.kv.page_size;
+                    const int pq = ps_shift >= 0 ? pos >> ps_shift : pos / ps;
+                    const int pr = pos - pq * ps;
+                    ri = ((int64_t)pages_s[pq - first_page] * p.Hkv + kvh) * ps + pr;
                 }
+                g = gb + ri * rb_ + dma_off[j];
             } else {
-                const int ps = p.kv.page_size;
-                const int pos = min(tb + dma_row[j], p1 - 1);
-                int pq, pr;
-                if (ps_shift >= 0) {
-                    pq = pos >> ps_shift;
-                    pr = pos & (ps - 1);
+                const bool is_v = dma_arr[j] != 0;
+                if constexpr (!PAGED) {
+                    if (full) {
+                        g = (is_v ? vbase : kbase) + (head_row0 + tb) * C::ROWB + dma_off[j];
+                    } else {
+                        const int pos = min(tb + dma_row[j], p1 - 1);
+                        g = (is_v ? vbase : kbase) + (head_row0 + pos) * C::ROWB +
+                            (dma_off[j] - (uint32_t)(dma_row[j] * C::ROWB));
+                    }
                 } else {
-                    pq = pos / ps;
-                    pr = pos - pq * ps;
+                    const int ps = p.kv.page_size;
+                    const int pos = min(tb + dma_row[j], p1 - 1);
+                    int pq, pr;
+                    if (ps_shift >= 0) {
+                        pq = pos >> ps_shift;
+                        pr = pos & (ps - 1);
+                    } else {
+                        pq = pos / ps;
+                        pr = pos - pq * ps;
+                    }
+                    const int pgid = pages_s[pq - first_page];
+                    const int64_t ri = ((int64_t)pgid * p.Hkv + kvh) * ps + pr;
+                    g = (is_v ? vbase : kbase) + ri * C::ROWB + (dma_off[j] - (uint32_t)(dma_row[j] * C::ROWB));
                 }
-                const int pgid = pages_s[pq - first_page];
-                const int64_t ri = ((int64_t)pgid * p.Hkv + kvh) * ps + pr;
-                g = (is_v ? vbase : kbase) + ri * C::ROWB + (dma_off[j] - (uint32_t)(dma_row[j] * C::ROWB));
             }
             dma16(__builtin_amdgcn_readfirstlane(slot + (uint32_t)(kbi * 1024)), g);
         }
@@ -266,113 +307,33 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
     // waits for those stages.
     wait_vm<0>();
 
-    // ---- main loop ---------------------------------------------------------
-#pragma unroll 1
-    for (int it = 0; it < n_st; ++it) {
-        wait_vm_dyn<C::LPW, S - 2>(min(S - 2, n_st - 1 - it));   // this wave's part of stage `it` landed
-        __syncthreads();                                           // everyone's part landed; slot it-1 free
-        if (it + S - 1 < n_st) issue(it + S - 1);
-
-        const uint8_t *Kl = ring + (it % S) * C::STAGE;
-        const uint8_t *Vl = Kl + C::KBYTES;
-        const int cb = pg * 32;
-        const int abase = p0 + it * T + cb;
-        if (abase >= p1) continue;
-
+    // ---- one 32-position chunk of K / V rows in LDS (natural order, 16-byte
+    // chunks swizzled): scores, masks, online softmax, O^T += V^T P^T ----------
+    auto compute = [&](const uint8_t *Kl, const uint8_t *Vl, const int cb, const int abase) {
         // Every wave runs all NT tile slots: a slot without rows holds zero
         // queries, gives finite scores and is never written back, and no
         // branch breaks the stream of matrix instructions (the waves meet at
         // the next barrier anyway).
+        //
+        // Order within a stage (one wavefront, so overlap comes from the
+        // instruction order): the K fragment reads, then the Q K^T matrix
+        // instructions with the V^T fragment reads of this stage slotted
+        // between them; the masks and lane-local maxima; then per tile the
+        // exponentials of tile i+1 slotted between the V^T P^T matrix
+        // instructions of tile i.
+        const uint8_t *kp = Kl + cb * C::ROWB + k_lane;
+        const uint8_t *vp = Vl + cb * C::ROWB + v_lane;
         f32x4 sacc[NT][2];
+        bf16x8 vf[C::DT];
         {
             // K fragment (t, k) sits at k_lane + 4t rows + (k / (W/4)) * 16W bytes
-            // + a lane constant that depends only on k % (W/4)
-            const uint8_t *kp = Kl + cb * C::ROWB + k_lane;
-            bf16x8 kf[2][C::KS];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int k = 0; k < C::KS; ++k)
-                    kf[t][k] = *(const bf16x8 *)(kp + 4 * t * C::ROWB + (k / (W / 4)) * (W * 16) + k_off[k % (W / 4)]);
-            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int i = 0; i < NT; ++i)
-                    sacc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][0], qf[i][0], zero, 0, 0, 0);
-#pragma unroll
-            for (int k = 1; k < C::KS; ++k)
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int i = 0; i < NT; ++i)
-                        sacc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][k], qf[i][k], sacc[i][t], 0, 0, 0);
-        }
-
-        const bool need_mask = (abase + 32 > ctx) || (abase + 32 > p1);
-        bf16x8 pb[NT];
-#pragma unroll
-        for (int i = 0; i < NT; ++i) {
-            // raw scores; the softmax scale (log2 units) is applied inside the
-            // exponent, so the maxima below are raw too
-            float sv[8];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sv[4 * t + j] = sacc[i][t][j];
-            if (need_mask) {
-                const uint64_t anc = node_of[i] >= 0 ? anc_s[node_of[i]] : 0ull;
-                const int rel0 = abase + 8 * qd - ctx;      // draft index of value 0
-                const int lim = p1 - (abase + 8 * qd);      // values e < lim are in the split
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int rel = rel0 + e;
-                    bool vis = e < lim;
-                    if (rel >= 0) vis = vis && (((anc >> (rel & 63)) & 1ull) != 0ull);
-                    sv[e] = vis ? sv[e] : -INFINITY;
-                }
-            }
-            // lazy rescale: the reference m_ref (log2 units) moves only when some
-            // score exceeds it by more than 8; a lane's own 8 values decide
-            // whether the wave looks at row maxima at all
-            float cm = sv[0];
-#pragma unroll
-            for (int e = 1; e < 8; ++e) cm = fmaxf(cm, sv[e]);
-            if (__any(cm * p.scale_log2 > m_ref[i] + 8.f)) {
-                cm = fmaxf(cm, xor_shfl(cm, 16));
-                cm = fmaxf(cm, xor_shfl(cm, 32));
-                const float cms = cm * p.scale_log2;
-                const bool need = cms > m_ref[i] + 8.f;
-                const float mn = need ? cms : m_ref[i];
-                const float alpha = need ? exp2f(m_ref[i] - mn) : 1.f;
-                m_ref[i] = mn;
-                l_sum[i] *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < C::DT; ++dt) o[i][dt] *= alpha;
-            }
-            const float mu = (m_ref[i] == -INFINITY) ? 0.f : m_ref[i];
-            float ls = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                // 2^(s * scale - m): v_exp_f32 (results below 2^-126 flush to 0)
-                const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], p.scale_log2, -mu));
-                ls += pr;
-                pb[i][e] = (__bf16)pr;
-            }
-            l_sum[i] += ls;
-        }
-
-        // O^T += V^T P^T: V^T fragments by transposed reads of the natural layout;
-        // fragment (dt, hh) sits at v_lane + 4hh rows + (dt / (W/2)) * 16W bytes +
-        // a lane constant that depends only on dt % (W/2)
-        const uint8_t *vp = Vl + cb * C::ROWB + v_lane;
-        constexpr int VB = C::DT < 8 ? C::DT : 8;                 // fragments per batch
-#pragma unroll
-        for (int d0 = 0; d0 < C::DT; d0 += VB) {
-            bf16x8 vf[VB];
-#pragma unroll
-            for (int dd = 0; dd < VB; ++dd) {
-                const int dt = d0 + dd;
+            // + a lane constant that depends only on k % (W/4); V^T fragment
+            // (dt, hh) at v_lane + 4hh rows + (dt / (W/2)) * 16W bytes + a lane
+            // constant that depends only on dt % (W/2)
+            auto kread = [&](int t, int k) {
+                return *(const bf16x8 *)(kp + 4 * t * C::ROWB + (k / (W / 4)) * (W * 16) + k_off[k % (W / 4)]);
+            };
+            auto vread = [&](int dt) {
                 s16x4 h[2];
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh)
@@ -381,13 +342,174 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
                             vp + 4 * hh * C::ROWB + (dt / (W / 2)) * (W * 16) + v_off[dt % (W / 2)]));
                 const short __attribute__((ext_vector_type(8))) w8 = {h[0][0], h[0][1], h[0][2], h[0][3],
                                                                       h[1][0], h[1][1], h[1][2], h[1][3]};
-                vf[dd] = __builtin_bit_cast(bf16x8, w8);
+                return __builtin_bit_cast(bf16x8, w8);
+            };
+            // k-step by k-step: the K fragments of step k+1 and a share of the
+            // V^T fragments are read while the matrix instructions of step k run
+            constexpr int VPK = (C::DT + C::KS - 1) / C::KS;     // V^T fragments per k-step
+            bf16x8 kc[2] = {kread(0, 0), kread(1, 0)};
+#pragma unroll
+            for (int k = 0; k < C::KS; ++k) {
+                bf16x8 kn[2];
+                if (k + 1 < C::KS) {
+                    kn[0] = kread(0, k + 1);
+                    kn[1] = kread(1, k + 1);
+                }
+#pragma unroll
+                for (int v = 0; v < VPK; ++v)
+                    if (k * VPK + v < C::DT) vf[k * VPK + v] = vread(k * VPK + v);
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int i = 0; i < NT; ++i)
+                        sacc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            kc[t], qf[i][k], k == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[i][t], 0, 0, 0);
+                if (k + 1 < C::KS) {
+                    kc[0] = kn[0];
+                    kc[1] = kn[1];
+                }
             }
+        }
+
+        // raw scores; the softmax scale (log2 units) is applied inside the
+        // exponent, so the maxima below are raw too
+        float sv[NT][8];
 #pragma unroll
-            for (int dd = 0; dd < VB; ++dd)
+        for (int i = 0; i < NT; ++i)
 #pragma unroll
-                for (int i = 0; i < NT; ++i)
-                    o[i][d0 + dd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dd], pb[i], o[i][d0 + dd], 0, 0, 0);
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sv[i][4 * t + j] = sacc[i][t][j];
+        if ((abase + 32 > ctx) || (abase + 32 > p1)) {
+            const int rel0 = abase + 8 * qd - ctx;          // draft index of value 0
+            const int lim = p1 - (abase + 8 * qd);          // values e < lim are in the split
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+                const uint64_t anc = node_of[i] >= 0 ? anc_s[node_of[i]] : 0ull;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int rel = rel0 + e;
+                    bool vis = e < lim;
+                    if (rel >= 0) vis = vis && (((anc >> (rel & 63)) & 1ull) != 0ull);
+                    sv[i][e] = vis ? sv[i][e] : -INFINITY;
+                }
+            }
+        }
+        // lazy rescale: the reference m_ref (log2 units) moves only when some
+        // score exceeds it by more than 8; a lane's own 8 values decide
+        // whether the wave looks at row maxima at all
+        float cm[NT];
+        bool grow = false;
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            cm[i] = sv[i][0];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) cm[i] = fmaxf(cm[i], sv[i][e]);
+            grow = grow || (cm[i] * p.scale_log2 > m_ref[i] + 8.f);
+        }
+        if (__any(grow)) {
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+                float c = fmaxf(cm[i], xor_shfl(cm[i], 16));
+                c = fmaxf(c, xor_shfl(c, 32));
+                const float cms = c * p.scale_log2;
+                const bool need = cms > m_ref[i] + 8.f;
+                const float mn = need ? cms : m_ref[i];
+                const float alpha = need ? exp2f(m_ref[i] - mn) : 1.f;
+                m_ref[i] = mn;
+                l_sum[i] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt) o[i][dt] *= alpha;
+            }
+        }
+
+        // P = 2^(s * scale - m) (v_exp_f32; results below 2^-126 flush to 0)
+        bf16x8 pb[NT];
+        auto softmax_tile = [&](int i) {
+            const float mu = (m_ref[i] == -INFINITY) ? 0.f : m_ref[i];
+            float ls = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i][e], p.scale_log2, -mu));
+                ls += pr;
+                pb[i][e] = (__bf16)pr;
+            }
+            l_sum[i] += ls;
+        };
+        // O^T += V^T P^T, the exponentials of the next tile between the
+        // matrix instructions of this one
+        softmax_tile(0);
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt)
+                o[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pb[i], o[i][dt], 0, 0, 0);
+            if (i + 1 < NT) {
+                softmax_tile(i + 1);
+#pragma unroll
+                for (int k = 0; k < C::DT; ++k) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
+                }
+            }
+        }
+    };
+
+    // ---- 4-bit cache: the 256 threads turn chunk c of a stage into bf16 rows in
+    // `staging` (thread: one row, one 32-value block; value = d * (code - 8)
+    // exactly in fp32, rounded to nearest-even bf16) ---------------------------
+    auto dequant = [&](int slot, int c) {
+        if constexpr (Q4) {
+            const uint8_t *stg = ring + slot * C::STAGE;
+            const int row = tid >> 3, blk = tid & 7;
+#pragma unroll
+            for (int which = 0; which < 2; ++which) {
+                const u32x4 w = *(const u32x4 *)(stg + which * C::T * C::CROWB + (c * 32 + row) * C::CROWB + blk * 16);
+                const float sc = fp16_bits_to_f32(*(const uint16_t *)(stg + 2 * C::T * C::CROWB +
+                                                                    which * C::T * C::SROWB +
+                                                                    (c * 32 + row) * C::SROWB + blk * 2));
+                const float off = -8.f * sc;
+                uint8_t *dst = staging + which * 32 * C::ROWB + row * C::ROWB;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    // byte t of the row holds values 2t (low nibble) and 2t + 1
+                    const uint32_t lo = w[m] & 0x0F0F0F0Fu, hi = (w[m] >> 4) & 0x0F0F0F0Fu;
+                    u32x4 out;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        out[k] = pack_bf16x2(__builtin_fmaf((float)((lo >> (8 * k)) & 0xFFu), sc, off),
+                                             __builtin_fmaf((float)((hi >> (8 * k)) & 0xFFu), sc, off));
+                    *(u32x4 *)(dst + ((4 * blk + m) ^ swz<C::W>(row)) * 16) = out;
+                }
+            }
+        }
+    };
+
+    // ---- main loop ---------------------------------------------------------
+#pragma unroll 1
+    for (int it = 0; it < n_st; ++it) {
+        wait_vm_dyn<C::LPW, S - 2>(min(S - 2, n_st - 1 - it));   // this wave's part of stage `it` landed
+        __syncthreads();                                           // everyone's part landed; slot it-1 free
+        if (it + S - 1 < n_st) issue(it + S - 1);
+
+        if constexpr (Q4) {
+#pragma unroll 1
+            for (int c = 0; c < C::CH; ++c) {
+                const int abase = p0 + it * T + c * 32;
+                if (abase >= p1) break;                            // uniform
+                if (c > 0) __syncthreads();                        // staging free again
+                dequant(it % S, c);
+                __syncthreads();
+                if (tile_on[0]) compute(staging, staging + 32 * C::ROWB, 0, abase);
+            }
+        } else {
+            const uint8_t *Kl = ring + (it % S) * C::STAGE;
+            const int cb = pg * 32;
+            const int abase = p0 + it * T + cb;
+            // a wavefront whose row group has no rows (fewer row tiles than
+            // wavefronts) only issues its share of the loads
+            if (abase >= p1 || !tile_on[0]) continue;
+            compute(Kl, Kl + C::KBYTES, cb, abase);
         }
     }
 
@@ -450,42 +572,51 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
     }
 }
 
-template <int D, int NT, int PG, bool PAGED>
+template <int D, int NT, int PG, bool PAGED, bool Q4>
 hipError_t launch_one(const AttnParams &p, hipStream_t st) {
     const int grid = ((p.n_units + 7) / 8) * 8 * p.n_rowblocks;
-    hipLaunchKernelGGL((attn_dma_kernel<D, NT, PG, PAGED>), dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((attn_dma_kernel<D, NT, PG, PAGED, Q4>), dim3(grid), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
 template <int D, bool PAGED>
-hipError_t launch_shape(const AttnParams &p, int nt, int pg, hipStream_t st) {
+hipError_t launch_shape(const AttnParams &p, int nt, int pg, bool q4, hipStream_t st) {
+    if (q4) {
+        if constexpr (D == 256) {
+            if (pg != 1) return hipErrorInvalidValue;
+            if (nt == 1) return launch_one<D, 1, 1, PAGED, true>(p, st);
+            if (nt == 2) return launch_one<D, 2, 1, PAGED, true>(p, st);
+            if (nt == 3) return launch_one<D, 3, 1, PAGED, true>(p, st);
+        }
+        return hipErrorInvalidValue;
+    }
     if (pg == 1) {
-        if (nt == 1) return launch_one<D, 1, 1, PAGED>(p, st);
-        if (nt == 2) return launch_one<D, 2, 1, PAGED>(p, st);
-        if (nt == 3) return launch_one<D, 3, 1, PAGED>(p, st);
+        if (nt == 1) return launch_one<D, 1, 1, PAGED, false>(p, st);
+        if (nt == 2) return launch_one<D, 2, 1, PAGED, false>(p, st);
+        if (nt == 3) return launch_one<D, 3, 1, PAGED, false>(p, st);
     } else if (nt == 1 && pg == 2) {
-        return launch_one<D, 1, 2, PAGED>(p, st);
+        return launch_one<D, 1, 2, PAGED, false>(p, st);
     } else if (nt == 1 && pg == 4 && D <= 128) {
-        return launch_one<D, 1, (D <= 128 ? 4 : 2), PAGED>(p, st);
+        return launch_one<D, 1, (D <= 128 ? 4 : 2), PAGED, false>(p, st);
     }
     return hipErrorInvalidValue;
 }
 
 template <int D>
-hipError_t launch_d(const AttnParams &p, int nt, int pg, hipStream_t st) {
-    return p.kv.page_table != nullptr ? launch_shape<D, true>(p, nt, pg, st)
-                                      : launch_shape<D, false>(p, nt, pg, st);
+hipError_t launch_d(const AttnParams &p, int nt, int pg, bool q4, hipStream_t st) {
+    return p.kv.page_table != nullptr ? launch_shape<D, true>(p, nt, pg, q4, st)
+                                      : launch_shape<D, false>(p, nt, pg, q4, st);
 }
 
 }  // namespace
 
 int attn_dma_max_split_pages() { return kMaxSplitPages; }
 
-hipError_t launch_attn_dma(const AttnParams &p, int D, int nt, int pg, hipStream_t st) {
+hipError_t launch_attn_dma(const AttnParams &p, int D, int nt, int pg, bool q4, hipStream_t st) {
     switch (D) {
-        case 64: return launch_d<64>(p, nt, pg, st);
-        case 128: return launch_d<128>(p, nt, pg, st);
-        case 256: return launch_d<256>(p, nt, pg, st);
+        case 64: return launch_d<64>(p, nt, pg, q4, st);
+        case 128: return launch_d<128>(p, nt, pg, q4, st);
+        case 256: return launch_d<256>(p, nt, pg, q4, st);
     }
     return hipErrorInvalidValue;
 }

@@ -30,22 +30,17 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
     const int tid = threadIdx.x;
     const int N = p.N;
 
+    // the length, the accept count and this thread's path entry load together
     const int ctx = clamp_ctx(p.ctx_lens[b], p.max_ctx);
     const int a = p.accept_len[b];
+    const int pj = (tid >= 1 && tid < N) ? p.path[(int64_t)b * N + tid] : -1;
     const bool a_ok = a >= 0 && a < N;
     if (p.new_lens != nullptr && which == 0 && h == 0 && layer == 0 && tid == 0)
         p.new_lens[b] = a_ok ? ctx + a + 1 : ctx;
     if (!a_ok) return;
 
     // moving rows: j in [1, a] with j < path[j] < N
-    if (tid < 64) {
-        int src = -1;
-        if (tid >= 1 && tid <= a) {
-            const int pj = p.path[(int64_t)b * N + tid];
-            if (pj > tid && pj < N) src = pj;
-        }
-        src_s[tid] = src;
-    }
+    if (tid < 64) src_s[tid] = (tid >= 1 && tid <= a && pj > tid && pj < N) ? pj : -1;
     __syncthreads();
 
     const int D = p.D;

@@ -88,8 +88,9 @@ struct AttnPlan {
 // gets the dynamic schedule (split length chosen by the kernel from the
 // actual lengths, see attn_sched.h).  Row blocks are added while the split
 // partials would exceed ~15% of the KV bytes.
-//   bf16 queries, >= 16 packed rows:  bf16 KV -> direct-to-LDS pipelined kernel
-//                                     4-bit KV -> register-staged kernel
+//   bf16 queries, >= 16 packed rows:  bf16 KV, 4-bit KV of head dim 256 ->
+//                                     direct-to-LDS pipelined kernel
+//                                     other 4-bit KV -> register-staged kernel
 //   otherwise                         vector-ALU kernel
 AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int Hkv, int max_ctx,
                    int page_size) {
@@ -98,7 +99,10 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
     const int R = G * N;
     const int64_t L = (int64_t)max_ctx + N;
     const bool mfma = (q_dtype == SV_BF16) && (kv_dtype == SV_BF16 || kv_dtype == SV_Q4) && R >= 16;
-    pl.kind = !mfma ? kValu : (kv_dtype == SV_BF16 ? kMfmaDma : kMfmaStaged);
+    // the pipelined kernel takes bf16 caches of any head dim and 4-bit caches of
+    // head dim 256; other 4-bit caches go to the register-staged kernel
+    const bool q4 = kv_dtype == SV_Q4;
+    pl.kind = !mfma ? kValu : ((kv_dtype == SV_BF16 || (q4 && D == 256)) ? kMfmaDma : kMfmaStaged);
     const int target = g_attn_target_wgs > 0 ? g_attn_target_wgs : (pl.kind == kMfmaDma ? 256 : 512);
     const double pos_bytes = kv_dtype == SV_F32 ? D * 8.0 : (kv_dtype == SV_BF16 ? D * 4.0 : D * 1.125);
     // the pipelined kernel keeps a split's page ids in LDS
@@ -106,11 +110,14 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
                                   ? (int64_t)(attn_dma_max_split_pages() - 1) * page_size
                                   : ((int64_t)1 << 40);
 
+    // static split lengths: multiples of 8 positions, of the 128-position stage
+    // for the pipelined kernel's 4-bit cache
+    const int64_t squant = (pl.kind == kMfmaDma && q4) ? 128 : 8;
     auto splits_for = [&](int units, int &split_len, int &n_splits) {
         const int64_t want = std::max<int64_t>(1, target / std::max(units, 1));
-        int64_t sl = round_up(std::max<int64_t>(ceil_div(L, want), 8), 8);
-        sl = std::max<int64_t>(sl, round_up(ceil_div(L, kMaxSplits), 8));   // merge keeps <= kMaxSplits weights
-        sl = std::min(sl, max_split);
+        int64_t sl = round_up(std::max<int64_t>(ceil_div(L, want), 8), squant);
+        sl = std::max<int64_t>(sl, round_up(ceil_div(L, kMaxSplits), squant));   // merge keeps <= kMaxSplits weights
+        sl = std::min(sl, max_split / squant * squant);
         split_len = (int)sl;
         n_splits = (int)ceil_div(L, split_len);
     };
@@ -121,9 +128,9 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
         // register-staged one
         const int max_tiles = pl.kind == kMfmaDma ? 12 : 8;
         if (RT == 1) {
-            pl.pg = pl.kind == kMfmaDma ? std::min(4, 65536 / (128 * D))
+            pl.pg = pl.kind == kMfmaDma ? (q4 ? 1 : std::min(4, 65536 / (128 * D)))
                                         : std::min(4, (kMfmaTileElems / D) / 32);
-            if (g_attn_posgroups > 0 && pl.kind == kMfmaDma)
+            if (g_attn_posgroups > 0 && pl.kind == kMfmaDma && !q4)
                 pl.pg = std::min(g_attn_posgroups, std::min(4, 65536 / (128 * D)));
             pl.nt = 1;
             pl.rows_per_block = 16;
@@ -168,7 +175,7 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
         // split lengths: multiples of the kernel's stage (8 positions for the
         // others), at most kMaxSplits splits per sequence, page ids of a split
         // within the pipelined kernel's LDS table
-        const int64_t q = pl.kind == kMfmaDma ? 32 * pl.pg : 8;    // a power of two
+        const int64_t q = pl.kind == kMfmaDma ? (q4 ? 128 : 32 * pl.pg) : 8;    // a power of two
         const int64_t smax = std::min(round_up(L, q), max_split / q * q);
         const int64_t smin = std::max<int64_t>(q, round_up(ceil_div(L, kMaxSplits), q));
         pl.split_q = (int)q;
@@ -307,7 +314,7 @@ int sv_verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
 
     hipStream_t st = (hipStream_t)stream;
     hipError_t e;
-    if (pl.kind == kMfmaDma) e = launch_attn_dma(p, D, pl.nt, pl.pg, st);
+    if (pl.kind == kMfmaDma) e = launch_attn_dma(p, D, pl.nt, pl.pg, kv->dtype == SV_Q4, st);
     else if (pl.kind == kMfmaStaged) e = launch_attn_mfma(p, kv->dtype, D, pl.nt, pl.pg, st);
     else e = launch_attn_valu(p, kv->dtype, D, st);
     if (e != hipSuccess) return hip_fail(e);
@@ -319,7 +326,7 @@ int sv_verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
 size_t sv_greedy_accept_workspace_size(int batch, int n_nodes, int vocab) {
     if (batch < 1 || n_nodes < 1 || n_nodes > 64 || vocab < 1) return 0;
     const int64_t rows = (int64_t)batch * n_nodes;
-    return (size_t)(round_up(rows * 8, 256) + round_up(rows * 4, 256) + round_up((int64_t)batch * 4, 256));
+    return (size_t)(round_up(rows * 8, 256) + round_up((int64_t)batch * 4, 256));
 }
 
 int sv_greedy_accept(int batch, int n_nodes, int vocab,
@@ -347,8 +354,7 @@ int sv_greedy_accept(int batch, int n_nodes, int vocab,
     p.argmax = argmax;
     const int64_t rows = (int64_t)batch * n_nodes;
     p.keys = (unsigned long long *)workspace;
-    p.rows_done = (unsigned int *)((char *)workspace + round_up(rows * 8, 256));
-    p.seqs_done = (unsigned int *)((char *)workspace + round_up(rows * 8, 256) + round_up(rows * 4, 256));
+    p.seqs_done = (unsigned int *)((char *)workspace + round_up(rows * 8, 256));
     p.B = batch;
     p.N = n_nodes;
     p.V = vocab;

@@ -49,8 +49,7 @@ struct AcceptParams {
     const int32_t *parent;        // [B][N]
     int32_t *accept_len, *path, *tokens, *argmax;
     unsigned long long *keys;     // [B][N] packed (value, index) maxima  (zero between calls)
-    unsigned int *rows_done;      // [B][N] chunks done                  (zero between calls)
-    unsigned int *seqs_done;      // [B]    rows done                    (zero between calls)
+    unsigned int *seqs_done;      // [B]    (row, chunk) workgroups done (zero between calls)
     int B, N, V, chunk, n_chunks;
     int logits_f32;
 };
@@ -70,7 +69,7 @@ constexpr int kMaxSplits = 1024;               // splits per (sequence, KV head,
 
 // launchers (return the hipError_t of the launch) -------------------------
 hipError_t launch_attn_mfma(const AttnParams &p, int dtype, int D, int nt, int pg, hipStream_t s);
-hipError_t launch_attn_dma(const AttnParams &p, int D, int nt, int pg, hipStream_t s);
+hipError_t launch_attn_dma(const AttnParams &p, int D, int nt, int pg, bool q4, hipStream_t s);
 int attn_dma_max_split_pages();
 hipError_t launch_attn_valu(const AttnParams &p, int dtype, int D, hipStream_t s);
 hipError_t launch_attn_merge(const AttnParams &p, int D, hipStream_t s);

@@ -109,9 +109,9 @@ def test_attention_workspace_size(lib):
 
 def test_accept_checks_and_workspace(lib):
     n = lib.sv_greedy_accept_workspace_size(1, 8, 151936)
-    # one 64-bit key and one counter per row, one counter per sequence
-    assert n == 3 * 256
-    assert lib.sv_greedy_accept_workspace_size(8, 64, 151936) == 4096 + 2048 + 256
+    # one 64-bit key per row, one counter per sequence
+    assert n == 2 * 256
+    assert lib.sv_greedy_accept_workspace_size(8, 64, 151936) == 4096 + 256
     P = ctypes.c_void_p(FAKE)
 
     def call(B=1, N=8, V=151936, ld=1, ws=FAKE, wsb=1 << 30):

@@ -69,6 +69,8 @@ VARIANT_SHAPES = [
     ("fp32 tree D256 rows>16", 12, 2, 256, 8, "f32", "f32", False, 64, "ddtree"),
     ("bf16 q4 paged tree", 12, 2, 64, 9, "bf16", "q4", True, 100, "ddtree"),
     ("many row blocks", 32, 1, 128, 12, "bf16", "bf16", False, 40, "ddtree"),
+    ("q4 D256 paged tree", 12, 2, 256, 4, "bf16", "q4", True, 300, "ddtree"),
+    ("q4 D256 rows 96", 24, 4, 256, 16, "bf16", "q4", False, 333, "chain"),
 ]
 
 
