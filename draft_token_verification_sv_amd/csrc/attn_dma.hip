@@ -55,7 +55,7 @@ struct DCfg {
     static constexpr int KBYTES = Q4 ? T * CROWB : T * ROWB;   // K part of a stage
     static constexpr int STAGE = Q4 ? 2 * T * (CROWB + SROWB) : 2 * KBYTES;
     static constexpr int S_RAW = 131072 / STAGE;
-    static constexpr int S = Q4 ? 3 : (S_RAW < 2 ? 2 : (S_RAW > 8 ? 8 : S_RAW));   // ring depth
+    static constexpr int S = Q4 ? 2 : (S_RAW < 2 ? 2 : (S_RAW > 8 ? 8 : S_RAW));   // ring depth
     static constexpr int NKB = STAGE / 1024;          // 1 KB DMA instructions per stage
     static constexpr int LPW = NKB / 4;               // per wave
     static constexpr int RPK = 1024 / ROWB;           // rows per DMA instruction (bf16)
@@ -63,7 +63,7 @@ struct DCfg {
     static constexpr int KS = D / 32;
     static constexpr int DT = D / 16;
     static constexpr int CH = Q4 ? T / 32 : 1;        // 32-position chunks per stage, in turn
-    static constexpr int STAGING = Q4 ? 2 * 32 * ROWB : 0;   // dequantised K and V of one chunk
+    static constexpr int STAGING = Q4 ? 2 * 32 * ROWB : 0;   // dequantised K and V of one chunk (x2 buffers)
     static_assert(Q4 ? (NKB % 4 == 0) : (NKB % 8 == 0), "stage split evenly between waves (and K/V)");
     static_assert(!Q4 || (D == 256 && PG == 1), "4-bit stages: head dim 256, one position group");
     static_assert(LPW * (S - 2) < 64, "vmcnt range");
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
     using C = DCfg<D, NT, PG, Q4>;
     constexpr int T = C::T, S = C::S;
     __shared__ __attribute__((aligned(1024))) uint8_t ring[S * C::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t staging[Q4 ? C::STAGING : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t staging[Q4 ? 2 * C::STAGING : 16];
     __shared__ int par_s[64];
     __shared__ uint64_t anc_s[64];
     __shared__ int pages_s[PAGED ? kMaxSplitPages : 1];
@@ -307,9 +307,43 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
     // waits for those stages.
     wait_vm<0>();
 
+    // ---- 4-bit cache: the 256 threads turn chunk c of ring slot `slot` into
+    // bf16 rows in staging buffer `buf` (thread: one row, one 32-value block of
+    // K and of V; value = d * (code - 8) exactly in fp32, rounded to
+    // nearest-even bf16) --------------------------------------------------------
+    auto dequant = [&](int slot, int c, int buf) {
+        if constexpr (Q4) {
+            const uint8_t *stg = ring + slot * C::STAGE;
+            const int row = tid >> 3, blk = tid & 7;
+#pragma unroll
+            for (int which = 0; which < 2; ++which) {
+                const u32x4 w = *(const u32x4 *)(stg + which * C::T * C::CROWB + (c * 32 + row) * C::CROWB + blk * 16);
+                const float sc = fp16_bits_to_f32(*(const uint16_t *)(stg + 2 * C::T * C::CROWB +
+                                                                    which * C::T * C::SROWB +
+                                                                    (c * 32 + row) * C::SROWB + blk * 2));
+                const float off = -8.f * sc;
+                uint8_t *dst = staging + buf * C::STAGING + which * 32 * C::ROWB + row * C::ROWB;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    // byte t of the row holds values 2t (low nibble) and 2t + 1
+                    const uint32_t lo = w[m] & 0x0F0F0F0Fu, hi = (w[m] >> 4) & 0x0F0F0F0Fu;
+                    u32x4 out;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        out[k] = pack_bf16x2(__builtin_fmaf((float)((lo >> (8 * k)) & 0xFFu), sc, off),
+                                             __builtin_fmaf((float)((hi >> (8 * k)) & 0xFFu), sc, off));
+                    *(u32x4 *)(dst + ((4 * blk + m) ^ swz<C::W>(row)) * 16) = out;
+                }
+            }
+        }
+    };
+
     // ---- one 32-position chunk of K / V rows in LDS (natural order, 16-byte
     // chunks swizzled): scores, masks, online softmax, O^T += V^T P^T ----------
-    auto compute = [&](const uint8_t *Kl, const uint8_t *Vl, const int cb, const int abase) {
+    // (4-bit cache: the next chunk's dequantisation runs between this chunk's
+    // Q K^T matrix instructions)
+    auto compute = [&](const uint8_t *Kl, const uint8_t *Vl, const int cb, const int abase, int n_slot, int n_c,
+                       int n_buf) {
         // Every wave runs all NT tile slots: a slot without rows holds zero
         // queries, gives finite scores and is never written back, and no
         // branch breaks the stream of matrix instructions (the waves meet at
@@ -368,6 +402,10 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
                     kc[0] = kn[0];
                     kc[1] = kn[1];
                 }
+            }
+            if constexpr (Q4) {
+                dequant(n_slot, n_c, n_buf);
+
             }
         }
 
@@ -455,61 +493,46 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
         }
     };
 
-    // ---- 4-bit cache: the 256 threads turn chunk c of a stage into bf16 rows in
-    // `staging` (thread: one row, one 32-value block; value = d * (code - 8)
-    // exactly in fp32, rounded to nearest-even bf16) ---------------------------
-    auto dequant = [&](int slot, int c) {
-        if constexpr (Q4) {
-            const uint8_t *stg = ring + slot * C::STAGE;
-            const int row = tid >> 3, blk = tid & 7;
-#pragma unroll
-            for (int which = 0; which < 2; ++which) {
-                const u32x4 w = *(const u32x4 *)(stg + which * C::T * C::CROWB + (c * 32 + row) * C::CROWB + blk * 16);
-                const float sc = fp16_bits_to_f32(*(const uint16_t *)(stg + 2 * C::T * C::CROWB +
-                                                                    which * C::T * C::SROWB +
-                                                                    (c * 32 + row) * C::SROWB + blk * 2));
-                const float off = -8.f * sc;
-                uint8_t *dst = staging + which * 32 * C::ROWB + row * C::ROWB;
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    // byte t of the row holds values 2t (low nibble) and 2t + 1
-                    const uint32_t lo = w[m] & 0x0F0F0F0Fu, hi = (w[m] >> 4) & 0x0F0F0F0Fu;
-                    u32x4 out;
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        out[k] = pack_bf16x2(__builtin_fmaf((float)((lo >> (8 * k)) & 0xFFu), sc, off),
-                                             __builtin_fmaf((float)((hi >> (8 * k)) & 0xFFu), sc, off));
-                    *(u32x4 *)(dst + ((4 * blk + m) ^ swz<C::W>(row)) * 16) = out;
-                }
-            }
-        }
-    };
-
     // ---- main loop ---------------------------------------------------------
+    if constexpr (Q4) {
+        // chunks g = 0 .. G-1 of 32 positions, CH per stage.  Staging buffer
+        // g % 2 holds chunk g, dequantised during chunk g - 1; one barrier per
+        // chunk.  Stage st + 1 is loaded while stage st is consumed.
+        const int G = (p1 - p0 + 31) / 32;
+        __syncthreads();                                   // stage 0 (waited above) landed everywhere
+        dequant(0, 0, 0);
+        __syncthreads();
 #pragma unroll 1
-    for (int it = 0; it < n_st; ++it) {
-        wait_vm_dyn<C::LPW, S - 2>(min(S - 2, n_st - 1 - it));   // this wave's part of stage `it` landed
-        __syncthreads();                                           // everyone's part landed; slot it-1 free
-        if (it + S - 1 < n_st) issue(it + S - 1);
-
-        if constexpr (Q4) {
-#pragma unroll 1
-            for (int c = 0; c < C::CH; ++c) {
-                const int abase = p0 + it * T + c * 32;
-                if (abase >= p1) break;                            // uniform
-                if (c > 0) __syncthreads();                        // staging free again
-                dequant(it % S, c);
+        for (int g = 0; g < G; ++g) {
+            const int st = g / C::CH, c = g % C::CH;
+            if (c == 0 && st + 1 < n_st) issue(st + 1);    // slot of stage st - 1: fully dequantised
+            if (c == C::CH - 1 && st + 1 < n_st) {
+                wait_vm<0>();                              // stage st + 1, dequantised during this chunk
                 __syncthreads();
-                if (tile_on[0]) compute(staging, staging + 32 * C::ROWB, 0, abase);
             }
-        } else {
+            // the chunk after this one (past the end: this one again, into the idle buffer)
+            const int gn = g + 1 < G ? g + 1 : g;
+            const uint8_t *Kl = staging + (g & 1) * C::STAGING;
+            if (tile_on[0]) {
+                compute(Kl, Kl + 32 * C::ROWB, 0, p0 + g * 32, (gn / C::CH) % S, gn % C::CH, (g + 1) & 1);
+            } else {
+                dequant((gn / C::CH) % S, gn % C::CH, (g + 1) & 1);
+            }
+            __syncthreads();
+        }
+    } else {
+#pragma unroll 1
+        for (int it = 0; it < n_st; ++it) {
+            wait_vm_dyn<C::LPW, S - 2>(min(S - 2, n_st - 1 - it));   // this wave's part of stage `it` landed
+            __syncthreads();                                           // everyone's part landed; slot it-1 free
+            if (it + S - 1 < n_st) issue(it + S - 1);
             const uint8_t *Kl = ring + (it % S) * C::STAGE;
             const int cb = pg * 32;
             const int abase = p0 + it * T + cb;
             // a wavefront whose row group has no rows (fewer row tiles than
             // wavefronts) only issues its share of the loads
             if (abase >= p1 || !tile_on[0]) continue;
-            compute(Kl, Kl + C::KBYTES, cb, abase);
+            compute(Kl, Kl + C::KBYTES, cb, abase, 0, 0, 0);
         }
     }
 
