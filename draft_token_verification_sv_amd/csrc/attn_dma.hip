@@ -587,7 +587,10 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
         const int r = row0 + rl;
         float *op = p.part_o + (part * R + r) * D + qd * 4;
 #pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt) *(f32x4 *)(op + 16 * dt) = o[i][dt];
+        for (int dt = 0; dt < C::DT; ++dt) {
+            if (p.part_nt) __builtin_nontemporal_store(o[i][dt], (f32x4 *)(op + 16 * dt));
+            else *(f32x4 *)(op + 16 * dt) = o[i][dt];
+        }
         if (qd == 0) {
             p.part_ml[(part * R + r) * 2 + 0] = m_ref[i];
             p.part_ml[(part * R + r) * 2 + 1] = ls;

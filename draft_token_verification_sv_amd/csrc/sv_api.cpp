@@ -311,6 +311,10 @@ int sv_verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
     const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)D);
     p.scale_log2 = scale * 1.4426950408889634f;
     p.q_f32 = q_dtype == SV_F32;
+    // Small partial sets (a few MB) are written with streaming stores: less to
+    // write back from L2 when the split kernel ends, which the merge waits for.
+    // Large ones stay cached for the merge (measured: 6 MB -1 us, 34 MB +3 us).
+    p.part_nt = pl.ml_off <= ((size_t)8 << 20);
 
     hipStream_t st = (hipStream_t)stream;
     hipError_t e;

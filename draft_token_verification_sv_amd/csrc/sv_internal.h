@@ -41,6 +41,7 @@ struct AttnParams {
     int n_units;                  // units the grid covers (without row blocks)
     float scale_log2;             // sm_scale * log2(e)
     int q_f32;                    // 1: q/out are fp32, 0: bf16
+    int part_nt;                  // 1: streaming (non-temporal) stores for the partial O
 };
 
 struct AcceptParams {
