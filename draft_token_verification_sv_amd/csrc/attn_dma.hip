@@ -105,6 +105,14 @@ __device__ __forceinline__ void dma16(uint32_t lds_base, const void *gptr) {
                  : "memory", "m0");
 }
 
+// the same with a wave-uniform 64-bit base in SGPRs and a 32-bit lane offset
+__device__ __forceinline__ void dma16s(uint32_t lds_base, const void *sbase, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+
 constexpr int kMaxSplitPages = 512;
 
 template <int D, int NT, int PG, bool PAGED, bool Q4>
@@ -126,9 +134,11 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
     const int rb = k8 % p.n_rowblocks;
     AttnUnit wu;
     if (!attn_unit(p, (k8 / p.n_rowblocks) * 8 + xcd, rb == 0, sched_s, wu)) return;
-    const int b = wu.b, kvh = wu.kvh;
+    // the unit is the same for the whole block: keep it in scalar registers
+    const int b = __builtin_amdgcn_readfirstlane(wu.b), kvh = __builtin_amdgcn_readfirstlane(wu.kvh);
     const int N = p.N, G = p.G, R = p.R;
-    const int ctx = wu.ctx, p0 = wu.p0, p1 = wu.p1;
+    const int ctx = __builtin_amdgcn_readfirstlane(wu.ctx);
+    const int p0 = __builtin_amdgcn_readfirstlane(wu.p0), p1 = __builtin_amdgcn_readfirstlane(wu.p1);
     const int n_st = (p1 - p0 + T - 1) / T;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -162,13 +172,14 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
     const int64_t head_row0 = ((int64_t)b * p.Hkv + kvh) * p.kv.capacity;   // contiguous
     const uint32_t ring_u32 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)ring;
 
-    // Lane constants of DMA instruction j: row within the stage, byte offset of
-    // the lane's 16 bytes within that row, and (4-bit cache) the array it reads:
-    // a 4-bit stage is [K codes][V codes][K scales][V scales], rows in order.
-    // bf16 rows are swizzled in 16-byte chunks as they land.
-    int dma_row[C::LPW];
+    // Lane constants of DMA instruction j: the byte offset of the lane's 16
+    // bytes within the array's part of a stage (row * row bytes + column, rows
+    // in order) and (4-bit cache) the array it reads: a 4-bit stage is
+    // [K codes][V codes][K scales][V scales].  bf16 rows are swizzled in
+    // 16-byte chunks as they land: the lane fetches the chunk whose swizzled
+    // place is its own slot of the 1 KB the instruction writes.
     uint32_t dma_off[C::LPW];
-    int dma_arr[C::LPW];
+    int dma_arr[C::LPW];                    // wave-uniform
 #pragma unroll
     for (int j = 0; j < C::LPW; ++j) {
         const int kbi = wave * C::LPW + j;
@@ -176,70 +187,80 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
             constexpr int KCI = C::T * C::CROWB / 1024, KSI = C::T * C::SROWB / 1024;
             const int arr = kbi < KCI ? 0 : (kbi < 2 * KCI ? 1 : (kbi < 2 * KCI + KSI ? 2 : 3));
             const int start = arr == 0 ? 0 : (arr == 1 ? KCI : (arr == 2 ? 2 * KCI : 2 * KCI + KSI));
-            const int rb_ = arr < 2 ? C::CROWB : C::SROWB;
             dma_arr[j] = arr;
-            dma_row[j] = ((kbi - start) * 1024 + lane * 16) / rb_;
-            dma_off[j] = (uint32_t)((lane * 16) % rb_);
+            dma_off[j] = (uint32_t)((kbi - start) * 1024 + lane * 16);
         } else {
             const int kb_in = kbi >= C::NKB / 2 ? kbi - C::NKB / 2 : kbi;
             const int row = kb_in * C::RPK + (lane * 16) / C::ROWB;
             const int chunk = ((lane * 16) % C::ROWB / 16) ^ swz<C::W>(row);
             dma_arr[j] = kbi >= C::NKB / 2;
-            dma_row[j] = row;
             dma_off[j] = (uint32_t)(row * C::ROWB + chunk * 16);
         }
     }
 
+    // Stage st = positions tb .. tb + T - 1 of the split; rows past the
+    // split's end (last stage) repeat its last row.  Contiguous cache: one
+    // uniform base per array and stage, lane offsets fixed for full stages.
     auto issue = [&](int st) {
         const int tb = p0 + st * T;
         const uint32_t slot = ring_u32 + (uint32_t)((st % S) * C::STAGE);
-        const bool full = tb + T <= p1;                          // uniform
-#pragma unroll
-        for (int j = 0; j < C::LPW; ++j) {
-            const int kbi = wave * C::LPW + j;                     // wave-uniform
-            const uint8_t *g;
+        // the array, its log2 row bytes and the LDS destination of instruction j
+        auto arr_of = [&](int j, const uint8_t *&gb, int &rsh, uint32_t &lds) {
+            const int arr = dma_arr[j];
             if constexpr (Q4) {
-                const int arr = dma_arr[j];
-                const uint8_t *gb = arr == 0 ? kbase : (arr == 1 ? vbase : (arr == 2 ? ksbase : vsbase));
-                const int rb_ = arr < 2 ? C::CROWB : C::SROWB;
-                const int pos = full ? tb + dma_row[j] : min(tb + dma_row[j], p1 - 1);
-                int64_t ri;
-                if constexpr (!PAGED) {
-                    ri = head_row0 + pos;
-                } else {
-                    const int ps = p.kv.page_size;
-                    const int pq = ps_shift >= 0 ? pos >> ps_shift : pos / ps;
-                    const int pr = pos - pq * ps;
-                    ri = ((int64_t)pages_s[pq - first_page] * p.Hkv + kvh) * ps + pr;
-                }
-                g = gb + ri * rb_ + dma_off[j];
+                gb = arr == 0 ? kbase : (arr == 1 ? vbase : (arr == 2 ? ksbase : vsbase));
+                rsh = arr < 2 ? __builtin_ctz(C::CROWB) : __builtin_ctz(C::SROWB);
             } else {
-                const bool is_v = dma_arr[j] != 0;
-                if constexpr (!PAGED) {
-                    if (full) {
-                        g = (is_v ? vbase : kbase) + (head_row0 + tb) * C::ROWB + dma_off[j];
-                    } else {
-                        const int pos = min(tb + dma_row[j], p1 - 1);
-                        g = (is_v ? vbase : kbase) + (head_row0 + pos) * C::ROWB +
-                            (dma_off[j] - (uint32_t)(dma_row[j] * C::ROWB));
-                    }
-                } else {
-                    const int ps = p.kv.page_size;
-                    const int pos = min(tb + dma_row[j], p1 - 1);
-                    int pq, pr;
-                    if (ps_shift >= 0) {
-                        pq = pos >> ps_shift;
-                        pr = pos & (ps - 1);
-                    } else {
-                        pq = pos / ps;
-                        pr = pos - pq * ps;
-                    }
-                    const int pgid = pages_s[pq - first_page];
-                    const int64_t ri = ((int64_t)pgid * p.Hkv + kvh) * ps + pr;
-                    g = (is_v ? vbase : kbase) + ri * C::ROWB + (dma_off[j] - (uint32_t)(dma_row[j] * C::ROWB));
+                gb = arr != 0 ? vbase : kbase;
+                rsh = __builtin_ctz(C::ROWB);
+            }
+            lds = __builtin_amdgcn_readfirstlane(slot + (uint32_t)((wave * C::LPW + j) * 1024));
+        };
+        if constexpr (!PAGED) {
+            if (tb + T <= p1) {                                  // full stage (uniform)
+#pragma unroll
+                for (int j = 0; j < C::LPW; ++j) {
+                    const uint8_t *gb;
+                    int rsh;
+                    uint32_t lds;
+                    arr_of(j, gb, rsh, lds);
+                    dma16s(lds, gb + ((head_row0 + tb) << rsh), dma_off[j]);
+                }
+            } else {
+                const int lim = p1 - 1 - tb;                     // last row of the split in this stage
+#pragma unroll
+                for (int j = 0; j < C::LPW; ++j) {
+                    const uint8_t *gb;
+                    int rsh;
+                    uint32_t lds;
+                    arr_of(j, gb, rsh, lds);
+                    const int row = (int)(dma_off[j] >> rsh);
+                    const uint32_t col = dma_off[j] & ((1u << rsh) - 1u);
+                    dma16s(lds, gb + ((head_row0 + tb) << rsh), ((uint32_t)min(row, lim) << rsh) | col);
                 }
             }
-            dma16(__builtin_amdgcn_readfirstlane(slot + (uint32_t)(kbi * 1024)), g);
+        } else {
+#pragma unroll
+            for (int j = 0; j < C::LPW; ++j) {
+                const uint8_t *gb;
+                int rsh;
+                uint32_t lds;
+                arr_of(j, gb, rsh, lds);
+                const int row = (int)(dma_off[j] >> rsh);
+                const uint32_t col = dma_off[j] & ((1u << rsh) - 1u);
+                const int ps = p.kv.page_size;
+                const int pos = min(tb + row, p1 - 1);
+                int pq, pr;
+                if (ps_shift >= 0) {
+                    pq = pos >> ps_shift;
+                    pr = pos & (ps - 1);
+                } else {
+                    pq = pos / ps;
+                    pr = pos - pq * ps;
+                }
+                const int64_t ri = ((int64_t)pages_s[pq - first_page] * p.Hkv + kvh) * ps + pr;
+                dma16(lds, gb + (ri << rsh) + col);
+            }
         }
     };
 

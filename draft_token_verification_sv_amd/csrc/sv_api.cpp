@@ -159,6 +159,12 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
             pl.n_rowblocks = (RT + tpb - 1) / tpb;
             pl.rows_per_block = tpb * 16;
             pl.nt = (tpb + 3) / 4;
+            // a block of one or two row tiles leaves wavefronts without rows:
+            // they take other positions of a longer stage instead (bf16 cache)
+            if (pl.kind == kMfmaDma && !q4 && pl.nt == 1 && g_attn_posgroups > 0) {
+                const int pg_rows = tpb == 1 ? 4 : (tpb == 2 ? 2 : 1);
+                pl.pg = std::min(std::min(g_attn_posgroups, pg_rows), std::min(4, 65536 / (128 * D)));
+            }
             splits_for(B * Hkv * pl.n_rowblocks, pl.split_len, pl.n_splits);
         }
     } else {
