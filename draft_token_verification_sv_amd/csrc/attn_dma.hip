@@ -63,6 +63,10 @@ struct DCfg {
     static constexpr int KS = D / 32;
     static constexpr int DT = D / 16;
     static constexpr int CH = Q4 ? T / 32 : 1;        // 32-position chunks per stage, in turn
+    // bf16, several row tiles per wave, one DMA instruction per k-step: a full
+    // stage's loads go out between the k-steps of the chunk before (with one
+    // tile the chunk is short and the branch costs more than it saves)
+    static constexpr bool SPREAD = !Q4 && LPW <= KS && NT >= 2;
     static constexpr int STAGING = Q4 ? 2 * 32 * ROWB : 0;   // dequantised K and V of one chunk (x2 buffers)
     static_assert(Q4 ? (NKB % 4 == 0) : (NKB % 8 == 0), "stage split evenly between waves (and K/V)");
     static_assert(!Q4 || (D == 256 && PG == 1), "4-bit stages: head dim 256, one position group");
@@ -105,11 +109,17 @@ __device__ __forceinline__ void dma16(uint32_t lds_base, const void *gptr) {
                  : "memory", "m0");
 }
 
-// the same with a wave-uniform 64-bit base in SGPRs and a 32-bit lane offset
+// the same with a wave-uniform 64-bit base (scalar registers) and a 32-bit
+// lane offset
 __device__ __forceinline__ void dma16s(uint32_t lds_base, const void *sbase, uint32_t voff) {
+    // (the builtin returns int: widen each half as unsigned, never sign-extend)
+    const uint64_t a = (uint64_t)(uintptr_t)sbase;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint64_t u = ((uint64_t)hi << 32) | (uint64_t)lo;
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
-                 : "s"(lds_base), "v"(voff), "s"(sbase)
+                 : "s"(lds_base), "v"(voff), "s"(u)
                  : "memory", "m0");
 }
 
@@ -180,6 +190,15 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
     // place is its own slot of the 1 KB the instruction writes.
     uint32_t dma_off[C::LPW];
     int dma_arr[C::LPW];                    // wave-uniform
+    // the array's base and log2 row bytes (wave-uniform; a bf16 wave reads
+    // one array only: waves 0-1 K, waves 2-3 V)
+    const uint8_t *dma_gb[Q4 ? C::LPW : 1];
+    int dma_rsh[Q4 ? C::LPW : 1];
+    static_assert(Q4 || (2 * C::LPW) % (C::NKB / 2) == 0 || C::NKB / 2 % C::LPW == 0, "one array per bf16 wave");
+    if constexpr (!Q4) {
+        dma_gb[0] = wave * C::LPW >= C::NKB / 2 ? vbase : kbase;
+        dma_rsh[0] = __builtin_ctz(C::ROWB);
+    }
 #pragma unroll
     for (int j = 0; j < C::LPW; ++j) {
         const int kbi = wave * C::LPW + j;
@@ -189,6 +208,8 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
             const int start = arr == 0 ? 0 : (arr == 1 ? KCI : (arr == 2 ? 2 * KCI : 2 * KCI + KSI));
             dma_arr[j] = arr;
             dma_off[j] = (uint32_t)((kbi - start) * 1024 + lane * 16);
+            dma_gb[j] = arr == 0 ? kbase : (arr == 1 ? vbase : (arr == 2 ? ksbase : vsbase));
+            dma_rsh[j] = arr < 2 ? __builtin_ctz(C::CROWB) : __builtin_ctz(C::SROWB);
         } else {
             const int kb_in = kbi >= C::NKB / 2 ? kbi - C::NKB / 2 : kbi;
             const int row = kb_in * C::RPK + (lane * 16) / C::ROWB;
@@ -201,54 +222,40 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
     // Stage st = positions tb .. tb + T - 1 of the split; rows past the
     // split's end (last stage) repeat its last row.  Contiguous cache: one
     // uniform base per array and stage, lane offsets fixed for full stages.
+    // This wave's DMA instructions for stage st: contiguous cache, a uniform
+    // base per array and a lane offset (rows past the split's end, last stage
+    // only, repeat its last row); paged cache, the lane addresses.
     auto issue = [&](int st) {
         const int tb = p0 + st * T;
-        const uint32_t slot = ring_u32 + (uint32_t)((st % S) * C::STAGE);
-        // the array, its log2 row bytes and the LDS destination of instruction j
-        auto arr_of = [&](int j, const uint8_t *&gb, int &rsh, uint32_t &lds) {
-            const int arr = dma_arr[j];
-            if constexpr (Q4) {
-                gb = arr == 0 ? kbase : (arr == 1 ? vbase : (arr == 2 ? ksbase : vsbase));
-                rsh = arr < 2 ? __builtin_ctz(C::CROWB) : __builtin_ctz(C::SROWB);
-            } else {
-                gb = arr != 0 ? vbase : kbase;
-                rsh = __builtin_ctz(C::ROWB);
-            }
-            lds = __builtin_amdgcn_readfirstlane(slot + (uint32_t)((wave * C::LPW + j) * 1024));
-        };
+        const uint32_t slot = ring_u32 + (uint32_t)((st % S) * C::STAGE + wave * C::LPW * 1024);
         if constexpr (!PAGED) {
             if (tb + T <= p1) {                                  // full stage (uniform)
 #pragma unroll
                 for (int j = 0; j < C::LPW; ++j) {
-                    const uint8_t *gb;
-                    int rsh;
-                    uint32_t lds;
-                    arr_of(j, gb, rsh, lds);
-                    dma16s(lds, gb + ((head_row0 + tb) << rsh), dma_off[j]);
+                    const int jj = Q4 ? j : 0;
+                    dma16s(__builtin_amdgcn_readfirstlane(slot + (uint32_t)(j * 1024)),
+                           dma_gb[jj] + ((head_row0 + tb) << dma_rsh[jj]), dma_off[j]);
                 }
             } else {
                 const int lim = p1 - 1 - tb;                     // last row of the split in this stage
 #pragma unroll
                 for (int j = 0; j < C::LPW; ++j) {
-                    const uint8_t *gb;
-                    int rsh;
-                    uint32_t lds;
-                    arr_of(j, gb, rsh, lds);
+                    const int jj = Q4 ? j : 0;
+                    const int rsh = dma_rsh[jj];
                     const int row = (int)(dma_off[j] >> rsh);
                     const uint32_t col = dma_off[j] & ((1u << rsh) - 1u);
-                    dma16s(lds, gb + ((head_row0 + tb) << rsh), ((uint32_t)min(row, lim) << rsh) | col);
+                    dma16s(__builtin_amdgcn_readfirstlane(slot + (uint32_t)(j * 1024)),
+                           dma_gb[jj] + ((head_row0 + tb) << rsh), ((uint32_t)min(row, lim) << rsh) | col);
                 }
             }
         } else {
+            const int ps = p.kv.page_size;
 #pragma unroll
             for (int j = 0; j < C::LPW; ++j) {
-                const uint8_t *gb;
-                int rsh;
-                uint32_t lds;
-                arr_of(j, gb, rsh, lds);
+                const int jj = Q4 ? j : 0;
+                const int rsh = dma_rsh[jj];
                 const int row = (int)(dma_off[j] >> rsh);
                 const uint32_t col = dma_off[j] & ((1u << rsh) - 1u);
-                const int ps = p.kv.page_size;
                 const int pos = min(tb + row, p1 - 1);
                 int pq, pr;
                 if (ps_shift >= 0) {
@@ -259,9 +266,15 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
                     pr = pos - pq * ps;
                 }
                 const int64_t ri = ((int64_t)pages_s[pq - first_page] * p.Hkv + kvh) * ps + pr;
-                dma16(lds, gb + (ri << rsh) + col);
+                dma16(__builtin_amdgcn_readfirstlane(slot + (uint32_t)(j * 1024)), dma_gb[jj] + (ri << rsh) + col);
             }
         }
+    };
+    // instruction j of full stage st of a contiguous cache
+    auto issue_full = [&](int st, int j) {
+        const int jj = Q4 ? j : 0;
+        dma16s(__builtin_amdgcn_readfirstlane(ring_u32 + (uint32_t)((st % S) * C::STAGE + (wave * C::LPW + j) * 1024)),
+               dma_gb[jj] + ((head_row0 + p0 + st * T) << dma_rsh[jj]), dma_off[j]);
     };
 
     // ---- pipeline prologue: the first stages go out before the query loads, so
@@ -363,8 +376,11 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
     // chunks swizzled): scores, masks, online softmax, O^T += V^T P^T ----------
     // (4-bit cache: the next chunk's dequantisation runs between this chunk's
     // Q K^T matrix instructions)
-    auto compute = [&](const uint8_t *Kl, const uint8_t *Vl, const int cb, const int abase, int n_slot, int n_c,
-                       int n_buf) {
+    // ist >= 0: this wave's DMA instructions of full stage ist (contiguous
+    // cache) go out between the k-steps (a wave that sends a whole stage at
+    // once stalls until the memory pipeline has taken them all)
+    auto compute = [&](const int ist, const uint8_t *Kl, const uint8_t *Vl, const int cb, const int abase,
+                       int n_slot, int n_c, int n_buf) {
         // Every wave runs all NT tile slots: a slot without rows holds zero
         // queries, gives finite scores and is never written back, and no
         // branch breaks the stream of matrix instructions (the waves meet at
@@ -409,6 +425,9 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
                 if (k + 1 < C::KS) {
                     kn[0] = kread(0, k + 1);
                     kn[1] = kread(1, k + 1);
+                }
+                if constexpr (C::SPREAD && !PAGED) {
+                    if (ist >= 0 && k < C::LPW) issue_full(ist, k);
                 }
 #pragma unroll
                 for (int v = 0; v < VPK; ++v)
@@ -535,7 +554,7 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
             const int gn = g + 1 < G ? g + 1 : g;
             const uint8_t *Kl = staging + (g & 1) * C::STAGING;
             if (tile_on[0]) {
-                compute(Kl, Kl + 32 * C::ROWB, 0, p0 + g * 32, (gn / C::CH) % S, gn % C::CH, (g + 1) & 1);
+                compute(-1, Kl, Kl + 32 * C::ROWB, 0, p0 + g * 32, (gn / C::CH) % S, gn % C::CH, (g + 1) & 1);
             } else {
                 dequant((gn / C::CH) % S, gn % C::CH, (g + 1) & 1);
             }
@@ -546,14 +565,21 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
         for (int it = 0; it < n_st; ++it) {
             wait_vm_dyn<C::LPW, S - 2>(min(S - 2, n_st - 1 - it));   // this wave's part of stage `it` landed
             __syncthreads();                                           // everyone's part landed; slot it-1 free
-            if (it + S - 1 < n_st) issue(it + S - 1);
+            const int ist = it + S - 1 < n_st ? it + S - 1 : -1;   // stage to load into slot it-1
             const uint8_t *Kl = ring + (it % S) * C::STAGE;
             const int cb = pg * 32;
             const int abase = p0 + it * T + cb;
             // a wavefront whose row group has no rows (fewer row tiles than
             // wavefronts) only issues its share of the loads
-            if (abase >= p1 || !tile_on[0]) continue;
-            compute(Kl, Kl + C::KBYTES, cb, abase, 0, 0, 0);
+            if (abase >= p1 || !tile_on[0]) {
+                if (ist >= 0) issue(ist);
+                continue;
+            }
+            // a full stage of a contiguous cache goes out over the k-steps;
+            // the last stage and paged caches at once
+            const bool spread = C::SPREAD && !PAGED && ist >= 0 && p0 + ist * T + T <= p1;
+            if (ist >= 0 && !spread) issue(ist);
+            compute(spread ? ist : -1, Kl, Kl + C::KBYTES, cb, abase, 0, 0, 0);
         }
     }
 
