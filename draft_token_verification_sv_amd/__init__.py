@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "SV_F32", "SV_BF16", "SV_Q4", "SVError", "KVCache", "lib", "library_path",
     "verify_attn", "verify_attn_workspace_size", "greedy_accept", "greedy_accept_workspace_size",
-    "kv_compact", "set_option", "SV_OPT_ATTN_TARGET_WGS", "SV_OPT_ARGMAX_CHUNK", "SV_OPT_ATTN_ROWBLOCKS",
+    "kv_compact", "greedy_accept_compact", "set_option", "SV_OPT_ATTN_TARGET_WGS", "SV_OPT_ARGMAX_CHUNK", "SV_OPT_ATTN_ROWBLOCKS",
     "SV_OPT_ATTN_POSGROUPS",
 ]
 
@@ -69,6 +69,9 @@ lib.sv_greedy_accept.restype = _I
 lib.sv_greedy_accept.argtypes = [_I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
 lib.sv_kv_compact.restype = _I
 lib.sv_kv_compact.argtypes = [ctypes.POINTER(_KvDesc), _I, _I, _I, _P, _I, _P, _P, _P, _P]
+lib.sv_greedy_accept_compact.restype = _I
+lib.sv_greedy_accept_compact.argtypes = [_I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P,
+                                         ctypes.POINTER(_KvDesc), _I, _P, _I, _P, _P, ctypes.c_size_t, _P]
 lib.sv_error_string.restype = ctypes.c_char_p
 lib.sv_error_string.argtypes = [_I]
 lib.sv_last_hip_error.restype = _I
@@ -285,6 +288,43 @@ def kv_compact(kv: KVCache, ctx_lens: torch.Tensor, max_ctx: int, path: torch.Te
                            _ptr(accept_len), _ptr(new_lens), _stream(path.device))
     _check(rc, "sv_kv_compact")
     return new_lens
+
+
+def greedy_accept_compact(logits: torch.Tensor, draft_ids: torch.Tensor, parent: torch.Tensor, kv: KVCache,
+                          ctx_lens: torch.Tensor, max_ctx: int, want_argmax: bool = True,
+                          workspace: Optional[torch.Tensor] = None, outputs=None, n_layers: Optional[int] = None,
+                          new_lens: Optional[torch.Tensor] = None):
+    """``greedy_accept`` then ``kv_compact`` in one launch.
+
+    Returns ``(accept_len, path, tokens, argmax or None, new_lens)``.
+    """
+    if logits.dim() != 3 or not logits.is_contiguous() or not logits.is_cuda:
+        raise ValueError("logits must be a contiguous [B, N, V] device tensor")
+    B, N, V = logits.shape
+    _i32(draft_ids, "draft_ids")
+    _i32(parent, "parent")
+    _i32(ctx_lens, "ctx_lens")
+    dev = logits.device
+    if outputs is None:
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        path = torch.empty((B, N), dtype=torch.int32, device=dev)
+        tok = torch.empty((B, N), dtype=torch.int32, device=dev)
+        am = torch.empty((B, N), dtype=torch.int32, device=dev) if want_argmax else None
+    else:
+        acc, path, tok, am = outputs
+    if new_lens is None:
+        new_lens = torch.empty(B, dtype=torch.int32, device=dev)
+    need = int(lib.sv_greedy_accept_workspace_size(B, N, V))
+    if workspace is None:
+        workspace = _workspace("accept", dev, need, zero=True)
+    d = kv.desc(0)
+    L = kv.n_layers if n_layers is None else n_layers
+    rc = lib.sv_greedy_accept_compact(B, N, V, _ptr(logits), _dtype_code(logits), _ptr(draft_ids), _ptr(parent),
+                                      _ptr(acc), _ptr(path), _ptr(tok), _ptr(am), ctypes.byref(d), L,
+                                      _ptr(ctx_lens), int(max_ctx), _ptr(new_lens), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(rc, "sv_greedy_accept_compact")
+    return acc, path, tok, am, new_lens
 
 
 def set_option(option: int, value: int) -> int:

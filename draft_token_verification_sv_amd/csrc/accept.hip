@@ -21,6 +21,10 @@
 // Each step is issued only after the previous atomic has returned, and all of
 // them act on the device-coherent copy, so the last workgroup sees every
 // key.  Every call leaves the keys and counters it used at zero.
+//
+// Fused form (acceptance + compaction): the last workgroup of sequence b then
+// moves the accepted rows' KV itself with all of its threads, so the sequence
+// needs no second launch (the standalone compaction kernel is compact.hip).
 #include "device_common.h"
 
 namespace sv {
@@ -64,11 +68,70 @@ __device__ __forceinline__ unsigned long long wave_max64(unsigned long long k) {
 // included, their results returned) has completed
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <bool F32, bool VEC>
+constexpr int kCompactLds = 32768;      // staging bytes of the fused compaction
+
+// In-place compaction of sequence b by one workgroup of 256 threads: for
+// every layer, KV head and K|V, row ctx + j <- row ctx + path[j] for the
+// accepted nodes j in [1, a] with path[j] > j (the others stay).  Copies go in
+// rounds that fill the staging buffer, each round reading all of its rows
+// before writing any; rounds take the moving rows in increasing j, and since
+// path[j] >= j a round's sources are never an earlier round's destinations.
+// path_s / mov_s live in LDS; mov_s[0 .. n_mov) lists the moving j in order.
+__device__ void compact_sequence(const CompactParams &cp, int b, int ctx, const int *path_s, const int *mov_s,
+                                 int n_mov, uint8_t *stage) {
+    if (n_mov == 0) return;
+    const int tid = threadIdx.x;
+    const int D = cp.D;
+    const bool q4 = cp.dtype == SV_Q4;
+    const int row_bytes = cp.dtype == SV_F32 ? D * 4 : (cp.dtype == SV_BF16 ? D * 2 : D / 2);
+    const int srow_bytes = q4 ? (D / 32) * 2 : 0;
+    const int vpieces = row_bytes / 16;                  // 16-byte pieces of a value row
+    const int pieces = vpieces + srow_bytes / 4;         // + 4-byte pieces of its scale row
+    const int unit_bytes = row_bytes + 16;               // staging room per (row, layer, head, K|V)
+    const int per_row = cp.n_layers * cp.Hkv * 2;
+    const int total = n_mov * per_row;
+    const int cap = kCompactLds / unit_bytes;
+    for (int u0 = 0; u0 < total; u0 += cap) {
+        const int nu = min(cap, total - u0);
+        for (int pass = 0; pass < 2; ++pass) {           // 0: sources -> LDS, 1: LDS -> destinations
+            for (int e = tid; e < nu * pieces; e += 256) {
+                const int ul = e / pieces, pc = e - ul * pieces;
+                const int u = u0 + ul;
+                const int m = u / per_row;
+                int r = u - m * per_row;
+                const int which = r & 1;
+                r >>= 1;
+                const int h = r % cp.Hkv, layer = r / cp.Hkv;
+                const int j = mov_s[m];
+                const int64_t ri = kv_row_index(cp.kv, b, cp.Hkv, h, ctx + (pass == 0 ? path_s[j] : j));
+                if (ri < 0) continue;
+                uint8_t *lds = stage + ul * unit_bytes;
+                if (pc < vpieces) {
+                    uint8_t *g = (uint8_t *)(which ? cp.kv.v : cp.kv.k) + (int64_t)layer * cp.layer_stride +
+                                 ri * row_bytes + pc * 16;
+                    if (pass == 0) *(u32x4 *)(lds + pc * 16) = *(const u32x4 *)g;
+                    else *(u32x4 *)g = *(const u32x4 *)(lds + pc * 16);
+                } else {
+                    const int w = pc - vpieces;
+                    uint8_t *g = (uint8_t *)(which ? cp.kv.vs : cp.kv.ks) + (int64_t)layer * cp.scale_layer_stride +
+                                 ri * srow_bytes + w * 4;
+                    if (pass == 0) *(uint32_t *)(lds + row_bytes + w * 4) = *(const uint32_t *)g;
+                    else *(uint32_t *)g = *(const uint32_t *)(lds + row_bytes + w * 4);
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+template <bool F32, bool VEC, bool COMPACT>
 __global__ __launch_bounds__(256) void argmax_accept_kernel(AcceptParams p) {
     __shared__ unsigned long long red[4];
     __shared__ int last_s;
     __shared__ int am_s[64], dr_s[64], par_s[64];
+    __shared__ int path_s[COMPACT ? 64 : 1], mov_s[COMPACT ? 64 : 1];
+    __shared__ int cinfo_s[2];                             // ctx, moving rows
+    __shared__ __attribute__((aligned(16))) uint8_t stage_s[COMPACT ? kCompactLds : 16];
 
     const int c = blockIdx.x % p.n_chunks;
     const int row = blockIdx.x / p.n_chunks;             // b * N + i
@@ -146,8 +209,17 @@ __global__ __launch_bounds__(256) void argmax_accept_kernel(AcceptParams p) {
     // ---- the last arrival of sequence b: take keys, then walk -----------------
     const int N = p.N;
     const int wave = tid >> 6, lane = tid & 63;
-    if (wave != 0) return;
+    if constexpr (!COMPACT) {
+        if (wave != 0) return;
+    } else if (wave != 0) {
+        __syncthreads();                                   // the walk's path in LDS
+        compact_sequence(p.cp, b, cinfo_s[0], path_s, mov_s, cinfo_s[1], stage_s);
+        return;
+    }
     if (lane == 0) __hip_atomic_store(&p.seqs_done[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (COMPACT) {
+        if (lane == 0) cinfo_s[0] = clamp_ctx(p.cp.ctx_lens[b], p.cp.max_ctx);
+    }
     if (lane < N) {
         const unsigned long long k =
             __hip_atomic_exchange(&p.keys[(int64_t)b * N + lane], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -185,6 +257,7 @@ __global__ __launch_bounds__(256) void argmax_accept_kernel(AcceptParams p) {
         int j = best_node;
         for (int d = a; d >= 0; --d) {
             path[d] = j;
+            if constexpr (COMPACT) path_s[d] = j;
             if (d > 0) tok[d - 1] = dr_s[j];
             j = (j > 0) ? par_s[j] : 0;
         }
@@ -196,6 +269,20 @@ __global__ __launch_bounds__(256) void argmax_accept_kernel(AcceptParams p) {
         tok[lane] = -1;
     }
     if (p.argmax != nullptr && lane < N) p.argmax[(int64_t)b * N + lane] = am_s[lane];
+    if constexpr (COMPACT) {
+        // the moving rows j in [1, a] (path[j] > j), in increasing order
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+        const bool mv = lane >= 1 && lane <= a && path_s[lane] > lane;
+        const uint64_t bal = __ballot(mv);
+        if (mv) mov_s[__popcll(bal & ((1ull << lane) - 1ull))] = lane;
+        if (lane == 0) {
+            cinfo_s[1] = __popcll(bal);
+            if (p.cp.new_lens != nullptr) p.cp.new_lens[b] = cinfo_s[0] + a + 1;
+        }
+        __syncthreads();
+        compact_sequence(p.cp, b, cinfo_s[0], path_s, mov_s, cinfo_s[1], stage_s);
+    }
 }
 
 }  // namespace
@@ -205,12 +292,22 @@ hipError_t launch_accept(const AcceptParams &p, hipStream_t st) {
     const int esize = p.logits_f32 ? 4 : 2;
     const bool vec = ((uintptr_t)p.logits % 16 == 0) && (((int64_t)p.V * esize) % 16 == 0) &&
                      ((int64_t)p.chunk * esize) % 16 == 0;
+    if (p.compact) {
+        if (p.logits_f32) {
+            if (vec) hipLaunchKernelGGL((argmax_accept_kernel<true, true, true>), dim3(grid), dim3(256), 0, st, p);
+            else hipLaunchKernelGGL((argmax_accept_kernel<true, false, true>), dim3(grid), dim3(256), 0, st, p);
+        } else {
+            if (vec) hipLaunchKernelGGL((argmax_accept_kernel<false, true, true>), dim3(grid), dim3(256), 0, st, p);
+            else hipLaunchKernelGGL((argmax_accept_kernel<false, false, true>), dim3(grid), dim3(256), 0, st, p);
+        }
+        return hipGetLastError();
+    }
     if (p.logits_f32) {
-        if (vec) hipLaunchKernelGGL((argmax_accept_kernel<true, true>), dim3(grid), dim3(256), 0, st, p);
-        else hipLaunchKernelGGL((argmax_accept_kernel<true, false>), dim3(grid), dim3(256), 0, st, p);
+        if (vec) hipLaunchKernelGGL((argmax_accept_kernel<true, true, false>), dim3(grid), dim3(256), 0, st, p);
+        else hipLaunchKernelGGL((argmax_accept_kernel<true, false, false>), dim3(grid), dim3(256), 0, st, p);
     } else {
-        if (vec) hipLaunchKernelGGL((argmax_accept_kernel<false, true>), dim3(grid), dim3(256), 0, st, p);
-        else hipLaunchKernelGGL((argmax_accept_kernel<false, false>), dim3(grid), dim3(256), 0, st, p);
+        if (vec) hipLaunchKernelGGL((argmax_accept_kernel<false, true, false>), dim3(grid), dim3(256), 0, st, p);
+        else hipLaunchKernelGGL((argmax_accept_kernel<false, false, false>), dim3(grid), dim3(256), 0, st, p);
     }
     return hipGetLastError();
 }

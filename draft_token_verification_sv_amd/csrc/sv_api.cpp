@@ -339,11 +339,14 @@ size_t sv_greedy_accept_workspace_size(int batch, int n_nodes, int vocab) {
     return (size_t)(round_up(rows * 8, 256) + round_up((int64_t)batch * 4, 256));
 }
 
-int sv_greedy_accept(int batch, int n_nodes, int vocab,
-                     const void *logits, int logits_dtype,
-                     const int32_t *draft_ids, const int32_t *parent,
-                     int32_t *accept_len, int32_t *path, int32_t *tokens, int32_t *argmax,
-                     void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// argument checks and parameters of an acceptance launch
+int accept_params(int batch, int n_nodes, int vocab, const void *logits, int logits_dtype,
+                  const int32_t *draft_ids, const int32_t *parent, int32_t *accept_len, int32_t *path,
+                  int32_t *tokens, int32_t *argmax, void *workspace, size_t workspace_bytes, AcceptParams &p) {
     if (batch < 1 || n_nodes < 1 || n_nodes > 64 || vocab < 1) return SV_EINVAL;
     if (logits == nullptr || draft_ids == nullptr || parent == nullptr || accept_len == nullptr ||
         path == nullptr || tokens == nullptr)
@@ -354,7 +357,7 @@ int sv_greedy_accept(int batch, int n_nodes, int vocab,
     const size_t need = sv_greedy_accept_workspace_size(batch, n_nodes, vocab);
     if (workspace == nullptr || workspace_bytes < need) return SV_EWORKSPACE;
     if (!aligned(workspace, 16)) return SV_EINVAL;
-    AcceptParams p{};
+    p = AcceptParams{};
     p.logits = logits;
     p.draft = draft_ids;
     p.parent = parent;
@@ -371,26 +374,25 @@ int sv_greedy_accept(int batch, int n_nodes, int vocab,
     p.chunk = g_argmax_chunk;
     p.n_chunks = (int)chunks;
     p.logits_f32 = logits_dtype == SV_F32;
-    const hipError_t e = launch_accept(p, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(e);
     return SV_OK;
 }
 
-int sv_kv_compact(const sv_kv_cache *kv, int n_layers, int batch, int n_nodes,
-                  const int32_t *ctx_lens, int max_ctx,
-                  const int32_t *path, const int32_t *accept_len,
-                  int32_t *new_lens, void *stream) {
+// argument checks and parameters of a compaction (path / accept_len may be
+// null when the fused call produces them)
+int compact_params(const sv_kv_cache *kv, int n_layers, int batch, int n_nodes, const int32_t *ctx_lens,
+                   int max_ctx, const int32_t *path, const int32_t *accept_len, int32_t *new_lens, bool fused,
+                   CompactParams &p) {
     if (n_layers < 1 || batch < 1 || n_nodes < 1 || n_nodes > 64 || max_ctx < 0) return SV_EINVAL;
     if (max_ctx > (1 << 30)) return SV_EINVAL;
     const int rc = check_kv(kv, batch, n_nodes, max_ctx);
     if (rc != SV_OK) return rc;
-    if (ctx_lens == nullptr || path == nullptr || accept_len == nullptr) return SV_EINVAL;
+    if (ctx_lens == nullptr || (!fused && (path == nullptr || accept_len == nullptr))) return SV_EINVAL;
     if (n_layers > 1 && (kv->layer_stride == 0 ||
                          (kv->dtype == SV_Q4 && kv->scale_layer_stride == 0)))
         return SV_EINVAL;
     if (kv->layer_stride % 16 != 0 || kv->scale_layer_stride % 4 != 0) return SV_EINVAL;
     if ((int64_t)batch * n_layers * kv->n_kv_heads * 2 > (int64_t)INT32_MAX) return SV_EUNSUPPORTED;
-    CompactParams p{};
+    p = CompactParams{};
     p.kv = view_of(kv);
     p.layer_stride = kv->layer_stride;
     p.scale_layer_stride = kv->scale_layer_stride;
@@ -405,7 +407,54 @@ int sv_kv_compact(const sv_kv_cache *kv, int n_layers, int batch, int n_nodes,
     p.n_layers = n_layers;
     p.max_ctx = max_ctx;
     p.dtype = kv->dtype;
+    return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sv_greedy_accept(int batch, int n_nodes, int vocab,
+                     const void *logits, int logits_dtype,
+                     const int32_t *draft_ids, const int32_t *parent,
+                     int32_t *accept_len, int32_t *path, int32_t *tokens, int32_t *argmax,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+    AcceptParams p;
+    const int rc = accept_params(batch, n_nodes, vocab, logits, logits_dtype, draft_ids, parent, accept_len, path,
+                                 tokens, argmax, workspace, workspace_bytes, p);
+    if (rc != SV_OK) return rc;
+    const hipError_t e = launch_accept(p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return SV_OK;
+}
+
+int sv_kv_compact(const sv_kv_cache *kv, int n_layers, int batch, int n_nodes,
+                  const int32_t *ctx_lens, int max_ctx,
+                  const int32_t *path, const int32_t *accept_len,
+                  int32_t *new_lens, void *stream) {
+    CompactParams p;
+    const int rc = compact_params(kv, n_layers, batch, n_nodes, ctx_lens, max_ctx, path, accept_len, new_lens,
+                                  false, p);
+    if (rc != SV_OK) return rc;
     const hipError_t e = launch_compact(p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return SV_OK;
+}
+
+int sv_greedy_accept_compact(int batch, int n_nodes, int vocab,
+                             const void *logits, int logits_dtype,
+                             const int32_t *draft_ids, const int32_t *parent,
+                             int32_t *accept_len, int32_t *path, int32_t *tokens, int32_t *argmax,
+                             const sv_kv_cache *kv, int n_layers, const int32_t *ctx_lens, int max_ctx,
+                             int32_t *new_lens, void *workspace, size_t workspace_bytes, void *stream) {
+    AcceptParams p;
+    int rc = accept_params(batch, n_nodes, vocab, logits, logits_dtype, draft_ids, parent, accept_len, path, tokens,
+                           argmax, workspace, workspace_bytes, p);
+    if (rc != SV_OK) return rc;
+    rc = compact_params(kv, n_layers, batch, n_nodes, ctx_lens, max_ctx, nullptr, nullptr, new_lens, true, p.cp);
+    if (rc != SV_OK) return rc;
+    p.compact = 1;
+    const hipError_t e = launch_accept(p, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);
     return SV_OK;
 }

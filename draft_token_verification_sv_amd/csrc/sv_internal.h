@@ -44,6 +44,14 @@ struct AttnParams {
     int part_nt;                  // 1: streaming (non-temporal) stores for the partial O
 };
 
+struct CompactParams {
+    KvView kv;
+    int64_t layer_stride, scale_layer_stride;   // bytes
+    const int32_t *ctx_lens, *path, *accept_len;
+    int32_t *new_lens;
+    int B, N, Hkv, D, n_layers, max_ctx, dtype;
+};
+
 struct AcceptParams {
     const void *logits;           // [B][N][V]
     const int32_t *draft;         // [B][N]
@@ -53,14 +61,8 @@ struct AcceptParams {
     unsigned int *seqs_done;      // [B]    (row, chunk) workgroups done (zero between calls)
     int B, N, V, chunk, n_chunks;
     int logits_f32;
-};
-
-struct CompactParams {
-    KvView kv;
-    int64_t layer_stride, scale_layer_stride;   // bytes
-    const int32_t *ctx_lens, *path, *accept_len;
-    int32_t *new_lens;
-    int B, N, Hkv, D, n_layers, max_ctx, dtype;
+    int compact;                  // also compact the KV of each sequence (cp; path / accept_len unused)
+    CompactParams cp;
 };
 
 // Kernel-side tile sizes (positions staged per iteration) -----------------

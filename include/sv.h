@@ -10,7 +10,8 @@
  *                     the longest root path whose drafts equal their parent's
  *                     argmax, plus the bonus token;
  *   sv_kv_compact     in-place compaction of the accepted rows' KV so that only
- *                     the accepted path remains.
+ *                     the accepted path remains;
+ *   sv_greedy_accept_compact  the last two in one launch.
  *
  * Sources (web pages on speculative decoding; citations name page and section):
  *   [DFN]  "Making Qwen3.5-27B token generation 6x faster on one RTX 3090"
@@ -187,6 +188,24 @@ int sv_kv_compact(const sv_kv_cache *kv, int n_layers, int batch, int n_nodes,
                   const int32_t *ctx_lens, int max_ctx,
                   const int32_t *path, const int32_t *accept_len,
                   int32_t *new_lens, void *stream);
+
+/*
+ * sv_greedy_accept_compact -- sv_greedy_accept followed by sv_kv_compact on
+ * the same stream, in one launch: the workgroup that finishes a sequence's
+ * acceptance walk moves that sequence's accepted KV rows itself (every layer,
+ * KV head, K and V, scale rows of a 4-bit cache), in rounds of at most 32 KB
+ * that each read all their rows before writing any.  Arguments, outputs,
+ * workspace rules and errors are those of the two calls (accept_len and path
+ * are outputs here, not inputs); results are identical to the two calls'.
+ * Sized for few moving rows per sequence (a tree's accepted branch): with many
+ * layers the single workgroup per sequence is slower than sv_kv_compact.
+ */
+int sv_greedy_accept_compact(int batch, int n_nodes, int vocab,
+                             const void *logits, int logits_dtype,
+                             const int32_t *draft_ids, const int32_t *parent,
+                             int32_t *accept_len, int32_t *path, int32_t *tokens, int32_t *argmax,
+                             const sv_kv_cache *kv, int n_layers, const int32_t *ctx_lens, int max_ctx,
+                             int32_t *new_lens, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static text for a return code. */
 const char *sv_error_string(int code);

@@ -134,6 +134,21 @@ def test_compact_checks(lib):
     assert call(kv(capacity=10)) == -1
 
 
+def test_accept_compact_checks(lib):
+    P = ctypes.c_void_p(FAKE)
+
+    def call(d=None, B=1, N=8, V=151936, L=1, ld=1, ctx=FAKE, ws=FAKE, wsb=1 << 30):
+        d = kv() if d is None else d
+        return lib.sv_greedy_accept_compact(B, N, V, P, ld, P, P, P, P, P, None, ctypes.byref(d), L,
+                                            ctypes.c_void_p(ctx), 4096, None, ctypes.c_void_p(ws),
+                                            ctypes.c_size_t(wsb), None)
+    # the checks of both calls apply
+    assert call(N=0) == -1 and call(N=65) == -1 and call(V=0) == -1 and call(ld=2) == -1
+    assert call(ws=0) == -3 and call(wsb=16) == -3
+    assert call(L=0) == -1 and call(L=3) == -1 and call(ctx=0) == -1
+    assert call(d=kv(capacity=10)) == -1 and call(d=kv(layer_stride=24)) == -1
+
+
 def test_options(lib):
     prev = lib.sv_set_option(1, 300)
     assert prev == 0

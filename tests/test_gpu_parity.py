@@ -330,6 +330,48 @@ def test_kv_compact(sv, label, cfg, layers, kw):
     np.testing.assert_array_equal(new_lens.cpu().numpy(), r_new)
 
 
+FUSED_CASES = COMPACT_CASES + [
+    # many moving rows over several layers: the staging rounds of the fused
+    # call (32 KB each) cut through rows and layers
+    # (seed 13: 4 moving rows in sequence 0, 101 KB of rows to move)
+    ("tree bf16 64 nodes 6 layers", workloads.Config("tbm", 2, 8, 4, 256, 40, "bf16", "bf16", "bf16", 500, 64,
+                                                     tree="ddtree", draft_rule="tree"), 6,
+     {"variant": "perfect", "seed": 13}),
+    ("tree q4 64 nodes 6 layers", workloads.Config("tqm", 2, 8, 4, 256, 40, "bf16", "q4", "bf16", 500, 64,
+                                                   tree="ddtree", draft_rule="tree"), 6,
+     {"variant": "perfect", "seed": 13}),
+]
+
+
+@pytest.mark.parametrize("label,cfg,layers,kw", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_accept_compact_fused(sv, label, cfg, layers, kw):
+    """The one-launch acceptance + compaction against the oracle's acceptance
+    and compaction (outputs, every cache array, new lengths)."""
+    say(f"[fused] {label}")
+    kw = dict(kw)
+    case = workloads.make_case(cfg, seed=kw.pop("seed", 23), capacity_pad=4, n_layers=layers, **kw)
+    for rep in range(2):              # the shared workspace comes back zeroed: a second call is exact too
+        dc = DeviceCase(case)
+        before = dc.cache_arrays_host()
+        acc, path, tok, am, new_lens = sv.greedy_accept_compact(dc.logits, dc.drafts, dc.parent, dc.kv, dc.ctx,
+                                                                dc.max_ctx)
+        torch.cuda.synchronize()
+        after = dc.cache_arrays_host()
+        r_am, r_acc, r_path, r_tok = oracle_accept(case)
+        np.testing.assert_array_equal(am.cpu().numpy(), r_am)
+        np.testing.assert_array_equal(acc.cpu().numpy(), r_acc)
+        np.testing.assert_array_equal(path.cpu().numpy(), r_path)
+        np.testing.assert_array_equal(tok.cpu().numpy(), r_tok)
+        lay = (lambda a: a[None]) if layers == 1 else (lambda a: a)
+        exp, r_new, _ = oracle.compact_cache([lay(a) for a in before], ctx_lens=case.ctx_lens, path=r_path,
+                                             accept_len=r_acc,
+                                             page_table=case.page_table if cfg.paged else None,
+                                             page_size=cfg.page_size)
+        for e, g in zip(exp, after):
+            np.testing.assert_array_equal(lay(g), e)
+        np.testing.assert_array_equal(new_lens.cpu().numpy(), r_new)
+
+
 def test_verify_step_end_to_end(sv):
     """attention -> acceptance -> compaction, twice, on a paged batch."""
     cfg = _small("C5", ctx=40, ctx_hi=300, vocab=3001)
