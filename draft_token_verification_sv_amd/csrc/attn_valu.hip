@@ -183,52 +183,47 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
     }
 }
 
-// Split merge: one group of D threads per output row (256 / D rows per block).
-// Pass 1 finds M = max_s m_s and the split weights 2^(m_s - M) in parallel
-// over the splits (weights kept in LDS); pass 2 accumulates the weighted
-// partial rows.  The first 32 partial values of a thread are loaded before
-// pass 1, so their latency overlaps the (m, l) loads; slots past the
-// sequence's splits (not written by this call) are selected away, never
-// multiplied.
+// Split merge: one block of 256 threads per output row.  Thread t covers the 4
+// columns 4 (t % (D/4)) .. +3 of the splits s = t / (D/4) (mod NSG), NSG =
+// 1024 / D split groups, with 16-byte loads.  The first OB partial rows of each
+// thread go out together with the (m, l) loads; the block then finds
+// M = max_s m_s and the weights 2^(m_s - M) (kept in LDS), every thread
+// accumulates its weighted partials, and the split groups add up through LDS.
+// Slots past the sequence's splits (not written by this call) are never read.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
-    constexpr int RPB = 256 / D;            // rows per block
-    constexpr int WPR = D / 64;             // waves per row
-    __shared__ float w_s[RPB][kMaxSplits];
-    __shared__ float red[4];
-    const int t = threadIdx.x % D;
-    const int rib = threadIdx.x / D;
-    const int row = blockIdx.x * RPB + rib;
-    const int rows = p.B * p.N * p.Hq;
-    const bool live = row < rows;
-    const int rr = live ? row : rows - 1;
-    const int h = rr % p.Hq;
-    const int n = (rr / p.Hq) % p.N;
-    const int b = rr / (p.Hq * p.N);
+    constexpr int CG = D / 4;               // column groups of one row
+    constexpr int NSG = 256 / CG;           // split groups
+    constexpr int OB = 16;                  // partial rows in flight per thread
+    __shared__ float w_s[kMaxSplits];
+    __shared__ float red[8];
+    __shared__ f32x4 acc_s[NSG - 1][CG];
+    const int tid = threadIdx.x;
+    const int c = tid % CG, sg = tid / CG;
+    const int row = blockIdx.x;
+    const int h = row % p.Hq;
+    const int n = (row / p.Hq) % p.N;
+    const int b = row / (p.Hq * p.N);
     const int kvh = h / p.G, g = h % p.G;
     const int r = n * p.G + g;
-    // reduction over the D threads (WPR waves) of one row
-    auto row_reduce = [&](float v, bool is_max) -> float {
+    // block-wide reduction (max or sum)
+    auto block_reduce = [&](float v, bool is_max) -> float {
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) {
             const float o = __shfl_xor(v, m, 64);
             v = is_max ? fmaxf(v, o) : v + o;
         }
-        if constexpr (WPR == 1) {
-            return v;
-        } else {
-            __syncthreads();                         // red[] free again
-            if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-            __syncthreads();
-            float a = red[rib * WPR];
+        __syncthreads();                             // red[] free again
+        if ((tid & 63) == 0) red[tid >> 6] = v;
+        __syncthreads();
+        float a = red[0];
 #pragma unroll
-            for (int k = 1; k < WPR; ++k) a = is_max ? fmaxf(a, red[rib * WPR + k]) : a + red[rib * WPR + k];
-            return a;
-        }
+        for (int k = 1; k < 4; ++k) a = is_max ? fmaxf(a, red[k]) : a + red[k];
+        return a;
     };
     // first partial slot and split count of (b, kvh); the static schedule
-    // knows the slots without the context length, so the (m, l) loads start
-    // together with the ctx_lens load
+    // knows the slots without the context length, so the loads start together
+    // with the ctx_lens load
     int64_t base;
     int ns, ns_cap;
     if (p.dyn) {
@@ -241,66 +236,74 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
         const int L = clamp_ctx(p.ctx_lens[b], p.max_ctx) + p.N;
         ns = min(p.n_splits, (L + p.split_len - 1) / p.split_len);
     }
-    // the first OB partial values of this thread's column go out together
-    // with the (m, l) loads; the weights are applied once they are known
-    constexpr int OB = 32;
-    const float *op = p.part_o + (base * p.R + r) * D + t;
+    const float *op = p.part_o + (base * p.R + r) * D + 4 * c;
     const int64_t sstride = (int64_t)p.R * D;
-    float ov[OB];
+    f32x4 ov[OB];
 #pragma unroll
-    for (int k = 0; k < OB; ++k) ov[k] = k < ns_cap ? op[k * sstride] : 0.f;
+    for (int k = 0; k < OB; ++k) {
+        const int sp = sg + k * NSG;
+        ov[k] = sp < ns_cap ? *(const f32x4 *)(op + sp * sstride) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     const float2 *ml = (const float2 *)p.part_ml;
-    constexpr int MLR = kMaxSplits / D;             // splits per thread (upper bound)
+    constexpr int MLR = kMaxSplits / 256;           // (m, l) pairs per thread (upper bound)
     float2 mlv[MLR];
 #pragma unroll
     for (int k = 0; k < MLR; ++k) {
-        const int sp = t + k * D;
+        const int sp = tid + k * 256;
         mlv[k] = sp < ns_cap ? ml[(base + sp) * p.R + r] : make_float2(-INFINITY, 0.f);
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int k = 0; k < MLR; ++k)
-        if (t + k * D < ns) mx = fmaxf(mx, mlv[k].x);
-    const float M = row_reduce(mx, true);
+        if (tid + k * 256 < ns) mx = fmaxf(mx, mlv[k].x);
+    const float M = block_reduce(mx, true);
     float ls = 0.f;
 #pragma unroll
     for (int k = 0; k < MLR; ++k) {
-        const int sp = t + k * D;
+        const int sp = tid + k * 256;
         if (sp < ns) {
             const float w = (mlv[k].x == -INFINITY) ? 0.f : exp2f(mlv[k].x - M);
-            w_s[rib][sp] = w;
+            w_s[sp] = w;
             ls += w * mlv[k].y;
         }
     }
-    const float lsum = row_reduce(ls, false);
-    __syncthreads();
+    const float lsum = block_reduce(ls, false);     // (its barriers also publish w_s)
 
-    float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < OB; k += 4) {
-        acc0 += k + 0 < ns ? w_s[rib][k + 0] * ov[k + 0] : 0.f;
-        acc1 += k + 1 < ns ? w_s[rib][k + 1] * ov[k + 1] : 0.f;
-        acc2 += k + 2 < ns ? w_s[rib][k + 2] * ov[k + 2] : 0.f;
-        acc3 += k + 3 < ns ? w_s[rib][k + 3] * ov[k + 3] : 0.f;
+    for (int k = 0; k < OB; ++k) {
+        const int sp = sg + k * NSG;
+        if (sp < ns) acc += w_s[sp] * ov[k];
     }
 #pragma unroll 1
-    for (int sp = OB; sp < ns; sp += OB) {
+    for (int s0 = OB * NSG; s0 < ns; s0 += OB * NSG) {
 #pragma unroll
-        for (int k = 0; k < OB; ++k) ov[k] = sp + k < ns ? op[(sp + k) * sstride] : 0.f;
+        for (int k = 0; k < OB; ++k) {
+            const int sp = s0 + sg + k * NSG;
+            ov[k] = sp < ns ? *(const f32x4 *)(op + sp * sstride) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-        for (int k = 0; k < OB; k += 4) {
-            acc0 += sp + k + 0 < ns ? w_s[rib][sp + k + 0] * ov[k + 0] : 0.f;
-            acc1 += sp + k + 1 < ns ? w_s[rib][sp + k + 1] * ov[k + 1] : 0.f;
-            acc2 += sp + k + 2 < ns ? w_s[rib][sp + k + 2] * ov[k + 2] : 0.f;
-            acc3 += sp + k + 3 < ns ? w_s[rib][sp + k + 3] * ov[k + 3] : 0.f;
+        for (int k = 0; k < OB; ++k) {
+            const int sp = s0 + sg + k * NSG;
+            if (sp < ns) acc += w_s[sp] * ov[k];
         }
     }
-    if (!live) return;
-    const float v = ((acc0 + acc1) + (acc2 + acc3)) / lsum;
-    const int64_t oi = (((int64_t)b * p.N + n) * p.Hq + h) * D + t;
-    if (p.q_f32) ((float *)p.out)[oi] = v;
-    else ((uint16_t *)p.out)[oi] = (uint16_t)f32_to_bf16_bits(v);
-    if (t == 0 && p.lse != nullptr)
+    if (sg > 0) acc_s[sg - 1][c] = acc;
+    __syncthreads();
+    if (sg > 0) return;
+#pragma unroll
+    for (int k = 0; k < NSG - 1; ++k) acc += acc_s[k][c];
+    const float inv = 1.f / lsum;
+    const int64_t oi = (((int64_t)b * p.N + n) * p.Hq + h) * D + 4 * c;
+    if (p.q_f32) {
+        *(f32x4 *)((float *)p.out + oi) = acc * inv;
+    } else {
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16_bits(acc[0] * inv) | ((uint32_t)f32_to_bf16_bits(acc[1] * inv) << 16);
+        pk.y = (uint32_t)f32_to_bf16_bits(acc[2] * inv) | ((uint32_t)f32_to_bf16_bits(acc[3] * inv) << 16);
+        *(uint2 *)((uint16_t *)p.out + oi) = pk;
+    }
+    if (tid == 0 && p.lse != nullptr)
         p.lse[((int64_t)b * p.N + n) * p.Hq + h] = (M + log2f(lsum)) * 0.69314718055994530942f;
 }
 
@@ -337,10 +340,10 @@ hipError_t launch_attn_merge(const AttnParams &p, int D, hipStream_t st) {
     const int rows = p.B * p.N * p.Hq;
     switch (D) {
         case 64:
-            hipLaunchKernelGGL(attn_merge_kernel<64>, dim3((rows + 3) / 4), dim3(256), 0, st, p);
+            hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(rows), dim3(256), 0, st, p);
             break;
         case 128:
-            hipLaunchKernelGGL(attn_merge_kernel<128>, dim3((rows + 1) / 2), dim3(256), 0, st, p);
+            hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(rows), dim3(256), 0, st, p);
             break;
         case 256:
             hipLaunchKernelGGL(attn_merge_kernel<256>, dim3(rows), dim3(256), 0, st, p);
