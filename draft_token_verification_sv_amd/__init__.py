@@ -23,11 +23,12 @@ __all__ = [
     "SV_F32", "SV_BF16", "SV_Q4", "SVError", "KVCache", "lib", "library_path",
     "verify_attn", "verify_attn_workspace_size", "greedy_accept", "greedy_accept_workspace_size",
     "kv_compact", "greedy_accept_compact", "set_option", "SV_OPT_ATTN_TARGET_WGS", "SV_OPT_ARGMAX_CHUNK", "SV_OPT_ATTN_ROWBLOCKS",
-    "SV_OPT_ATTN_POSGROUPS",
+    "SV_OPT_ATTN_POSGROUPS", "SV_OPT_ATTN_OCCUPANCY",
 ]
 
 SV_F32, SV_BF16, SV_Q4 = 0, 1, 2
 SV_OPT_ATTN_TARGET_WGS, SV_OPT_ARGMAX_CHUNK, SV_OPT_ATTN_ROWBLOCKS, SV_OPT_ATTN_POSGROUPS = 1, 2, 3, 4
+SV_OPT_ATTN_OCCUPANCY = 5
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsv.so")
 if not os.path.exists(library_path):

@@ -43,7 +43,7 @@ namespace {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-template <int D, int NT, int PG, bool Q4>
+template <int D, int NT, int PG, bool Q4, int OCC>
 struct DCfg {
     static constexpr int W = D >= 128 ? SV_SWZ_W : 8;          // swizzle width (chunks)
     // positions per stage: 32 per position group for bf16; for the 4-bit
@@ -54,7 +54,7 @@ struct DCfg {
     static constexpr int SROWB = D / 16;              // fp16 scales per row
     static constexpr int KBYTES = Q4 ? T * CROWB : T * ROWB;   // K part of a stage
     static constexpr int STAGE = Q4 ? 2 * T * (CROWB + SROWB) : 2 * KBYTES;
-    static constexpr int S_RAW = 131072 / STAGE;
+    static constexpr int S_RAW = 131072 / OCC / STAGE;   // OCC workgroups share a CU's LDS
     static constexpr int S = Q4 ? 2 : (S_RAW < 2 ? 2 : (S_RAW > 8 ? 8 : S_RAW));   // ring depth
     static constexpr int NKB = STAGE / 1024;          // 1 KB DMA instructions per stage
     static constexpr int LPW = NKB / 4;               // per wave
@@ -125,9 +125,9 @@ __device__ __forceinline__ void dma16s(uint32_t lds_base, const void *sbase, uin
 
 constexpr int kMaxSplitPages = 512;
 
-template <int D, int NT, int PG, bool PAGED, bool Q4>
-__global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
-    using C = DCfg<D, NT, PG, Q4>;
+template <int D, int NT, int PG, bool PAGED, bool Q4, int OCC>
+__global__ __launch_bounds__(256, OCC) void attn_dma_kernel(AttnParams p) {
+    using C = DCfg<D, NT, PG, Q4, OCC>;
     constexpr int T = C::T, S = C::S;
     __shared__ __attribute__((aligned(1024))) uint8_t ring[S * C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t staging[Q4 ? 2 * C::STAGING : 16];
@@ -645,15 +645,25 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnParams p) {
     }
 }
 
-template <int D, int NT, int PG, bool PAGED, bool Q4>
+template <int D, int NT, int PG, bool PAGED, bool Q4, int OCC = 1>
 hipError_t launch_one(const AttnParams &p, hipStream_t st) {
     const int grid = ((p.n_units + 7) / 8) * 8 * p.n_rowblocks;
-    hipLaunchKernelGGL((attn_dma_kernel<D, NT, PG, PAGED, Q4>), dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((attn_dma_kernel<D, NT, PG, PAGED, Q4, OCC>), dim3(grid), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
 template <int D, bool PAGED>
-hipError_t launch_shape(const AttnParams &p, int nt, int pg, bool q4, hipStream_t st) {
+hipError_t launch_shape(const AttnParams &p, int nt, int pg, bool q4, int occ, hipStream_t st) {
+    if (occ == 2) {
+        // two workgroups per CU (half-size rings): one row tile, stages of <= 16 KB
+        if (q4 || nt != 1) return hipErrorInvalidValue;
+        if (pg == 1) return launch_one<D, 1, 1, PAGED, false, 2>(p, st);
+        if constexpr (D <= 128) {
+            if (pg == 2) return launch_one<D, 1, 2, PAGED, false, 2>(p, st);
+        }
+        return hipErrorInvalidValue;
+    }
+    if (occ != 1) return hipErrorInvalidValue;
     if (q4) {
         if constexpr (D == 256) {
             if (pg != 1) return hipErrorInvalidValue;
@@ -676,20 +686,20 @@ hipError_t launch_shape(const AttnParams &p, int nt, int pg, bool q4, hipStream_
 }
 
 template <int D>
-hipError_t launch_d(const AttnParams &p, int nt, int pg, bool q4, hipStream_t st) {
-    return p.kv.page_table != nullptr ? launch_shape<D, true>(p, nt, pg, q4, st)
-                                      : launch_shape<D, false>(p, nt, pg, q4, st);
+hipError_t launch_d(const AttnParams &p, int nt, int pg, bool q4, int occ, hipStream_t st) {
+    return p.kv.page_table != nullptr ? launch_shape<D, true>(p, nt, pg, q4, occ, st)
+                                      : launch_shape<D, false>(p, nt, pg, q4, occ, st);
 }
 
 }  // namespace
 
 int attn_dma_max_split_pages() { return kMaxSplitPages; }
 
-hipError_t launch_attn_dma(const AttnParams &p, int D, int nt, int pg, bool q4, hipStream_t st) {
+hipError_t launch_attn_dma(const AttnParams &p, int D, int nt, int pg, bool q4, int occ, hipStream_t st) {
     switch (D) {
-        case 64: return launch_d<64>(p, nt, pg, q4, st);
-        case 128: return launch_d<128>(p, nt, pg, q4, st);
-        case 256: return launch_d<256>(p, nt, pg, q4, st);
+        case 64: return launch_d<64>(p, nt, pg, q4, occ, st);
+        case 128: return launch_d<128>(p, nt, pg, q4, occ, st);
+        case 256: return launch_d<256>(p, nt, pg, q4, occ, st);
     }
     return hipErrorInvalidValue;
 }

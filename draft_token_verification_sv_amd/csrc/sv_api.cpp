@@ -17,6 +17,7 @@ int g_attn_target_wgs = 0;     // 0: choose by batch (see plan_attn)
 int g_argmax_chunk = 16384;
 int g_attn_rowblocks = 0;      // 0: planner's choice
 int g_attn_posgroups = 0;      // 0: planner's choice
+int g_attn_occupancy = 0;      // 0: planner's choice
 
 int hip_fail(hipError_t e) {
     g_last_hip_error = (int)e;
@@ -74,6 +75,7 @@ enum AttnKind { kValu = 0, kMfmaStaged = 1, kMfmaDma = 2 };
 struct AttnPlan {
     int kind;
     int nt, pg;
+    int occ;                                  // pipelined kernel: workgroups per CU
     int rows_per_block, n_rowblocks;
     int n_splits, split_len;                  // static schedule
     int dyn, units, split_q, split_min, split_max;
@@ -103,7 +105,8 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
     // head dim 256; other 4-bit caches go to the register-staged kernel
     const bool q4 = kv_dtype == SV_Q4;
     pl.kind = !mfma ? kValu : ((kv_dtype == SV_BF16 || (q4 && D == 256)) ? kMfmaDma : kMfmaStaged);
-    const int target = g_attn_target_wgs > 0 ? g_attn_target_wgs : (pl.kind == kMfmaDma ? 256 : 512);
+    int target = g_attn_target_wgs > 0 ? g_attn_target_wgs : (pl.kind == kMfmaDma ? 256 : 512);
+    pl.occ = 1;
     const double pos_bytes = kv_dtype == SV_F32 ? D * 8.0 : (kv_dtype == SV_BF16 ? D * 4.0 : D * 1.125);
     // the pipelined kernel keeps a split's page ids in LDS
     const int64_t max_split = (pl.kind == kMfmaDma && page_size > 0)
@@ -122,6 +125,19 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
         n_splits = (int)ceil_div(L, split_len);
     };
 
+    // Two workgroups per CU on the pipelined kernel (half-size rings, stages of
+    // <= 32 KB, one row tile per wavefront): twice the units balance uneven
+    // sequences better and each workgroup's start overlaps the other's work.
+    // Default for batches (8 paged sequences of 1K-16K positions: -3 %); a
+    // single sequence is split evenly anyway and loses (one of 4K: +10 %).
+    auto occupancy2 = [&]() {
+        const bool want = g_attn_occupancy == 2 || (g_attn_occupancy == 0 && B > 1);
+        if (!want || pl.kind != kMfmaDma || q4 || pl.nt != 1) return;
+        pl.occ = 2;
+        pl.pg = std::min(pl.pg, std::max(1, std::min(2, 32768 / (128 * D))));
+        if (g_attn_target_wgs == 0) target = 512;
+    };
+
     if (mfma) {
         const int RT = (R + 15) / 16;
         // row tiles per wave: up to 3 on the pipelined kernel, 2 on the
@@ -135,6 +151,7 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
             pl.nt = 1;
             pl.rows_per_block = 16;
             pl.n_rowblocks = 1;
+            occupancy2();
             splits_for(B * Hkv, pl.split_len, pl.n_splits);
         } else {
             pl.pg = 1;
@@ -165,6 +182,7 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
                 const int pg_rows = tpb == 1 ? 4 : (tpb == 2 ? 2 : 1);
                 pl.pg = std::min(std::min(g_attn_posgroups, pg_rows), std::min(4, 65536 / (128 * D)));
             }
+            occupancy2();
             splits_for(B * Hkv * pl.n_rowblocks, pl.split_len, pl.n_splits);
         }
     } else {
@@ -248,6 +266,11 @@ int sv_set_option(int option, int value) {
             prev = g_attn_posgroups;
             g_attn_posgroups = value;
             return prev;
+        case SV_OPT_ATTN_OCCUPANCY:
+            if (value < 0 || value > 2) return SV_EINVAL;
+            prev = g_attn_occupancy;
+            g_attn_occupancy = value;
+            return prev;
         case SV_OPT_ARGMAX_CHUNK:
             if (value <= 0 || value % 8 != 0) return SV_EINVAL;
             prev = g_argmax_chunk;
@@ -324,7 +347,7 @@ int sv_verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
 
     hipStream_t st = (hipStream_t)stream;
     hipError_t e;
-    if (pl.kind == kMfmaDma) e = launch_attn_dma(p, D, pl.nt, pl.pg, kv->dtype == SV_Q4, st);
+    if (pl.kind == kMfmaDma) e = launch_attn_dma(p, D, pl.nt, pl.pg, kv->dtype == SV_Q4, pl.occ, st);
     else if (pl.kind == kMfmaStaged) e = launch_attn_mfma(p, kv->dtype, D, pl.nt, pl.pg, st);
     else e = launch_attn_valu(p, kv->dtype, D, st);
     if (e != hipSuccess) return hip_fail(e);

@@ -72,7 +72,7 @@ constexpr int kMaxSplits = 1024;               // splits per (sequence, KV head,
 
 // launchers (return the hipError_t of the launch) -------------------------
 hipError_t launch_attn_mfma(const AttnParams &p, int dtype, int D, int nt, int pg, hipStream_t s);
-hipError_t launch_attn_dma(const AttnParams &p, int D, int nt, int pg, bool q4, hipStream_t s);
+hipError_t launch_attn_dma(const AttnParams &p, int D, int nt, int pg, bool q4, int occ, hipStream_t s);
 int attn_dma_max_split_pages();
 hipError_t launch_attn_valu(const AttnParams &p, int dtype, int D, hipStream_t s);
 hipError_t launch_attn_merge(const AttnParams &p, int D, hipStream_t s);

@@ -224,6 +224,10 @@ int sv_last_hip_error(void);
  *   SV_OPT_ATTN_POSGROUPS   waves sharing one 16-row tile on the pipelined bf16
  *                           path (1, 2 or 4; each takes 32 positions of a
  *                           stage); 0 (default) = planner's choice
+ *   SV_OPT_ATTN_OCCUPANCY   workgroups per CU on the pipelined bf16 path for
+ *                           one row tile per wave (1 or 2: half-size LDS
+ *                           rings, twice the work units); 0 (default) =
+ *                           planner's choice
  * Returns the previous value, or SV_EINVAL for an unknown option or a value
  * out of range.  A workspace sized under one setting may be too small under
  * another (the call then returns SV_EWORKSPACE).
@@ -233,6 +237,7 @@ int sv_last_hip_error(void);
 #define SV_OPT_ARGMAX_CHUNK    2
 #define SV_OPT_ATTN_ROWBLOCKS  3
 #define SV_OPT_ATTN_POSGROUPS  4
+#define SV_OPT_ATTN_OCCUPANCY  5
 int sv_set_option(int option, int value);
 
 #ifdef __cplusplus

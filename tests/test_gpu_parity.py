@@ -158,6 +158,27 @@ def test_attention_position_groups(sv, pg):
     check_attention(case, out, lse)
 
 
+OCC_CASES = ["C2 ctx333", "C2 ctx1000 peaked", "C3 tree22 ctx16 peaked", "C5 paged b8", "C5 paged b8 peaked"]
+
+
+@pytest.mark.parametrize("label", OCC_CASES)
+@pytest.mark.parametrize("target", [0, 37, 700])
+def test_attention_two_per_cu(sv, label, target):
+    """Two workgroups per CU (half-size rings, twice the units) against the oracle."""
+    cfg, kw = [(c, k) for (l, c, k) in ATTN_CASES if l == label][0]
+    say(f"[attn occ2] {label} target={target}")
+    case = workloads.make_case(cfg, seed=5, **kw)
+    prev = sv.set_option(sv.SV_OPT_ATTN_OCCUPANCY, 2)
+    prev_t = sv.set_option(sv.SV_OPT_ATTN_TARGET_WGS, target)
+    try:
+        out, lse = DeviceCase(case).attn()
+        torch.cuda.synchronize()
+    finally:
+        sv.set_option(sv.SV_OPT_ATTN_OCCUPANCY, prev)
+        sv.set_option(sv.SV_OPT_ATTN_TARGET_WGS, prev_t)
+    check_attention(case, out, lse)
+
+
 @pytest.mark.parametrize("B", [64, 65, 1024])
 def test_attention_large_batch(sv, B):
     """Batch sizes at the schedule's paths: one wavefront (<= 64 sequences),
