@@ -15,7 +15,9 @@ the stored inputs:
 * ``accept``: per-row argmax (lowest index wins ties), the greedy acceptance
   walk (longest accepted root path, plus the bonus token), and an
   independent brute-force version of the walk;
-* ``compact``: the post-acceptance KV compaction as a snapshot copy.
+* ``compact``: the post-acceptance KV compaction as a snapshot copy;
+* ``append``: writing the verify block's K/V rows into the cache, with the
+  4-bit quantisation at write time.
 
 Sources: the single-RTX-3090 DFlash + DDTree note ("Making Qwen3.5-27B token
 generation 6x faster on one RTX 3090", blog.xiaohack.org): greedy verify and
@@ -36,10 +38,11 @@ from .formats import widen_bf16, widen_fp16, widen_f32, q4_decode
 from .attention import ancestor_matrix, verify_mask, verify_attention_seq, verify_attention
 from .accept import argmax_first, accept_walk, accept_bruteforce, greedy_accept
 from .compact import compact_cache
+from .append import bf16_round, q4_quantise, kv_append
 
 __all__ = [
     "widen_bf16", "widen_fp16", "widen_f32", "q4_decode",
     "ancestor_matrix", "verify_mask", "verify_attention_seq", "verify_attention",
     "argmax_first", "accept_walk", "accept_bruteforce", "greedy_accept",
-    "compact_cache",
+    "compact_cache", "bf16_round", "q4_quantise", "kv_append",
 ]
