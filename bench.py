@@ -201,6 +201,17 @@ def main():
     def compact(i):
         sv.kv_compact(kvs[i % n_copies], ctx, max_ctx, path, acc, new_lens=new_lens)
 
+    # the verify block's K/V rows written into the cache (timed separately)
+    src_kind = "bf16" if cfg.q_dtype == "bf16" else "f32"
+    rng_new = np.random.default_rng(977)
+    new_rows = [up((rng_new.standard_normal((B, N, cfg.n_kv_heads, D)) * 0.5).astype(np.float32)
+                   if src_kind == "f32" else
+                   workloads.bf16_bits((rng_new.standard_normal((B, N, cfg.n_kv_heads, D)) * 0.5).astype(np.float32)),
+                   src_kind) for _ in range(2)]
+
+    def append(i):
+        sv.kv_append(kvs[i % n_copies], new_rows[0], new_rows[1], ctx, max_ctx)
+
     def accept_compact(i):
         sv.greedy_accept_compact(copies[i % n_copies]["logits"], drafts, parent, kvs[i % n_copies], ctx, max_ctx,
                                  workspace=ws_g, outputs=(acc, path, tok, None), new_lens=new_lens)
@@ -247,6 +258,8 @@ def main():
     compact_us = timed(g_cmp) / args.steps * 1e3
     g_ac = capture(accept_compact)
     accept_compact_us = timed(g_ac) / args.steps * 1e3
+    g_app = capture(append)                 # last: it rewrites the draft rows of the rotated caches
+    append_us = timed(g_app) / args.steps * 1e3
     attn_ms = np.array([attn_total_ms / args.steps])
 
     ms_per_step = total_ms / args.steps
@@ -279,7 +292,8 @@ def main():
                      "kernel": "sv_verify_attn (split + merge kernels)",
                      "algorithmic_bytes": int(attn_bytes)},
         "breakdown_us": {"verify_attn": round(attn_us, 2), "greedy_accept": round(accept_us, 2),
-                         "kv_compact": round(compact_us, 2), "greedy_accept_compact": round(accept_compact_us, 2)},
+                         "kv_compact": round(compact_us, 2), "greedy_accept_compact": round(accept_compact_us, 2),
+                         "kv_append (not in the step)": round(append_us, 2)},
         "accepted_tokens_per_step": None,
     }
     a_host = acc.cpu().numpy()

@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "SV_F32", "SV_BF16", "SV_Q4", "SVError", "KVCache", "lib", "library_path",
     "verify_attn", "verify_attn_workspace_size", "greedy_accept", "greedy_accept_workspace_size",
-    "kv_compact", "greedy_accept_compact", "set_option", "SV_OPT_ATTN_TARGET_WGS", "SV_OPT_ARGMAX_CHUNK", "SV_OPT_ATTN_ROWBLOCKS",
+    "kv_compact", "greedy_accept_compact", "kv_append", "set_option", "SV_OPT_ATTN_TARGET_WGS", "SV_OPT_ARGMAX_CHUNK", "SV_OPT_ATTN_ROWBLOCKS",
     "SV_OPT_ATTN_POSGROUPS", "SV_OPT_ATTN_OCCUPANCY",
 ]
 
@@ -70,6 +70,8 @@ lib.sv_greedy_accept.restype = _I
 lib.sv_greedy_accept.argtypes = [_I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
 lib.sv_kv_compact.restype = _I
 lib.sv_kv_compact.argtypes = [ctypes.POINTER(_KvDesc), _I, _I, _I, _P, _I, _P, _P, _P, _P]
+lib.sv_kv_append.restype = _I
+lib.sv_kv_append.argtypes = [ctypes.POINTER(_KvDesc), _I, _I, _P, _I, _P, _P, _I, _P]
 lib.sv_greedy_accept_compact.restype = _I
 lib.sv_greedy_accept_compact.argtypes = [_I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P,
                                          ctypes.POINTER(_KvDesc), _I, _P, _I, _P, _P, ctypes.c_size_t, _P]
@@ -326,6 +328,22 @@ def greedy_accept_compact(logits: torch.Tensor, draft_ids: torch.Tensor, parent:
                                       workspace.numel() * workspace.element_size(), _stream(dev))
     _check(rc, "sv_greedy_accept_compact")
     return acc, path, tok, am, new_lens
+
+
+def kv_append(kv: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, ctx_lens: torch.Tensor, max_ctx: int) -> None:
+    """Write the verify block's rows ``[B, n, Hkv, D]`` (fp32 or bf16) into layer 0
+    of ``kv`` at positions ctx .. ctx + n - 1 (quantised for a 4-bit cache)."""
+    for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+        if t.dim() != 4 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous [B, n, Hkv, D] device tensor")
+    if k_new.shape != v_new.shape or k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new differ in shape or dtype")
+    _i32(ctx_lens, "ctx_lens")
+    B, n, H, D = k_new.shape
+    d = kv.desc(0)
+    rc = lib.sv_kv_append(ctypes.byref(d), B, n, _ptr(ctx_lens), int(max_ctx), _ptr(k_new), _ptr(v_new),
+                          _dtype_code(k_new), _stream(k_new.device))
+    _check(rc, "sv_kv_append")
 
 
 def set_option(option: int, value: int) -> int:

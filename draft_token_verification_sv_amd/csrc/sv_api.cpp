@@ -464,6 +464,30 @@ int sv_kv_compact(const sv_kv_cache *kv, int n_layers, int batch, int n_nodes,
     return SV_OK;
 }
 
+int sv_kv_append(const sv_kv_cache *kv, int batch, int n_rows, const int32_t *ctx_lens, int max_ctx,
+                 const void *k_new, const void *v_new, int src_dtype, void *stream) {
+    if (batch < 1 || n_rows < 1 || n_rows > 64 || max_ctx < 0 || max_ctx > (1 << 30)) return SV_EINVAL;
+    const int rc = check_kv(kv, batch, n_rows, max_ctx);
+    if (rc != SV_OK) return rc;
+    if (ctx_lens == nullptr || k_new == nullptr || v_new == nullptr) return SV_EINVAL;
+    if (src_dtype != SV_F32 && src_dtype != SV_BF16) return SV_EINVAL;
+    if (!aligned(k_new, 16) || !aligned(v_new, 16)) return SV_EINVAL;
+    if ((int64_t)batch * n_rows * kv->n_kv_heads * 2 / 4 + 1 > (int64_t)INT32_MAX) return SV_EUNSUPPORTED;
+    AppendParams p{};
+    p.kv = view_of(kv);
+    p.ctx_lens = ctx_lens;
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.B = batch;
+    p.n = n_rows;
+    p.Hkv = kv->n_kv_heads;
+    p.D = kv->head_dim;
+    p.max_ctx = max_ctx;
+    const hipError_t e = launch_append(p, src_dtype, kv->dtype, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return SV_OK;
+}
+
 int sv_greedy_accept_compact(int batch, int n_nodes, int vocab,
                              const void *logits, int logits_dtype,
                              const int32_t *draft_ids, const int32_t *parent,

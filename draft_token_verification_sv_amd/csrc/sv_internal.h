@@ -65,6 +65,13 @@ struct AcceptParams {
     CompactParams cp;
 };
 
+struct AppendParams {
+    KvView kv;                    // layer 0; k / v (and ks / vs) are written
+    const int32_t *ctx_lens;      // [B]
+    const void *k_new, *v_new;    // [B][n][Hkv][D], fp32 or bf16
+    int B, n, Hkv, D, max_ctx;
+};
+
 // Kernel-side tile sizes (positions staged per iteration) -----------------
 constexpr int kMfmaTileElems = 16384;          // T * D bf16 elements per K (or V) tile
 constexpr int kValuTileElems = 8192;           // T * D fp32 elements per K (or V) tile
@@ -78,5 +85,6 @@ hipError_t launch_attn_valu(const AttnParams &p, int dtype, int D, hipStream_t s
 hipError_t launch_attn_merge(const AttnParams &p, int D, hipStream_t s);
 hipError_t launch_accept(const AcceptParams &p, hipStream_t s);
 hipError_t launch_compact(const CompactParams &p, hipStream_t s);
+hipError_t launch_append(const AppendParams &p, int src_dtype, int dst_dtype, hipStream_t s);
 
 }  // namespace sv

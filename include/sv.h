@@ -11,7 +11,9 @@
  *                     argmax, plus the bonus token;
  *   sv_kv_compact     in-place compaction of the accepted rows' KV so that only
  *                     the accepted path remains;
- *   sv_greedy_accept_compact  the last two in one launch.
+ *   sv_greedy_accept_compact  the last two in one launch;
+ *   sv_kv_append      the verify block's K/V rows written into the cache
+ *                     (quantised at write time for a 4-bit cache).
  *
  * Sources (web pages on speculative decoding; citations name page and section):
  *   [DFN]  "Making Qwen3.5-27B token generation 6x faster on one RTX 3090"
@@ -188,6 +190,27 @@ int sv_kv_compact(const sv_kv_cache *kv, int n_layers, int batch, int n_nodes,
                   const int32_t *ctx_lens, int max_ctx,
                   const int32_t *path, const int32_t *accept_len,
                   int32_t *new_lens, void *stream);
+
+/*
+ * sv_kv_append -- write the verify block's K/V rows into the cache, quantising
+ * them for a 4-bit cache [DFN "128K context in 24 GB": the KV cache is kept in
+ * 4 bits and converted as rows are written].  The step just before
+ * sv_verify_attn: row i of sequence b goes to position ctx_b + i (ctx clamped
+ * to [0, max_ctx]) of every KV head, layer 0 of `kv`.
+ *   k_new, v_new  device [batch][n_rows][n_kv_heads][head_dim], src_dtype
+ *                 SV_F32 or SV_BF16, 16-byte aligned (bf16 sources are
+ *                 widened exactly to fp32).
+ *   SV_F32 cache: the values; SV_BF16 cache: round to nearest even;
+ *   SV_Q4 cache:  per 32-value block d = half(max|x| / 7) (fp32 division, then
+ *                 round to nearest even into IEEE half), code =
+ *                 clamp(round_half_even(x / d), -8, 7) + 8 (fp32 division),
+ *                 8 for every value of a block with d = 0; layout as above.
+ * Paged: positions whose page id lies outside the pool are skipped.
+ * 1 <= n_rows <= 64; the capacity checks of sv_verify_attn apply with
+ * n_nodes = n_rows.  Non-finite inputs give unspecified codes.
+ */
+int sv_kv_append(const sv_kv_cache *kv, int batch, int n_rows, const int32_t *ctx_lens, int max_ctx,
+                 const void *k_new, const void *v_new, int src_dtype, void *stream);
 
 /*
  * sv_greedy_accept_compact -- sv_greedy_accept followed by sv_kv_compact on

@@ -149,6 +149,19 @@ def test_accept_compact_checks(lib):
     assert call(d=kv(capacity=10)) == -1 and call(d=kv(layer_stride=24)) == -1
 
 
+def test_kv_append_checks(lib):
+    P = ctypes.c_void_p(FAKE)
+
+    def call(d=None, B=1, n=8, ctx=FAKE, k=FAKE, src=1, max_ctx=4096):
+        d = kv() if d is None else d
+        return lib.sv_kv_append(ctypes.byref(d), B, n, ctypes.c_void_p(ctx), max_ctx, ctypes.c_void_p(k), P,
+                                src, None)
+    assert call(n=0) == -1 and call(n=65) == -1 and call(B=0) == -1
+    assert call(src=2) == -1 and call(src=7) == -1          # sources are fp32 or bf16
+    assert call(ctx=0) == -1 and call(k=0) == -1 and call(k=FAKE + 8) == -1
+    assert call(d=kv(capacity=4100)) == -1                   # 4096 + 8 rows do not fit
+
+
 def test_options(lib):
     prev = lib.sv_set_option(1, 300)
     assert prev == 0

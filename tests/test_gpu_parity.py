@@ -393,6 +393,78 @@ def test_accept_compact_fused(sv, label, cfg, layers, kw):
         np.testing.assert_array_equal(new_lens.cpu().numpy(), r_new)
 
 
+# ---------------------------------------------------------------------------
+# writing the verify block into the cache
+# ---------------------------------------------------------------------------
+
+# (label, cache dtype, D, B, n, Hkv, page_size (0: contiguous), source dtype)
+APPEND_CASES = [
+    ("bf16 chain block D256", "bf16", 256, 1, 8, 4, 0, "bf16"),
+    ("bf16 from f32 D128 B3", "bf16", 128, 3, 5, 2, 0, "f32"),
+    ("f32 from f32 D64", "f32", 64, 2, 4, 1, 0, "f32"),
+    ("f32 from bf16 D64", "f32", 64, 2, 4, 1, 0, "bf16"),
+    ("q4 block16 D256", "q4", 256, 1, 16, 4, 0, "bf16"),
+    ("q4 from f32 D256", "q4", 256, 2, 22, 4, 0, "f32"),
+    ("q4 paged D128 B3", "q4", 128, 3, 5, 2, 16, "f32"),
+    ("q4 paged D64 bad page", "q4", 64, 2, 9, 2, 8, "bf16"),
+    ("bf16 paged batch8 D128", "bf16", 128, 8, 4, 8, 16, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", APPEND_CASES, ids=[c[0] for c in APPEND_CASES])
+def test_kv_append(sv, case):
+    """Cache bytes after the write equal the oracle's, bit for bit (rounding
+    to bf16, the 4-bit quantiser's half-precision scale and ties to even)."""
+    label, dt, D, B, n, H, ps, src = case
+    say(f"[append] {label}")
+    from sv_harness import dev_tensor
+    rng = np.random.default_rng(31)
+    ctx = rng.integers(0, 40, B).astype(np.int32)
+    ctx[-1] = 60                                          # clamped to max_ctx
+    max_ctx = 45
+    # new rows: mixed magnitudes, zero blocks and exact ties of x / d
+    x = (rng.standard_normal((2, B, n, H, D)) * rng.uniform(0.01, 30, (2, B, n, H, 1))).astype(np.float32)
+    x[0, 0, 0, 0, :32] = 0.0
+    x[1, 0, 0, 0, :32] = np.float32(0.5) * np.arange(-16, 16, dtype=np.float32)
+    if src == "bf16":
+        new = [workloads.bf16_bits(x[0]), workloads.bf16_bits(x[1])]
+    else:
+        new = [x[0], x[1]]
+    if ps == 0:
+        lead = (B, H, max_ctx + n)
+        pt = None
+    else:
+        per = (max_ctx + n + ps - 1) // ps
+        pool = B * per + 3
+        lead = (pool, H, ps)
+        pt = rng.permutation(pool)[:B * per].reshape(B, per).astype(np.int32)
+        if "bad page" in label:
+            pt[0, -1] = pool + 5                          # outside the pool: skipped
+    if dt == "q4":
+        arrs = [rng.integers(0, 256, lead + (D // 2,), dtype=np.uint8) for _ in range(2)]
+        arrs += [rng.integers(0, 2**15, lead + (D // 32,), dtype=np.uint16) for _ in range(2)]
+        kinds = ["u8", "u8", "u16", "u16"]
+    elif dt == "bf16":
+        arrs = [rng.integers(0, 2**15, lead + (D,), dtype=np.uint16) for _ in range(2)]
+        kinds = ["bf16", "bf16"]
+    else:
+        arrs = [rng.standard_normal(lead + (D,)).astype(np.float32) for _ in range(2)]
+        kinds = ["f32", "f32"]
+    dev = [dev_tensor(a, k_) for a, k_ in zip(arrs, kinds)]
+    kv = sv.KVCache(k=dev[0], v=dev[1], k_scale=dev[2] if dt == "q4" else None,
+                    v_scale=dev[3] if dt == "q4" else None,
+                    page_table=dev_tensor(pt, "i32") if pt is not None else None)
+    sv.kv_append(kv, dev_tensor(new[0], src), dev_tensor(new[1], src), dev_tensor(ctx, "i32"), max_ctx)
+    torch.cuda.synchronize()
+    exp = oracle.kv_append(arrs, new[0], new[1], ctx_lens=ctx, dtype=dt, src_dtype=src, max_ctx=max_ctx,
+                           page_table=pt, page_size=ps)
+    for e, g, k_ in zip(exp, dev, kinds):
+        got = g.view(torch.int16).cpu().numpy().view(np.uint16) if k_ == "bf16" else g.cpu().numpy()
+        if k_ == "u16":
+            got = got.view(np.uint16)
+        np.testing.assert_array_equal(got, e)
+
+
 def test_verify_step_end_to_end(sv):
     """attention -> acceptance -> compaction, twice, on a paged batch."""
     cfg = _small("C5", ctx=40, ctx_hi=300, vocab=3001)
