@@ -106,8 +106,11 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
 
 #pragma unroll 1
     for (int tp = p0; tp < p1; tp += T) {
-        // stage K and V rows [tp, tp + T) as fp32
-        for (int c = tid; c < T * CPR; c += 256) {
+        // the tile's positions in the split: the loops below stop there (a
+        // short split costs what its positions cost, not a whole tile)
+        const int nv = min(T, p1 - tp);
+        // stage K and V rows [tp, tp + nv) as fp32
+        for (int c = tid; c < nv * CPR; c += 256) {
             const int row = c / CPR, ch = c % CPR;
             const int pos = tp + row;
             float kv8[VPC], vv8[VPC];
@@ -136,8 +139,10 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
             const int pt = j + 16 * i;
             const int pos = tp + pt;
             float acc = 0.f;
+            if (pt < nv) {
 #pragma unroll 8
-            for (int d = 0; d < D; ++d) acc = __builtin_fmaf(Qs[r * D + d], Ks[pt * DP + d], acc);
+                for (int d = 0; d < D; ++d) acc = __builtin_fmaf(Qs[r * D + d], Ks[pt * DP + d], acc);
+            }
             const int rel = pos - ctx;          // draft index (negative: cache row)
             bool vis = row_ok && pos < p1;
             if (rel >= 0) vis = vis && (((anc >> (rel & 63)) & 1ull) != 0ull);
@@ -167,7 +172,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
             const int d = j + 16 * k;
             float acc = o[k] * alpha;
 #pragma unroll 8
-            for (int pt = 0; pt < T; ++pt) acc = __builtin_fmaf(Ps[r * T + pt], Vs[pt * D + d], acc);
+            for (int pt = 0; pt < nv; ++pt) acc = __builtin_fmaf(Ps[r * T + pt], Vs[pt * D + d], acc);
             o[k] = acc;
         }
         __syncthreads();
