@@ -18,6 +18,11 @@ DDTree verification (the single-RTX-3090 DFlash note, sections "From
 autoregressive to DDTree" and "Key breakthroughs") runs exactly this for the
 budget+1 rows of the tree: each node attends to the cache and its own root
 path.
+
+Sliding window (same note, the addendum on 60K context: flash attention over
+only the most recent 2,048 KV positions instead of the whole context): with a
+window W >= N the key range shrinks to its last W rows, ``j >= ctx + N - W``,
+for every verify row of the block alike (the draft rows always stay inside).
 """
 import numpy as np
 
@@ -44,17 +49,22 @@ def ancestor_matrix(parent) -> np.ndarray:
     return A
 
 
-def verify_mask(parent, ctx: int) -> np.ndarray:
-    """Explicit boolean mask ``[N, ctx + N]`` of the verify rows."""
+def verify_mask(parent, ctx: int, window: int = 0) -> np.ndarray:
+    """Explicit boolean mask ``[N, ctx + N]`` of the verify rows (``window`` > 0:
+    only the last ``window`` key rows)."""
     A = ancestor_matrix(parent)
     n = A.shape[0]
     M = np.zeros((n, ctx + n), dtype=bool)
     M[:, :ctx] = True
     M[:, ctx:] = A
+    if window > 0:
+        if window < n:
+            raise ValueError("the window must hold the N verify rows")
+        M[:, :max(0, ctx + n - window)] = False
     return M
 
 
-def verify_attention_seq(q, K, V, ctx: int, parent, scale: float, heads=None):
+def verify_attention_seq(q, K, V, ctx: int, parent, scale: float, heads=None, window: int = 0):
     """One sequence.
 
     ``q``: float64 ``[N, Hq, D]``; ``K``, ``V``: float64 ``[Hkv, ctx + N, D]``
@@ -66,7 +76,7 @@ def verify_attention_seq(q, K, V, ctx: int, parent, scale: float, heads=None):
     n, hq, d = q.shape
     hkv = K.shape[0]
     group = hq // hkv
-    mask = verify_mask(parent, ctx)
+    mask = verify_mask(parent, ctx, window)
     out = np.full((n, hq, d), np.nan)
     lse = np.full((n, hq), np.nan)
     for h in (range(hq) if heads is None else heads):
@@ -104,7 +114,7 @@ def logical_rows(store, scale_store, *, b: int, head: int, length: int, dtype: s
     return widen(raw, dtype)
 
 
-def verify_attention(case, *, scale=None, heads=None, batch=None):
+def verify_attention(case, *, scale=None, heads=None, batch=None, window=0):
     """Whole-batch attention for a case object (``workloads.Case`` shape).
 
     Returns ``out [B, N, Hq, D]`` and ``lse [B, N, Hq]``.  ``heads`` /
@@ -137,7 +147,7 @@ def verify_attention(case, *, scale=None, heads=None, batch=None):
             # run the single-sequence definition on this KV head only
             qg = qb[:, g * group:(g + 1) * group, :]
             o, ls = verify_attention_seq(qg, K[None], V[None], ctx, case.parent[b], scale,
-                                         heads=[h - g * group for h in hs])
+                                         heads=[h - g * group for h in hs], window=window)
             for h in hs:
                 out[b, :, h] = o[:, h - g * group]
                 lse[b, :, h] = ls[:, h - g * group]

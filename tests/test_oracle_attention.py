@@ -265,3 +265,48 @@ def test_paged_rows_equal_contiguous_rows():
             g = logical_rows(pages, None, b=b, head=h, length=int(L[b]), dtype="f32",
                              page_table=pt, page_size=ps)
             np.testing.assert_array_equal(a, g)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_window_equals_attention_over_the_last_rows(seed):
+    """Sliding window: attention with window W equals the un-windowed
+    definition run on a cache cut to its last W key rows (the rows are sliced,
+    not masked), and each row equals SDPA over the window rows of its root
+    path."""
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(1, 12))
+    ctx = int(rng.integers(0, 60))
+    W = int(rng.integers(n, ctx + n + 5))
+    Hq, Hkv, D = 4, 2, 16
+    parent = _random_parent(rng, n)
+    q = _rand(rng, n, Hq, D)
+    K = _rand(rng, Hkv, ctx + n, D)
+    V = _rand(rng, Hkv, ctx + n, D)
+    out, lse = oracle.verify_attention_seq(q, K, V, ctx, parent, 0.3, window=W)
+    lo = max(0, ctx + n - W)
+    ref, ref_lse = oracle.verify_attention_seq(q, K[:, lo:], V[:, lo:], ctx - lo, parent, 0.3)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-13)
+    for i in range(n):
+        rows = list(range(lo, ctx)) + [ctx + j for j in _path(parent, i)]
+        r = _sdpa(q[i][:, None, :], K[:, rows], V[:, rows], 0.3, enable_gqa=True)
+        np.testing.assert_allclose(out[i], r[:, 0, :], rtol=1e-11, atol=1e-12)
+
+
+def test_window_special_cases():
+    rng = np.random.default_rng(9)
+    n, ctx = 5, 30
+    parent = _random_parent(rng, n)
+    q = _rand(rng, n, 2, 8)
+    K = _rand(rng, 1, ctx + n, 8)
+    V = _rand(rng, 1, ctx + n, 8)
+    full, _ = oracle.verify_attention_seq(q, K, V, ctx, parent, 0.5)
+    for W in (ctx + n, ctx + n + 100):                  # a window over everything changes nothing
+        w, _ = oracle.verify_attention_seq(q, K, V, ctx, parent, 0.5, window=W)
+        np.testing.assert_array_equal(w, full)
+    # W = N: the cache drops out, every row sees its root path only
+    w, _ = oracle.verify_attention_seq(q, K, V, ctx, parent, 0.5, window=n)
+    only, _ = oracle.verify_attention_seq(q, K[:, ctx:], V[:, ctx:], 0, parent, 0.5)
+    np.testing.assert_allclose(w, only, rtol=1e-12, atol=1e-13)
+    with pytest.raises(ValueError):
+        oracle.verify_mask(parent, ctx, window=n - 1)
