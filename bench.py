@@ -44,9 +44,12 @@ def kv_bytes_per_position(cfg):
     return 2 * (D // 2 + (D // 32) * 2)          # 4-bit codes + fp16 scales, K and V
 
 
-def attn_algorithmic_bytes(cfg, ctx_lens):
+def attn_algorithmic_bytes(cfg, ctx_lens, window=0):
     qb = 4 if cfg.q_dtype == "f32" else 2
-    rows = int(np.sum(ctx_lens + cfg.n_nodes))
+    lens = ctx_lens + cfg.n_nodes
+    if window:
+        lens = np.minimum(lens, window)
+    rows = int(np.sum(lens))
     kv = rows * cfg.n_kv_heads * kv_bytes_per_position(cfg)
     q_out = 2 * cfg.batch * cfg.n_nodes * cfg.n_q_heads * cfg.head_dim * qb
     lse = cfg.batch * cfg.n_nodes * cfg.n_q_heads * 4
@@ -120,6 +123,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate-bytes", type=float, default=1.1 * 2 ** 30)
     ap.add_argument("--target-wgs", type=int, default=0, help="attention grid target (0: library default)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding-window attention over the last W key rows (0: the whole key range)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run 5 device-to-device copies of BYTES bytes (reference kernel for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -187,12 +192,14 @@ def main():
     path = torch.empty((B, N), dtype=torch.int32, device=dev)
     tok = torch.empty((B, N), dtype=torch.int32, device=dev)
     new_lens = torch.empty(B, dtype=torch.int32, device=dev)
-    ws_a = torch.empty(sv.verify_attn_workspace_size(kvs[0], B, N, Hq, max_ctx), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(sv.verify_attn_workspace_size(kvs[0], B, N, Hq, max_ctx, window=args.window),
+                       dtype=torch.uint8, device=dev)
     ws_g = torch.zeros(sv.greedy_accept_workspace_size(B, N, cfg.vocab), dtype=torch.uint8, device=dev)
 
     def attn(i):
         c, kv = copies[i % n_copies], kvs[i % n_copies]
-        sv.verify_attn(kv, c["q"], ctx, parent, max_ctx, out=outs[i & 1], lse=lse, workspace=ws_a)
+        sv.verify_attn(kv, c["q"], ctx, parent, max_ctx, out=outs[i & 1], lse=lse, workspace=ws_a,
+                       window=args.window)
 
     def accept(i):
         sv.greedy_accept(copies[i % n_copies]["logits"], drafts, parent, workspace=ws_g,
@@ -265,7 +272,7 @@ def main():
     ms_per_step = total_ms / args.steps
     drafts_per_step = B * (N - 1)
     value = drafts_per_step / (ms_per_step / 1e3)
-    attn_bytes = attn_algorithmic_bytes(cfg, case.ctx_lens)
+    attn_bytes = attn_algorithmic_bytes(cfg, case.ctx_lens, args.window)
     attn_us = float(np.mean(attn_ms) * 1e3)
     achieved = attn_bytes / (attn_us * 1e-6) / 1e9
     rec = {
@@ -285,10 +292,10 @@ def main():
                    "head_dim": D, "n_nodes": N, "tree": cfg.tree, "kv": cfg.kv_dtype,
                    "kv_layout": "paged16" if cfg.paged else "contiguous",
                    "ctx": int(cfg.ctx) if not cfg.ctx_hi else [int(cfg.ctx), int(cfg.ctx_hi)],
-                   "vocab": cfg.vocab, "rotation_copies": n_copies},
+                   "vocab": cfg.vocab, "rotation_copies": n_copies, "window": args.window},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(cfg.name, attn_bytes),
+                     "traffic": None if args.window else measured_traffic(cfg.name, attn_bytes),
                      "kernel": "sv_verify_attn (split + merge kernels)",
                      "algorithmic_bytes": int(attn_bytes)},
         "breakdown_us": {"verify_attn": round(attn_us, 2), "greedy_accept": round(accept_us, 2),

@@ -64,6 +64,11 @@ lib.sv_verify_attn_workspace_size.argtypes = [ctypes.POINTER(_KvDesc), _I, _I, _
 lib.sv_verify_attn.restype = _I
 lib.sv_verify_attn.argtypes = [ctypes.POINTER(_KvDesc), _I, _I, _I, _P, _I, _P, _I, _P,
                                ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]
+lib.sv_verify_attn_window_workspace_size.restype = ctypes.c_size_t
+lib.sv_verify_attn_window_workspace_size.argtypes = [ctypes.POINTER(_KvDesc), _I, _I, _I, _I, _I]
+lib.sv_verify_attn_window.restype = _I
+lib.sv_verify_attn_window.argtypes = [ctypes.POINTER(_KvDesc), _I, _I, _I, _P, _I, _P, _I, _P,
+                                      ctypes.c_float, _I, _P, _P, _P, ctypes.c_size_t, _P]
 lib.sv_greedy_accept_workspace_size.restype = ctypes.c_size_t
 lib.sv_greedy_accept_workspace_size.argtypes = [_I, _I, _I]
 lib.sv_greedy_accept.restype = _I
@@ -211,16 +216,22 @@ def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
     return t
 
 
-def verify_attn_workspace_size(kv: KVCache, batch: int, n_nodes: int, n_q_heads: int, max_ctx: int) -> int:
+def verify_attn_workspace_size(kv: KVCache, batch: int, n_nodes: int, n_q_heads: int, max_ctx: int,
+                               window: int = 0) -> int:
     d = kv.desc()
+    if window:
+        return int(lib.sv_verify_attn_window_workspace_size(ctypes.byref(d), batch, n_nodes, n_q_heads, max_ctx,
+                                                            window))
     return int(lib.sv_verify_attn_workspace_size(ctypes.byref(d), batch, n_nodes, n_q_heads, max_ctx))
 
 
 def verify_attn(kv: KVCache, q: torch.Tensor, ctx_lens: torch.Tensor, parent: torch.Tensor,
                 max_ctx: int, sm_scale: float = 0.0, out: Optional[torch.Tensor] = None,
                 lse: Optional[torch.Tensor] = None, want_lse: bool = True,
-                workspace: Optional[torch.Tensor] = None, layer: int = 0):
-    """Masked GQA attention of the verify rows.  ``q`` ``[B, N, Hq, D]``."""
+                workspace: Optional[torch.Tensor] = None, layer: int = 0, window: int = 0):
+    """Masked GQA attention of the verify rows.  ``q`` ``[B, N, Hq, D]``.
+
+    ``window`` > 0: only the last ``window`` key rows of each sequence."""
     if q.dim() != 4 or not q.is_contiguous() or not q.is_cuda:
         raise ValueError("q must be a contiguous [B, N, Hq, D] device tensor")
     B, N, Hq, D = q.shape
@@ -231,14 +242,21 @@ def verify_attn(kv: KVCache, q: torch.Tensor, ctx_lens: torch.Tensor, parent: to
     if lse is None and want_lse:
         lse = torch.empty((B, N, Hq), dtype=torch.float32, device=q.device)
     d = kv.desc(layer)
-    need = int(lib.sv_verify_attn_workspace_size(ctypes.byref(d), B, N, Hq, int(max_ctx)))
+    if window:
+        need = int(lib.sv_verify_attn_window_workspace_size(ctypes.byref(d), B, N, Hq, int(max_ctx), int(window)))
+    else:
+        need = int(lib.sv_verify_attn_workspace_size(ctypes.byref(d), B, N, Hq, int(max_ctx)))
     if workspace is None:
         workspace = _workspace("attn", q.device, need, zero=False)
-    rc = lib.sv_verify_attn(ctypes.byref(d), B, N, Hq, _ptr(ctx_lens), int(max_ctx), _ptr(q),
-                            _dtype_code(q), _ptr(parent), float(sm_scale), _ptr(out), _ptr(lse),
-                            _ptr(workspace), workspace.numel() * workspace.element_size(),
-                            _stream(q.device))
-    _check(rc, "sv_verify_attn")
+    args = (ctypes.byref(d), B, N, Hq, _ptr(ctx_lens), int(max_ctx), _ptr(q), _dtype_code(q), _ptr(parent),
+            float(sm_scale))
+    tail = (_ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device))
+    if window:
+        rc = lib.sv_verify_attn_window(*args, int(window), *tail)
+        _check(rc, "sv_verify_attn_window")
+    else:
+        rc = lib.sv_verify_attn(*args, *tail)
+        _check(rc, "sv_verify_attn")
     return out, lse
 
 

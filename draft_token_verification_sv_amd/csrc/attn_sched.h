@@ -41,7 +41,7 @@ struct AttnUnit {
 struct SchedLds {
     double tot[4];
     uint32_t red[2][4];
-    int pick[5];                  // b, first unit, splits, L, split length of the chosen sequence
+    int pick[6];                  // b, first unit, splits, L, split length, ctx + N of the chosen sequence
 };
 
 // Inclusive prefix sum over the 64 lanes of a wavefront with DPP moves (row
@@ -136,18 +136,26 @@ __device__ __forceinline__ uint32_t split_search(int lo, int hi, int qm, long lo
 
 // Records sequence b (length L, ns splits from unit `first`) as the owner of
 // unit u when u falls in its range.
-__device__ __forceinline__ void sched_pick(SchedLds &sm, int u, int b, uint32_t L, uint32_t ns, long long first,
-                                           int H, int qm) {
+__device__ __forceinline__ void sched_pick(SchedLds &sm, int u, int b, uint32_t L, uint32_t full, uint32_t ns,
+                                           long long first, int H, int qm) {
     if (ns > 0 && u >= first && u < first + (long long)H * ns) {
         sm.pick[0] = b;
         sm.pick[1] = (int)first;
         sm.pick[2] = (int)ns;
         sm.pick[3] = (int)L;
+        sm.pick[5] = (int)full;
         // the sequence's own length: its ns splits made as even as the
         // quantum allows (<= sl, so the unit count is unchanged)
         const uint32_t even = (L + ns - 1u) / ns;
         sm.pick[4] = (int)((even + (uint32_t)qm) & ~(uint32_t)qm);
     }
+}
+
+// Length of the key range that sequence b's units cover: ctx + N, or its last
+// `window` rows.
+__device__ __forceinline__ uint32_t key_range(const AttnParams &p, int ctx) {
+    const int L = ctx + p.N;
+    return (uint32_t)(p.window > 0 && L > p.window ? p.window : L);
 }
 
 // Decodes unit u.  Must be called by all 256 threads of the block (the dynamic
@@ -163,7 +171,8 @@ __device__ __forceinline__ bool attn_unit(const AttnParams &p, int u, bool recor
         w.b = bh / p.Hkv;
         w.ctx = clamp_ctx(p.ctx_lens[w.b], p.max_ctx);
         const int L = w.ctx + p.N;
-        w.p0 = w.s * p.split_len;
+        const int lo = L - (int)key_range(p, w.ctx);    // first key row (0 without a window)
+        w.p0 = lo + w.s * p.split_len;
         if (w.p0 >= L) return false;
         w.p1 = min(w.p0 + p.split_len, L);
         w.part = u;
@@ -178,7 +187,8 @@ __device__ __forceinline__ bool attn_unit(const AttnParams &p, int u, bool recor
         // one sequence per lane of wavefront 0: every reduction is a DPP scan,
         // no barrier until the result is published
         if (wave == 0) {
-            const uint32_t Lb = lane < p.B ? (uint32_t)(clamp_ctx(p.ctx_lens[lane], p.max_ctx) + p.N) : 0u;
+            const int cb = lane < p.B ? clamp_ctx(p.ctx_lens[lane], p.max_ctx) : 0;
+            const uint32_t Lb = lane < p.B ? key_range(p, cb) : 0u;
             const double tot = wave_sum_f64((double)Lb);
             int lo, hi;
             split_bounds(p, tot, lo, hi);
@@ -189,17 +199,19 @@ __device__ __forceinline__ bool attn_unit(const AttnParams &p, int u, bool recor
             const uint32_t ns = (Lb + sl - 1u) / sl;
             const uint32_t before = wave_scan_u32(ns) - ns;
             if (lane == 0) sm.pick[0] = -1;           // same wavefront: ordered before the pick
-            sched_pick(sm, u, lane, Lb, ns, (long long)H * before, H, qm);
+            sched_pick(sm, u, lane, Lb, (uint32_t)(cb + p.N), ns, (long long)H * before, H, qm);
         }
         __syncthreads();
     } else {
         const int rounds = (p.B + 255) >> 8;         // uniform, <= kSchedRounds
-        uint32_t Lr[kSchedRounds];
+        uint32_t Lr[kSchedRounds], Fr[kSchedRounds];
         double tl = 0.0;
 #pragma unroll
         for (int k = 0; k < kSchedRounds; ++k) {
             const int b = 256 * k + tid;
-            Lr[k] = b < p.B ? (uint32_t)(clamp_ctx(p.ctx_lens[b], p.max_ctx) + p.N) : 0u;
+            const int cb = b < p.B ? clamp_ctx(p.ctx_lens[b], p.max_ctx) : 0;
+            Lr[k] = b < p.B ? key_range(p, cb) : 0u;
+            Fr[k] = (uint32_t)(cb + p.N);
             tl += (double)Lr[k];
         }
         tl = wave_sum_f64(tl);
@@ -236,7 +248,7 @@ __device__ __forceinline__ bool attn_unit(const AttnParams &p, int u, bool recor
                 all += t;
             }
             par ^= 1;
-            sched_pick(sm, u, 256 * k + tid, Lr[k], ns, (long long)H * before, H, qm);
+            sched_pick(sm, u, 256 * k + tid, Lr[k], Fr[k], ns, (long long)H * before, H, qm);
             first += all;
         }
         __syncthreads();
@@ -246,10 +258,10 @@ __device__ __forceinline__ bool attn_unit(const AttnParams &p, int u, bool recor
     const int rel = u - sm.pick[1];
     w.kvh = rel / sm.pick[2];
     w.s = rel % sm.pick[2];
-    const int L = sm.pick[3], slb = sm.pick[4];
-    w.ctx = L - p.N;
-    w.p0 = w.s * slb;
-    w.p1 = min(w.p0 + slb, L);
+    const int L = sm.pick[3], slb = sm.pick[4], full = sm.pick[5];
+    w.ctx = full - p.N;
+    w.p0 = (full - L) + w.s * slb;                     // the key range starts at full - L
+    w.p1 = min(w.p0 + slb, full);
     w.part = u;
     if (record && rel == 0 && tid == 0) p.seq_tab[w.b] = make_int4(sm.pick[1], sm.pick[2], slb, 0);
     return true;

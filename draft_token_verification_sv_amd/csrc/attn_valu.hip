@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
     } else {
         base = ((int64_t)b * p.Hkv + kvh) * p.n_splits;
         ns_cap = p.n_splits;
-        const int L = clamp_ctx(p.ctx_lens[b], p.max_ctx) + p.N;
+        const int L = (int)key_range(p, clamp_ctx(p.ctx_lens[b], p.max_ctx));
         ns = min(p.n_splits, (L + p.split_len - 1) / p.split_len);
     }
     const float *op = p.part_o + (base * p.R + r) * D + 4 * c;

@@ -95,11 +95,12 @@ struct AttnPlan {
 //                                     other 4-bit KV -> register-staged kernel
 //   otherwise                         vector-ALU kernel
 AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int Hkv, int max_ctx,
-                   int page_size) {
+                   int page_size, int window) {
     AttnPlan pl{};
     const int G = Hq / Hkv;
     const int R = G * N;
-    const int64_t L = (int64_t)max_ctx + N;
+    // the key range of the longest sequence (its last `window` rows with a window)
+    const int64_t L = window > 0 ? std::min<int64_t>((int64_t)max_ctx + N, window) : (int64_t)max_ctx + N;
     const bool mfma = (q_dtype == SV_BF16) && (kv_dtype == SV_BF16 || kv_dtype == SV_Q4) && R >= 16;
     // the pipelined kernel takes bf16 caches of any head dim and 4-bit caches of
     // head dim 256; other 4-bit caches go to the register-staged kernel
@@ -280,23 +281,26 @@ int sv_set_option(int option, int value) {
     return SV_EINVAL;
 }
 
-size_t sv_verify_attn_workspace_size(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
-                                     int max_ctx) {
+}  // extern "C"
+
+namespace {
+
+size_t attn_workspace_size(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads, int max_ctx, int window) {
     if (check_attn_shape(kv, batch, n_nodes, n_q_heads, max_ctx) != SV_OK) return 0;
+    if (window < 0 || (window > 0 && window < n_nodes)) return 0;
     const AttnPlan pl = plan_attn(kv->dtype, SV_BF16, kv->head_dim, batch, n_nodes, n_q_heads,
-                                  kv->n_kv_heads, max_ctx, kv->page_size);
+                                  kv->n_kv_heads, max_ctx, kv->page_size, window);
     const AttnPlan pf = plan_attn(kv->dtype, SV_F32, kv->head_dim, batch, n_nodes, n_q_heads,
-                                  kv->n_kv_heads, max_ctx, kv->page_size);
+                                  kv->n_kv_heads, max_ctx, kv->page_size, window);
     return std::max(pl.ws_bytes, pf.ws_bytes);
 }
 
-int sv_verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
-                   const int32_t *ctx_lens, int max_ctx,
-                   const void *q, int q_dtype, const int32_t *parent, float sm_scale,
-                   void *out, float *lse,
-                   void *workspace, size_t workspace_bytes, void *stream) {
+int verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads, const int32_t *ctx_lens, int max_ctx,
+                const void *q, int q_dtype, const int32_t *parent, float sm_scale, int window, void *out, float *lse,
+                void *workspace, size_t workspace_bytes, void *stream) {
     int rc = check_attn_shape(kv, batch, n_nodes, n_q_heads, max_ctx);
     if (rc != SV_OK) return rc;
+    if (window < 0 || (window > 0 && window < n_nodes)) return SV_EINVAL;
     if (q == nullptr || out == nullptr || ctx_lens == nullptr || parent == nullptr) return SV_EINVAL;
     if (q_dtype != SV_F32 && q_dtype != SV_BF16) return SV_EINVAL;
     if (!aligned(q, 16) || !aligned(out, 16)) return SV_EINVAL;
@@ -304,7 +308,7 @@ int sv_verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
     if (q_dtype == SV_BF16 && kv->dtype == SV_F32) return SV_EUNSUPPORTED;
     const int D = kv->head_dim;
     const AttnPlan pl = plan_attn(kv->dtype, q_dtype, D, batch, n_nodes, n_q_heads, kv->n_kv_heads, max_ctx,
-                                  kv->page_size);
+                                  kv->page_size, window);
     if (pl.dyn ? (batch > kSchedMaxBatch || pl.split_max < 0) : pl.n_splits > kMaxSplits)
         return SV_EUNSUPPORTED;
     if (workspace == nullptr || workspace_bytes < pl.ws_bytes) return SV_EWORKSPACE;
@@ -327,6 +331,7 @@ int sv_verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
     p.G = n_q_heads / kv->n_kv_heads;
     p.R = p.G * n_nodes;
     p.max_ctx = max_ctx;
+    p.window = window;
     p.n_splits = pl.n_splits;
     p.split_len = pl.split_len;
     p.dyn = pl.dyn;
@@ -354,6 +359,38 @@ int sv_verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
     e = launch_attn_merge(p, D, st);
     if (e != hipSuccess) return hip_fail(e);
     return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sv_verify_attn_workspace_size(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
+                                     int max_ctx) {
+    return attn_workspace_size(kv, batch, n_nodes, n_q_heads, max_ctx, 0);
+}
+
+int sv_verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
+                   const int32_t *ctx_lens, int max_ctx,
+                   const void *q, int q_dtype, const int32_t *parent, float sm_scale,
+                   void *out, float *lse,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+    return verify_attn(kv, batch, n_nodes, n_q_heads, ctx_lens, max_ctx, q, q_dtype, parent, sm_scale, 0, out, lse,
+                       workspace, workspace_bytes, stream);
+}
+
+size_t sv_verify_attn_window_workspace_size(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
+                                            int max_ctx, int window) {
+    return attn_workspace_size(kv, batch, n_nodes, n_q_heads, max_ctx, window);
+}
+
+int sv_verify_attn_window(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
+                          const int32_t *ctx_lens, int max_ctx,
+                          const void *q, int q_dtype, const int32_t *parent, float sm_scale, int window,
+                          void *out, float *lse,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    return verify_attn(kv, batch, n_nodes, n_q_heads, ctx_lens, max_ctx, q, q_dtype, parent, sm_scale, window, out,
+                       lse, workspace, workspace_bytes, stream);
 }
 
 size_t sv_greedy_accept_workspace_size(int batch, int n_nodes, int vocab) {

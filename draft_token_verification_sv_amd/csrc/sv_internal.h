@@ -42,6 +42,7 @@ struct AttnParams {
     float scale_log2;             // sm_scale * log2(e)
     int q_f32;                    // 1: q/out are fp32, 0: bf16
     int part_nt;                  // 1: streaming (non-temporal) stores for the partial O
+    int window;                   // > 0: only the last `window` key rows of each sequence
 };
 
 struct CompactParams {

@@ -13,7 +13,8 @@
  *                     the accepted path remains;
  *   sv_greedy_accept_compact  the last two in one launch;
  *   sv_kv_append      the verify block's K/V rows written into the cache
- *                     (quantised at write time for a 4-bit cache).
+ *                     (quantised at write time for a 4-bit cache);
+ *   sv_verify_attn_window  the attention over a sliding window of keys.
  *
  * Sources (web pages on speculative decoding; citations name page and section):
  *   [DFN]  "Making Qwen3.5-27B token generation 6x faster on one RTX 3090"
@@ -142,6 +143,24 @@ int sv_verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
                    const void *q, int q_dtype, const int32_t *parent, float sm_scale,
                    void *out, float *lse,
                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sv_verify_attn_window -- sv_verify_attn over a sliding window [DFN, the
+ * 60K-context addendum: flash attention over only the most recent 2,048 KV
+ * positions instead of the whole context].  The key range of sequence b is
+ * cut to its last `window` rows, [max(0, ctx_b + N - window), ctx_b + N), for
+ * every verify row of the block alike; the tree mask applies as before.
+ * N <= window (the draft rows always stay inside); window = 0 is
+ * sv_verify_attn.  Anything else as sv_verify_attn, with the workspace sized
+ * by sv_verify_attn_window_workspace_size (0 for invalid arguments).
+ */
+size_t sv_verify_attn_window_workspace_size(const sv_kv_cache *kv, int batch, int n_nodes,
+                                            int n_q_heads, int max_ctx, int window);
+int sv_verify_attn_window(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
+                          const int32_t *ctx_lens, int max_ctx,
+                          const void *q, int q_dtype, const int32_t *parent, float sm_scale, int window,
+                          void *out, float *lse,
+                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * sv_greedy_accept -- greedy acceptance [DFN "Architecture": greedy verify;

@@ -162,6 +162,22 @@ def test_kv_append_checks(lib):
     assert call(d=kv(capacity=4100)) == -1                   # 4096 + 8 rows do not fit
 
 
+def test_window_checks(lib):
+    lib.sv_verify_attn_window_workspace_size.restype = ctypes.c_size_t
+    d = kv()
+    full = lib.sv_verify_attn_workspace_size(ctypes.byref(d), 1, 8, 24, 4096)
+    assert lib.sv_verify_attn_window_workspace_size(ctypes.byref(d), 1, 8, 24, 4096, 0) == full
+    assert lib.sv_verify_attn_window_workspace_size(ctypes.byref(d), 1, 8, 24, 4096, 2048) > 0
+    assert lib.sv_verify_attn_window_workspace_size(ctypes.byref(d), 1, 8, 24, 4096, 7) == 0   # < N
+    assert lib.sv_verify_attn_window_workspace_size(ctypes.byref(d), 1, 8, 24, 4096, -1) == 0
+    P = ctypes.c_void_p(FAKE)
+
+    def call(w):
+        return lib.sv_verify_attn_window(ctypes.byref(d), 1, 8, 24, P, 4096, P, 1, P, ctypes.c_float(0.0), w,
+                                         P, None, P, ctypes.c_size_t(1 << 30), None)
+    assert call(7) == -1 and call(-5) == -1
+
+
 def test_options(lib):
     prev = lib.sv_set_option(1, 300)
     assert prev == 0

@@ -158,6 +158,25 @@ def test_attention_position_groups(sv, pg):
     check_attention(case, out, lse)
 
 
+WINDOW_CASES = [("C1 tiny fp32 chain", [4, 100, 1000]), ("C2 ctx1000 peaked", [8, 100, 517, 5000]),
+                ("C3 tree22 ctx500", [22, 64, 300]), ("C4 q4 ctx700", [16, 200]),
+                ("C5 paged b8", [4, 50, 600]), ("C5 paged b8 peaked", [4, 137])]
+
+
+@pytest.mark.parametrize("label,windows", WINDOW_CASES, ids=[w[0] for w in WINDOW_CASES])
+def test_attention_window(sv, label, windows):
+    """Sliding window over the key range against the oracle's windowed mask
+    (windows from N, where the cache drops out, to past the whole range)."""
+    cfg, kw = [(c, k) for (l, c, k) in ATTN_CASES if l == label][0]
+    case = workloads.make_case(cfg, seed=6, **kw)
+    dc = DeviceCase(case)
+    for w in windows:
+        say(f"[attn window] {label} W={w}")
+        out, lse = dc.attn(window=w)
+        torch.cuda.synchronize()
+        check_attention(case, out, lse, ref=oracle.verify_attention(case, window=w))
+
+
 OCC_CASES = ["C2 ctx333", "C2 ctx1000 peaked", "C3 tree22 ctx16 peaked", "C5 paged b8", "C5 paged b8 peaked"]
 
 
