@@ -107,3 +107,47 @@ def greedy_accept(logits64, draft_ids, parent):
             am[b, i] = argmax_first(logits64[b, i])
         acc[b], path[b], tok[b] = accept_walk(am[b], draft_ids[b], parent[b])
     return am, acc, path, tok
+
+
+# ----------------------------------------------------------------------------
+# stochastic verification (temperature sampling)
+# ----------------------------------------------------------------------------
+#
+# The single-RTX-3090 DFlash note plans temperature / top-k sampling in the
+# verify path (section "Next steps": only greedy decoding is wired in).  With
+# a deterministic drafter the lossless form of it samples the target at every
+# node and accepts a draft exactly when it equals the parent's sample:
+# committed tokens are then distributed as autoregressive sampling from the
+# target.  A sample of softmax(l / T) is drawn with the Gumbel-max rule,
+# y = argmax_v (l_v / T + g_v) with g_v independent standard Gumbel noise; the
+# noise is an input (drawn by the caller), and the key is formed in fp32 --
+# the division, then the addition, each rounded to nearest -- so the argmax
+# is decided identically on every implementation.  Ties go to the lowest
+# index, as for the greedy argmax.
+
+
+def sample_row(logits32, gumbel32, temperature) -> int:
+    """Lowest index of the maximum fp32 key l / T + g of one row (numpy's
+    float32 division and addition round each result to nearest)."""
+    l32 = np.asarray(logits32, dtype=np.float32)
+    g32 = np.asarray(gumbel32, dtype=np.float32)
+    keys = (l32 / np.float32(temperature)).astype(np.float32) + g32
+    assert keys.dtype == np.float32
+    return int(np.argmax(keys))            # first occurrence of the maximum
+
+
+def sample_accept(logits32, gumbel32, temperature, draft_ids, parent):
+    """Whole batch.  ``logits32``: float32 ``[B, N, V]`` (exact widening of the
+    stored logits); ``gumbel32``: float32 ``[B, N, V]``.  Returns ``sampled
+    [B, N]``, ``accept_len [B]``, ``path [B, N]``, ``tokens [B, N]`` -- the
+    greedy walk with every row's argmax replaced by its sample."""
+    B, N, _ = logits32.shape
+    ys = np.empty((B, N), dtype=np.int32)
+    acc = np.empty(B, dtype=np.int32)
+    path = np.empty((B, N), dtype=np.int32)
+    tok = np.empty((B, N), dtype=np.int32)
+    for b in range(B):
+        for i in range(N):
+            ys[b, i] = sample_row(logits32[b, i], gumbel32[b, i], temperature)
+        acc[b], path[b], tok[b] = accept_walk(ys[b], draft_ids[b], parent[b])
+    return ys, acc, path, tok
