@@ -216,6 +216,16 @@ def main():
                    workloads.bf16_bits((rng_new.standard_normal((B, N, cfg.n_kv_heads, D)) * 0.5).astype(np.float32)),
                    src_kind) for _ in range(2)]
 
+    # stochastic verification at T = 0.8 with standard Gumbel noise drawn once on the device
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(991)
+    gumbel = -torch.log(-torch.log(torch.rand(base["logits"].shape, generator=gen, device=dev,
+                                              dtype=torch.float32).clamp_(1e-12, 1.0)))
+
+    def sample(i):
+        sv.sample_accept(copies[i % n_copies]["logits"], gumbel, 0.8, drafts, parent, workspace=ws_g,
+                         outputs=(acc, path, tok, None))
+
     def append(i):
         sv.kv_append(kvs[i % n_copies], new_rows[0], new_rows[1], ctx, max_ctx)
 
@@ -265,6 +275,8 @@ def main():
     compact_us = timed(g_cmp) / args.steps * 1e3
     g_ac = capture(accept_compact)
     accept_compact_us = timed(g_ac) / args.steps * 1e3
+    g_smp = capture(sample)
+    sample_us = timed(g_smp) / args.steps * 1e3
     g_app = capture(append)                 # last: it rewrites the draft rows of the rotated caches
     append_us = timed(g_app) / args.steps * 1e3
     attn_ms = np.array([attn_total_ms / args.steps])
@@ -300,7 +312,8 @@ def main():
                      "algorithmic_bytes": int(attn_bytes)},
         "breakdown_us": {"verify_attn": round(attn_us, 2), "greedy_accept": round(accept_us, 2),
                          "kv_compact": round(compact_us, 2), "greedy_accept_compact": round(accept_compact_us, 2),
-                         "kv_append (not in the step)": round(append_us, 2)},
+                         "kv_append (not in the step)": round(append_us, 2),
+                         "sample_accept T=0.8 (not in the step)": round(sample_us, 2)},
         "accepted_tokens_per_step": None,
     }
     a_host = acc.cpu().numpy()

@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "SV_F32", "SV_BF16", "SV_Q4", "SVError", "KVCache", "lib", "library_path",
     "verify_attn", "verify_attn_workspace_size", "greedy_accept", "greedy_accept_workspace_size",
-    "kv_compact", "greedy_accept_compact", "kv_append", "set_option", "SV_OPT_ATTN_TARGET_WGS", "SV_OPT_ARGMAX_CHUNK", "SV_OPT_ATTN_ROWBLOCKS",
+    "kv_compact", "greedy_accept_compact", "kv_append", "sample_accept", "set_option", "SV_OPT_ATTN_TARGET_WGS", "SV_OPT_ARGMAX_CHUNK", "SV_OPT_ATTN_ROWBLOCKS",
     "SV_OPT_ATTN_POSGROUPS", "SV_OPT_ATTN_OCCUPANCY",
 ]
 
@@ -75,6 +75,9 @@ lib.sv_greedy_accept.restype = _I
 lib.sv_greedy_accept.argtypes = [_I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
 lib.sv_kv_compact.restype = _I
 lib.sv_kv_compact.argtypes = [ctypes.POINTER(_KvDesc), _I, _I, _I, _P, _I, _P, _P, _P, _P]
+lib.sv_sample_accept.restype = _I
+lib.sv_sample_accept.argtypes = [_I, _I, _I, _P, _I, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P,
+                                 ctypes.c_size_t, _P]
 lib.sv_kv_append.restype = _I
 lib.sv_kv_append.argtypes = [ctypes.POINTER(_KvDesc), _I, _I, _P, _I, _P, _P, _I, _P]
 lib.sv_greedy_accept_compact.restype = _I
@@ -291,6 +294,39 @@ def greedy_accept(logits: torch.Tensor, draft_ids: torch.Tensor, parent: torch.T
                               workspace.numel() * workspace.element_size(), _stream(dev))
     _check(rc, "sv_greedy_accept")
     return acc, path, tok, am
+
+
+def sample_accept(logits: torch.Tensor, gumbel: torch.Tensor, temperature: float, draft_ids: torch.Tensor,
+                  parent: torch.Tensor, want_samples: bool = True, workspace: Optional[torch.Tensor] = None,
+                  outputs=None):
+    """Stochastic verification at ``temperature`` with the caller's standard
+    Gumbel noise ``gumbel`` (float32, the shape of ``logits``).
+
+    Returns ``(accept_len [B], path [B, N], tokens [B, N], samples [B, N] or None)``.
+    """
+    if logits.dim() != 3 or not logits.is_contiguous() or not logits.is_cuda:
+        raise ValueError("logits must be a contiguous [B, N, V] device tensor")
+    if gumbel.shape != logits.shape or gumbel.dtype != torch.float32 or not gumbel.is_contiguous():
+        raise ValueError("gumbel must be a contiguous float32 tensor shaped like logits")
+    B, N, V = logits.shape
+    _i32(draft_ids, "draft_ids")
+    _i32(parent, "parent")
+    dev = logits.device
+    if outputs is None:
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        path = torch.empty((B, N), dtype=torch.int32, device=dev)
+        tok = torch.empty((B, N), dtype=torch.int32, device=dev)
+        ys = torch.empty((B, N), dtype=torch.int32, device=dev) if want_samples else None
+    else:
+        acc, path, tok, ys = outputs
+    need = int(lib.sv_greedy_accept_workspace_size(B, N, V))
+    if workspace is None:
+        workspace = _workspace("accept", dev, need, zero=True)
+    rc = lib.sv_sample_accept(B, N, V, _ptr(logits), _dtype_code(logits), _ptr(gumbel), float(temperature),
+                              _ptr(draft_ids), _ptr(parent), _ptr(acc), _ptr(path), _ptr(tok), _ptr(ys),
+                              _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(rc, "sv_sample_accept")
+    return acc, path, tok, ys
 
 
 def kv_compact(kv: KVCache, ctx_lens: torch.Tensor, max_ctx: int, path: torch.Tensor,

@@ -124,7 +124,12 @@ __device__ void compact_sequence(const CompactParams &cp, int b, int ctx, const 
     }
 }
 
-template <bool F32, bool VEC, bool COMPACT>
+// SAMPLE: stochastic verification at temperature T -- the row's key for
+// token v is the fp32 sum l_v / T + g_v (Gumbel-max sampling with the given
+// noise g; the division and the addition each round to nearest), its maximum
+// (lowest index on ties) is the row's sample and replaces the argmax in the
+// walk [single-RTX-3090 note, "Next steps": temperature sampling in verify].
+template <bool F32, bool VEC, bool COMPACT, bool SAMPLE>
 __global__ __launch_bounds__(256) void argmax_accept_kernel(AcceptParams p) {
     __shared__ unsigned long long red[4];
     __shared__ int last_s;
@@ -143,50 +148,64 @@ __global__ __launch_bounds__(256) void argmax_accept_kernel(AcceptParams p) {
     constexpr int EPL = F32 ? 4 : 8;                      // elements per 16-byte load
     constexpr int UNR = 8;                                // loads in flight per thread
 
+    const float *grow = SAMPLE ? p.gumbel + (int64_t)row * V : nullptr;
+    // the key value of token index e with logit l (g: its noise when sampling)
+    auto keyv = [&](float l, float g) -> float {
+        if constexpr (SAMPLE) return l / p.temperature + g;
+        else return l;
+    };
     unsigned long long best = 0ull;
     if constexpr (VEC) {
         // full groups of UNR loads, then the rest one load at a time
         const void *base = F32 ? (const void *)((const float *)p.logits + (int64_t)row * V)
                                : (const void *)((const uint16_t *)p.logits + (int64_t)row * V);
-        int64_t e = lo + (int64_t)tid * EPL;
-        for (; e + (int64_t)(UNR - 1) * 256 * EPL < hi; e += (int64_t)UNR * 256 * EPL) {
-            u32x4 v[UNR];
-#pragma unroll
-            for (int k = 0; k < UNR; ++k)
-                v[k] = *(const u32x4 *)((const uint8_t *)base + (e + (int64_t)k * 256 * EPL) * (F32 ? 4 : 2));
-#pragma unroll
-            for (int k = 0; k < UNR; ++k) {
-                const uint32_t i0 = (uint32_t)(e + (int64_t)k * 256 * EPL);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    if constexpr (F32) {
-                        best = umax64(best, make_key(__uint_as_float(v[k][t]), i0 + t));
-                    } else {
-                        best = umax64(best, make_key(bf16_bits_to_f32(v[k][t] & 0xFFFFu), i0 + 2 * t));
-                        best = umax64(best, make_key(bf16_bits_to_f32(v[k][t] >> 16), i0 + 2 * t + 1));
-                    }
-                }
-            }
-        }
-        for (; e < hi; e += 256 * EPL) {
-            const u32x4 v = *(const u32x4 *)((const uint8_t *)base + e * (F32 ? 4 : 2));
+        // EPL consecutive values at e (their noise in gn when sampling)
+        auto consume = [&](const u32x4 &v, const f32x4 (&gn)[2], int64_t e) {
+            const uint32_t i0 = (uint32_t)e;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 if constexpr (F32) {
-                    best = umax64(best, make_key(__uint_as_float(v[t]), (uint32_t)(e + t)));
+                    best = umax64(best, make_key(keyv(__uint_as_float(v[t]), gn[0][t]), i0 + t));
                 } else {
-                    best = umax64(best, make_key(bf16_bits_to_f32(v[t] & 0xFFFFu), (uint32_t)(e + 2 * t)));
-                    best = umax64(best, make_key(bf16_bits_to_f32(v[t] >> 16), (uint32_t)(e + 2 * t + 1)));
+                    best = umax64(best, make_key(keyv(bf16_bits_to_f32(v[t] & 0xFFFFu), gn[(2 * t) / 4][(2 * t) % 4]),
+                                                 i0 + 2 * t));
+                    best = umax64(best, make_key(keyv(bf16_bits_to_f32(v[t] >> 16), gn[(2 * t + 1) / 4][(2 * t + 1) % 4]),
+                                                 i0 + 2 * t + 1));
                 }
             }
+        };
+        auto gload = [&](int64_t e, f32x4 (&gn)[2]) {
+            if constexpr (SAMPLE) {
+                gn[0] = *(const f32x4 *)(grow + e);
+                if constexpr (!F32) gn[1] = *(const f32x4 *)(grow + e + 4);
+            }
+        };
+        int64_t e = lo + (int64_t)tid * EPL;
+        for (; e + (int64_t)(UNR - 1) * 256 * EPL < hi; e += (int64_t)UNR * 256 * EPL) {
+            u32x4 v[UNR];
+            f32x4 gv[UNR][2];
+#pragma unroll
+            for (int k = 0; k < UNR; ++k) {
+                v[k] = *(const u32x4 *)((const uint8_t *)base + (e + (int64_t)k * 256 * EPL) * (F32 ? 4 : 2));
+                gload(e + (int64_t)k * 256 * EPL, gv[k]);
+            }
+#pragma unroll
+            for (int k = 0; k < UNR; ++k) consume(v[k], gv[k], e + (int64_t)k * 256 * EPL);
+        }
+        for (; e < hi; e += 256 * EPL) {
+            const u32x4 v = *(const u32x4 *)((const uint8_t *)base + e * (F32 ? 4 : 2));
+            f32x4 gv[2];
+            gload(e, gv);
+            consume(v, gv, e);
         }
     } else if constexpr (F32) {
         const float *rowp = (const float *)p.logits + (int64_t)row * V;
-        for (int64_t e = lo + tid; e < hi; e += 256) best = umax64(best, make_key(rowp[e], (uint32_t)e));
+        for (int64_t e = lo + tid; e < hi; e += 256)
+            best = umax64(best, make_key(keyv(rowp[e], SAMPLE ? grow[e] : 0.f), (uint32_t)e));
     } else {
         const uint16_t *rowp = (const uint16_t *)p.logits + (int64_t)row * V;
         for (int64_t e = lo + tid; e < hi; e += 256)
-            best = umax64(best, make_key(bf16_bits_to_f32(rowp[e]), (uint32_t)e));
+            best = umax64(best, make_key(keyv(bf16_bits_to_f32(rowp[e]), SAMPLE ? grow[e] : 0.f), (uint32_t)e));
     }
     best = wave_max64(best);
     if ((tid & 63) == 0) red[tid >> 6] = best;
@@ -285,30 +304,28 @@ __global__ __launch_bounds__(256) void argmax_accept_kernel(AcceptParams p) {
     }
 }
 
+template <bool COMPACT, bool SAMPLE>
+void launch_accept_t(const AcceptParams &p, bool vec, int grid, hipStream_t st) {
+    if (p.logits_f32) {
+        if (vec) hipLaunchKernelGGL((argmax_accept_kernel<true, true, COMPACT, SAMPLE>), dim3(grid), dim3(256), 0, st, p);
+        else hipLaunchKernelGGL((argmax_accept_kernel<true, false, COMPACT, SAMPLE>), dim3(grid), dim3(256), 0, st, p);
+    } else {
+        if (vec) hipLaunchKernelGGL((argmax_accept_kernel<false, true, COMPACT, SAMPLE>), dim3(grid), dim3(256), 0, st, p);
+        else hipLaunchKernelGGL((argmax_accept_kernel<false, false, COMPACT, SAMPLE>), dim3(grid), dim3(256), 0, st, p);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_accept(const AcceptParams &p, hipStream_t st) {
     const int grid = p.B * p.N * p.n_chunks;
     const int esize = p.logits_f32 ? 4 : 2;
-    const bool vec = ((uintptr_t)p.logits % 16 == 0) && (((int64_t)p.V * esize) % 16 == 0) &&
-                     ((int64_t)p.chunk * esize) % 16 == 0;
-    if (p.compact) {
-        if (p.logits_f32) {
-            if (vec) hipLaunchKernelGGL((argmax_accept_kernel<true, true, true>), dim3(grid), dim3(256), 0, st, p);
-            else hipLaunchKernelGGL((argmax_accept_kernel<true, false, true>), dim3(grid), dim3(256), 0, st, p);
-        } else {
-            if (vec) hipLaunchKernelGGL((argmax_accept_kernel<false, true, true>), dim3(grid), dim3(256), 0, st, p);
-            else hipLaunchKernelGGL((argmax_accept_kernel<false, false, true>), dim3(grid), dim3(256), 0, st, p);
-        }
-        return hipGetLastError();
-    }
-    if (p.logits_f32) {
-        if (vec) hipLaunchKernelGGL((argmax_accept_kernel<true, true, false>), dim3(grid), dim3(256), 0, st, p);
-        else hipLaunchKernelGGL((argmax_accept_kernel<true, false, false>), dim3(grid), dim3(256), 0, st, p);
-    } else {
-        if (vec) hipLaunchKernelGGL((argmax_accept_kernel<false, true, false>), dim3(grid), dim3(256), 0, st, p);
-        else hipLaunchKernelGGL((argmax_accept_kernel<false, false, false>), dim3(grid), dim3(256), 0, st, p);
-    }
+    bool vec = ((uintptr_t)p.logits % 16 == 0) && (((int64_t)p.V * esize) % 16 == 0) &&
+               ((int64_t)p.chunk * esize) % 16 == 0;
+    if (p.gumbel != nullptr) vec = vec && ((uintptr_t)p.gumbel % 16 == 0) && (p.V % 4 == 0);
+    if (p.compact) launch_accept_t<true, false>(p, vec, grid, st);
+    else if (p.gumbel != nullptr) launch_accept_t<false, true>(p, vec, grid, st);
+    else launch_accept_t<false, false>(p, vec, grid, st);
     return hipGetLastError();
 }
 

@@ -64,6 +64,8 @@ struct AcceptParams {
     int logits_f32;
     int compact;                  // also compact the KV of each sequence (cp; path / accept_len unused)
     CompactParams cp;
+    const float *gumbel;          // [B][N][V] noise: sample at `temperature` instead of the argmax (or null)
+    float temperature;
 };
 
 struct AppendParams {

@@ -14,7 +14,8 @@
  *   sv_greedy_accept_compact  the last two in one launch;
  *   sv_kv_append      the verify block's K/V rows written into the cache
  *                     (quantised at write time for a 4-bit cache);
- *   sv_verify_attn_window  the attention over a sliding window of keys.
+ *   sv_verify_attn_window  the attention over a sliding window of keys;
+ *   sv_sample_accept  stochastic verification at a temperature.
  *
  * Sources (web pages on speculative decoding; citations name page and section):
  *   [DFN]  "Making Qwen3.5-27B token generation 6x faster on one RTX 3090"
@@ -209,6 +210,29 @@ int sv_kv_compact(const sv_kv_cache *kv, int n_layers, int batch, int n_nodes,
                   const int32_t *ctx_lens, int max_ctx,
                   const int32_t *path, const int32_t *accept_len,
                   int32_t *new_lens, void *stream);
+
+/*
+ * sv_sample_accept -- stochastic verification at temperature T [DFN "Next
+ * steps": temperature sampling planned for the verify path].  Every row (b, i)
+ * is sampled instead of maximised: y = the lowest index of the maximum of the
+ * fp32 key  logits[b][i][v] / T + gumbel[b][i][v]  (Gumbel-max sampling of
+ * softmax(logits / T) with the caller's standard-Gumbel noise; the division
+ * and the addition each round to nearest).  The acceptance walk then runs as
+ * in sv_greedy_accept with y in place of the argmax: a draft is accepted iff
+ * it equals its parent's sample, the bonus token is the sample at the last
+ * accepted node.  With a deterministic drafter this commits tokens
+ * distributed as sampling from the target one token at a time.
+ *   gumbel   device float [batch][N][vocab], 4-byte aligned (16-byte aligned
+ *            with vocab % 4 == 0 for the vectorised loads).
+ *   temperature  > 0 and finite.
+ *   sampled  device int32 [batch][N]: y, or NULL.
+ * Other arguments, outputs, workspace and errors as sv_greedy_accept.
+ */
+int sv_sample_accept(int batch, int n_nodes, int vocab,
+                     const void *logits, int logits_dtype, const float *gumbel, float temperature,
+                     const int32_t *draft_ids, const int32_t *parent,
+                     int32_t *accept_len, int32_t *path, int32_t *tokens, int32_t *sampled,
+                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * sv_kv_append -- write the verify block's K/V rows into the cache, quantising

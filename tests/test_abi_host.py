@@ -178,6 +178,17 @@ def test_window_checks(lib):
     assert call(7) == -1 and call(-5) == -1
 
 
+def test_sample_accept_checks(lib):
+    P = ctypes.c_void_p(FAKE)
+
+    def call(T=0.8, g=FAKE, N=8, ws=FAKE):
+        return lib.sv_sample_accept(1, N, 151936, P, 1, ctypes.c_void_p(g), ctypes.c_float(T), P, P, P, P, P,
+                                    None, ctypes.c_void_p(ws), ctypes.c_size_t(1 << 30), None)
+    assert call(T=0.0) == -1 and call(T=-1.0) == -1 and call(T=float("inf")) == -1 and call(T=float("nan")) == -1
+    assert call(g=0) == -1 and call(g=FAKE + 2) == -1
+    assert call(N=0) == -1 and call(ws=0) == -3
+
+
 def test_options(lib):
     prev = lib.sv_set_option(1, 300)
     assert prev == 0

@@ -330,6 +330,43 @@ def test_accept_repeated_calls_and_chunk_sizes(sv):
             sv.set_option(sv.SV_OPT_ARGMAX_CHUNK, prev)
 
 
+SAMPLE_CASES = [
+    ("C2 full vocab T1", _small("C2", ctx=8, vocab=151936), 1.0),
+    ("C3 tree22 T0.7", _small("C3", ctx=8, vocab=151936), 0.7),
+    ("C5 batch8 T1.3", _small("C5", ctx=8, ctx_hi=20, vocab=151936), 1.3),
+    ("odd vocab f32 T2", workloads.Config("oddv", 3, 2, 1, 64, 7, "f32", "f32", "f32", 4099, 8,
+                                          tree="ddtree", draft_rule="tree"), 2.0),
+    ("odd vocab bf16 T0.3", workloads.Config("oddb", 2, 2, 1, 64, 64, "bf16", "bf16", "bf16", 12345, 8,
+                                             tree="ddtree", draft_rule="tree"), 0.3),
+]
+
+
+@pytest.mark.parametrize("label,cfg,T", SAMPLE_CASES, ids=[c[0] for c in SAMPLE_CASES])
+def test_sample_accept(sv, label, cfg, T):
+    """Stochastic verification: samples, accept length, path and tokens equal
+    the oracle's, bit for bit (fp32 keys l / T + g on both sides); drafts are
+    built from the oracle's samples so that long paths get accepted."""
+    say(f"[sample] {label}")
+    rng = np.random.default_rng(41)
+    case = workloads.make_case(cfg, seed=5)
+    lg32 = (oracle.widen_bf16(case.logits) if cfg.logits_dtype == "bf16" else case.logits.astype(np.float64))
+    lg32 = lg32.astype(np.float32)
+    g = (-np.log(-np.log(rng.random(case.logits.shape)))).astype(np.float32)
+    B, N = case.draft_ids.shape
+    ys = np.array([[oracle.sample_row(lg32[b, i], g[b, i], T) for i in range(N)] for b in range(B)])
+    par = np.maximum(case.parent, 0)
+    drafts = np.where(rng.random((B, N)) < 0.8, ys[np.arange(B)[:, None], par], case.draft_ids).astype(np.int32)
+    from sv_harness import dev_tensor
+    acc, path, tok, y = sv.sample_accept(dev_tensor(case.logits, cfg.logits_dtype), dev_tensor(g, "f32"), T,
+                                         dev_tensor(drafts, "i32"), dev_tensor(case.parent, "i32"))
+    torch.cuda.synchronize()
+    r_y, r_acc, r_path, r_tok = oracle.sample_accept(lg32, g, T, drafts, case.parent)
+    np.testing.assert_array_equal(y.cpu().numpy(), r_y)
+    np.testing.assert_array_equal(acc.cpu().numpy(), r_acc)
+    np.testing.assert_array_equal(path.cpu().numpy(), r_path)
+    np.testing.assert_array_equal(tok.cpu().numpy(), r_tok)
+
+
 # ---------------------------------------------------------------------------
 # compaction
 # ---------------------------------------------------------------------------
