@@ -18,7 +18,11 @@ the stored inputs:
   row's Gumbel-max sample at temperature T in place of its argmax);
 * ``compact``: the post-acceptance KV compaction as a snapshot copy;
 * ``append``: writing the verify block's K/V rows into the cache, with the
-  4-bit quantisation at write time.
+  4-bit quantisation at write time;
+* ``recurrent``: the tree-aware recurrent state of the hybrid target's Gated
+  DeltaNet layers: the short causal conv with each node's window along its
+  parent chain, the gated delta rule over the tree keeping every node's
+  state, and the commit of the accepted node's state and conv window.
 
 Sources: the single-RTX-3090 DFlash + DDTree note ("Making Qwen3.5-27B token
 generation 6x faster on one RTX 3090", blog.xiaohack.org): greedy verify and
@@ -40,10 +44,12 @@ from .attention import ancestor_matrix, verify_mask, verify_attention_seq, verif
 from .accept import argmax_first, accept_walk, accept_bruteforce, greedy_accept, sample_row, sample_accept
 from .compact import compact_cache
 from .append import bf16_round, q4_quantise, kv_append
+from .recurrent import tree_parent, root_path, conv_tree, delta_rule_step, delta_net_tree, recurrent_commit
 
 __all__ = [
     "widen_bf16", "widen_fp16", "widen_f32", "q4_decode",
     "ancestor_matrix", "verify_mask", "verify_attention_seq", "verify_attention",
     "argmax_first", "accept_walk", "accept_bruteforce", "greedy_accept", "sample_row", "sample_accept",
     "compact_cache", "bf16_round", "q4_quantise", "kv_append",
+    "tree_parent", "root_path", "conv_tree", "delta_rule_step", "delta_net_tree", "recurrent_commit",
 ]

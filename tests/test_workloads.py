@@ -67,3 +67,20 @@ def test_peaked_variant_makes_mask_matter():
     c = workloads.make_case(cfg, seed=3, variant="peaked")
     out, _ = oracle.verify_attention(c)
     assert np.abs(out).max() > 0.2
+
+
+@pytest.mark.parametrize("name", sorted(workloads.DELTA_CONFIGS))
+def test_delta_cases_are_well_formed(name):
+    cfg = workloads.DELTA_CONFIGS[name]
+    c = workloads.make_delta_case(cfg, 5)
+    B, N = cfg.batch, cfg.n_nodes
+    assert c.x.shape == (B, N, cfg.channels) and c.conv_state.shape == (B, cfg.conv_width - 1, cfg.channels)
+    assert c.q.shape == (B, N, cfg.n_k_heads, cfg.k_dim) and c.v.shape == (B, N, cfg.n_v_heads, cfg.v_dim)
+    assert c.state.shape == (B, cfg.n_v_heads, cfg.v_dim, cfg.k_dim)
+    assert np.all(c.g < 0) and np.all((c.beta > 0) & (c.beta <= 1))
+    for b in range(B):
+        a = int(c.accept_len[b])
+        path = c.path[b]
+        assert path[0] == 0 and np.all(path[a + 1:] == -1)
+        for j in range(1, a + 1):
+            assert c.parent[b, path[j]] == path[j - 1]

@@ -39,7 +39,7 @@ import numpy as np
 __all__ = [
     "Config", "CONFIGS", "Case", "make_case", "bf16_bits", "fp16_bits",
     "q4_encode", "chain_parent", "ddtree_parent", "drafts_from_targets",
-    "small_variant",
+    "small_variant", "DeltaConfig", "DELTA_CONFIGS", "DeltaCase", "make_delta_case",
 ]
 
 
@@ -391,3 +391,107 @@ def make_case(cfg: Config, seed: int, *, variant: str = "", capacity_pad: int = 
                 k=k_all, v=v_all, k_scale=k_sc, v_scale=v_sc, page_table=page_table,
                 parent=parent.astype(np.int32), logits=logits, draft_ids=drafts,
                 target=target, kv_layers=n_layers)
+
+
+# ----------------------------------------------------------------------------
+# recurrent (Gated DeltaNet) layers of the hybrid target
+# ----------------------------------------------------------------------------
+#
+# The single-RTX-3090 note's target has 48 Gated DeltaNet layers of 64 ("Why
+# we ran this test") but gives no sizes for them.  The sizes assumed here: 16
+# key heads and 48 value heads of dimension 128, a conv of width 4 over the q,
+# k and v channels (2 * 16 * 128 + 48 * 128 = 10240 channels).
+# Input recipe: conv inputs and conv state ~ N(0, 1); conv weights
+# ~ N(0, 0.5^2), bias ~ N(0, 0.1^2); q and k rows unit-length (normal draws
+# divided by their norm, as the layer normalises them before the recurrence);
+# v ~ N(0, 1); log decay g ~ -U(0.02, 2) (decay exp(g) in (0.14, 0.98));
+# beta ~ U(0.05, 1); committed state entries ~ N(0, 0.1^2).
+
+@dataclass(frozen=True)
+class DeltaConfig:
+    name: str
+    batch: int
+    n_nodes: int
+    n_k_heads: int
+    n_v_heads: int
+    k_dim: int
+    v_dim: int
+    conv_width: int
+    dtype: str              # "f32" | "bf16": q, k, v, conv inputs, conv state, outputs
+    state_dtype: str        # "f32" | "f16": the per-node states as stored
+    tree: str = "chain"     # "chain" | "ddtree"
+
+    @property
+    def channels(self) -> int:
+        return 2 * self.n_k_heads * self.k_dim + self.n_v_heads * self.v_dim
+
+
+DELTA_CONFIGS = {
+    # tiny fp32 chain (fast on the oracle)
+    "D1": DeltaConfig("deltanet_tiny_f32", 1, 4, 1, 2, 64, 64, 4, "f32", "f32"),
+    # the DDTree budget-22 tree of the attention configuration, one sequence
+    "D2": DeltaConfig("deltanet_ddtree22", 1, 22, 16, 48, 128, 128, 4, "bf16", "f16", tree="ddtree"),
+    # a DFlash block of 16 rows
+    "D3": DeltaConfig("deltanet_block16", 1, 16, 16, 48, 128, 128, 4, "bf16", "f16"),
+    # 8 sequences, 4-row chains each
+    "D4": DeltaConfig("deltanet_batch8", 8, 4, 16, 48, 128, 128, 4, "bf16", "f16"),
+}
+
+
+@dataclass
+class DeltaCase:
+    cfg: DeltaConfig
+    seed: int
+    parent: np.ndarray        # int32 [B][N]
+    x: np.ndarray             # [B][N][C]       conv inputs (float32 or bf16 bits)
+    conv_state: np.ndarray    # [B][K-1][C]     committed conv inputs, oldest first
+    conv_weight: np.ndarray   # float32 [C][K]  (tap K-1 on the token itself)
+    conv_bias: np.ndarray     # float32 [C]
+    q: np.ndarray             # [B][N][Hk][Dk]
+    k: np.ndarray             # [B][N][Hk][Dk]
+    v: np.ndarray             # [B][N][Hv][Dv]
+    g: np.ndarray             # float32 [B][N][Hv]  log decay
+    beta: np.ndarray          # float32 [B][N][Hv]
+    state: np.ndarray         # float32 [B][Hv][Dv][Dk]
+    accept_len: np.ndarray    # int32 [B]  depth of the accepted node
+    path: np.ndarray          # int32 [B][N] its root path, then -1
+
+
+def _unit_rows(rng, shape):
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    return (x / np.sqrt((x * x).sum(axis=-1, keepdims=True))).astype(np.float32)
+
+
+def make_delta_case(cfg: DeltaConfig, seed: int) -> DeltaCase:
+    rng = np.random.default_rng(seed)
+    B, N, Hk, Hv, Dk, Dv, K = (cfg.batch, cfg.n_nodes, cfg.n_k_heads, cfg.n_v_heads,
+                               cfg.k_dim, cfg.v_dim, cfg.conv_width)
+    C = cfg.channels
+    if cfg.tree == "ddtree":
+        parent = np.stack([ddtree_parent(rng, N) for _ in range(B)])
+    else:
+        parent = np.stack([chain_parent(N) for _ in range(B)])
+    x = _store(_normal(rng, (B, N, C), 1.0), cfg.dtype)
+    conv_state = _store(_normal(rng, (B, K - 1, C), 1.0), cfg.dtype)
+    w = _normal(rng, (C, K), 0.5)
+    bias = _normal(rng, (C,), 0.1)
+    q = _store(_unit_rows(rng, (B, N, Hk, Dk)), cfg.dtype)
+    k = _store(_unit_rows(rng, (B, N, Hk, Dk)), cfg.dtype)
+    v = _store(_normal(rng, (B, N, Hv, Dv), 1.0), cfg.dtype)
+    g = (-rng.uniform(0.02, 2.0, size=(B, N, Hv))).astype(np.float32)
+    beta = rng.uniform(0.05, 1.0, size=(B, N, Hv)).astype(np.float32)
+    state = _normal(rng, (B, Hv, Dv, Dk), 0.1)
+    # an accepted node per sequence (its parent chain is the accepted path)
+    accept_len = np.empty(B, dtype=np.int32)
+    path = np.full((B, N), -1, dtype=np.int32)
+    for b in range(B):
+        node = int(rng.integers(0, N))
+        chain = [node]
+        while parent[b, chain[-1]] >= 0:
+            chain.append(int(parent[b, chain[-1]]))
+        chain.reverse()
+        accept_len[b] = len(chain) - 1
+        path[b, :len(chain)] = chain
+    return DeltaCase(cfg=cfg, seed=seed, parent=parent.astype(np.int32), x=x, conv_state=conv_state,
+                     conv_weight=w, conv_bias=bias, q=q, k=k, v=v, g=g, beta=beta, state=state,
+                     accept_len=accept_len, path=path)
