@@ -23,10 +23,11 @@ __all__ = [
     "SV_F32", "SV_BF16", "SV_Q4", "SVError", "KVCache", "lib", "library_path",
     "verify_attn", "verify_attn_workspace_size", "greedy_accept", "greedy_accept_workspace_size",
     "kv_compact", "greedy_accept_compact", "kv_append", "sample_accept", "set_option", "SV_OPT_ATTN_TARGET_WGS", "SV_OPT_ARGMAX_CHUNK", "SV_OPT_ATTN_ROWBLOCKS",
-    "SV_OPT_ATTN_POSGROUPS", "SV_OPT_ATTN_OCCUPANCY",
+    "SV_OPT_ATTN_POSGROUPS", "SV_OPT_ATTN_OCCUPANCY", "SV_F16",
+    "ssm_conv_tree", "gated_delta_net_tree", "recurrent_commit",
 ]
 
-SV_F32, SV_BF16, SV_Q4 = 0, 1, 2
+SV_F32, SV_BF16, SV_Q4, SV_F16 = 0, 1, 2, 3
 SV_OPT_ATTN_TARGET_WGS, SV_OPT_ARGMAX_CHUNK, SV_OPT_ATTN_ROWBLOCKS, SV_OPT_ATTN_POSGROUPS = 1, 2, 3, 4
 SV_OPT_ATTN_OCCUPANCY = 5
 
@@ -83,6 +84,13 @@ lib.sv_kv_append.argtypes = [ctypes.POINTER(_KvDesc), _I, _I, _P, _I, _P, _P, _I
 lib.sv_greedy_accept_compact.restype = _I
 lib.sv_greedy_accept_compact.argtypes = [_I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P,
                                          ctypes.POINTER(_KvDesc), _I, _P, _I, _P, _P, ctypes.c_size_t, _P]
+lib.sv_ssm_conv_tree.restype = _I
+lib.sv_ssm_conv_tree.argtypes = [_I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _I, _P, _P]
+lib.sv_gated_delta_net_tree.restype = _I
+lib.sv_gated_delta_net_tree.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, ctypes.c_int64, ctypes.c_int64, _I,
+                                        _P, _P, _P, _P, ctypes.c_float, _P, _P, _I, _P]
+lib.sv_recurrent_commit.restype = _I
+lib.sv_recurrent_commit.argtypes = [_I, _I, _I, _I, _I, _P, _I, _P, _I, _I, _P, _P, _I, _P, _P, _P]
 lib.sv_error_string.restype = ctypes.c_char_p
 lib.sv_error_string.argtypes = [_I]
 lib.sv_last_hip_error.restype = _I
@@ -398,6 +406,120 @@ def kv_append(kv: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, ctx_lens: t
     rc = lib.sv_kv_append(ctypes.byref(d), B, n, _ptr(ctx_lens), int(max_ctx), _ptr(k_new), _ptr(v_new),
                           _dtype_code(k_new), _stream(k_new.device))
     _check(rc, "sv_kv_append")
+
+
+def _dev(t: torch.Tensor, name: str, dim: int) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dim() != dim:
+        raise ValueError(f"{name} must be a {dim}-d device tensor")
+
+
+def _state_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SV_F32
+    if t.dtype == torch.float16:
+        return SV_F16
+    raise TypeError(f"per-node states must be float32 or float16, not {t.dtype}")
+
+
+def ssm_conv_tree(x: torch.Tensor, conv_state: torch.Tensor, weight: torch.Tensor,
+                  bias: Optional[torch.Tensor] = None, parent: Optional[torch.Tensor] = None,
+                  activation: str = "silu", out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal depthwise conv of the verify block ``x [B, N, C]`` with each node's
+    window along its parent chain (then ``conv_state [B, K-1, C]``); ``weight
+    [C, K]`` fp32, tap K-1 on the node itself; SiLU when ``activation == "silu"``."""
+    _dev(x, "x", 3)
+    _dev(conv_state, "conv_state", 3)
+    _dev(weight, "weight", 2)
+    B, N, C = x.shape
+    K = weight.shape[1]
+    for t, name in ((x, "x"), (conv_state, "conv_state"), (weight, "weight")):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if conv_state.shape != (B, K - 1, C) or conv_state.dtype != x.dtype:
+        raise ValueError("conv_state must be [B, K-1, C] in x's dtype")
+    if weight.dtype != torch.float32 or weight.shape[0] != C:
+        raise ValueError("weight must be float32 [C, K]")
+    if bias is not None and (bias.dtype != torch.float32 or bias.shape != (C,) or not bias.is_contiguous()):
+        raise ValueError("bias must be float32 [C]")
+    if parent is not None:
+        _i32(parent, "parent")
+    if activation not in ("silu", "none"):
+        raise ValueError("activation is 'silu' or 'none'")
+    if out is None:
+        out = torch.empty_like(x)
+    rc = lib.sv_ssm_conv_tree(B, N, C, K, _ptr(x), _ptr(conv_state), _dtype_code(x), _ptr(weight), _ptr(bias),
+                              _ptr(parent), 1 if activation == "silu" else 0, _ptr(out), _stream(x.device))
+    _check(rc, "sv_ssm_conv_tree")
+    return out
+
+
+def _token_stride(t: torch.Tensor, name: str) -> int:
+    """Row stride of a [B, N, H, D] view whose (H, D) block is packed."""
+    _dev(t, name, 4)
+    B, N, H, D = t.shape
+    s = t.stride()
+    if s[3] != 1 or s[2] != D or (B > 1 and s[0] != N * s[1]):
+        raise ValueError(f"{name} must be [B, N, H, D] with packed heads and a uniform token stride")
+    return s[1]
+
+
+def gated_delta_net_tree(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                         state: torch.Tensor, parent: Optional[torch.Tensor] = None, scale: float = 0.0,
+                         state_dtype: torch.dtype = torch.float16, out: Optional[torch.Tensor] = None,
+                         state_nodes: Optional[torch.Tensor] = None):
+    """Gated delta rule over the verify tree: returns ``(out [B, N, Hv, Dv],
+    state_nodes [B, N, Hv, Dv, Dk])``.  ``q``/``k`` ``[B, N, Hk, Dk]`` and ``v``
+    ``[B, N, Hv, Dv]`` (fp32 or bf16; views into one packed buffer are fine),
+    ``g``/``beta`` fp32 ``[B, N, Hv]``, ``state`` fp32 ``[B, Hv, Dv, Dk]``."""
+    sq, sk, sv_ = _token_stride(q, "q"), _token_stride(k, "k"), _token_stride(v, "v")
+    if sq != sk or q.shape != k.shape or q.dtype != k.dtype or v.dtype != q.dtype:
+        raise ValueError("q and k must share shape, token stride and dtype (v the dtype)")
+    B, N, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    if v.shape[:2] != (B, N):
+        raise ValueError("v must be [B, N, Hv, Dv]")
+    for t, name in ((g, "g"), (beta, "beta")):
+        if t.dtype != torch.float32 or t.shape != (B, N, Hv) or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous float32 [B, N, Hv] device tensor")
+    if state.dtype != torch.float32 or state.shape != (B, Hv, Dv, Dk) or not state.is_contiguous():
+        raise ValueError("state must be a contiguous float32 [B, Hv, Dv, Dk] tensor")
+    if parent is not None:
+        _i32(parent, "parent")
+    if out is None:
+        out = torch.empty((B, N, Hv, Dv), dtype=q.dtype, device=q.device)
+    if state_nodes is None:
+        state_nodes = torch.empty((B, N, Hv, Dv, Dk), dtype=state_dtype, device=q.device)
+    if state_nodes.shape != (B, N, Hv, Dv, Dk) or not state_nodes.is_contiguous():
+        raise ValueError("state_nodes must be a contiguous [B, N, Hv, Dv, Dk] tensor")
+    rc = lib.sv_gated_delta_net_tree(B, N, Hk, Hv, Dk, Dv, _ptr(q), _ptr(k), _ptr(v), sq, sv_, _dtype_code(q),
+                                     _ptr(g), _ptr(beta), _ptr(state), _ptr(parent), float(scale), _ptr(out),
+                                     _ptr(state_nodes), _state_code(state_nodes), _stream(q.device))
+    _check(rc, "sv_gated_delta_net_tree")
+    return out, state_nodes
+
+
+def recurrent_commit(state_nodes: torch.Tensor, state: torch.Tensor, x: torch.Tensor, conv_state: torch.Tensor,
+                     path: torch.Tensor, accept_len: torch.Tensor) -> None:
+    """In place: ``state[b] <- state_nodes[b, path[b, a]]`` and ``conv_state[b]`` <-
+    the last K-1 of (conv_state[b], x[b, path[b, 0..a]]), a = accept_len[b]."""
+    _dev(state_nodes, "state_nodes", 5)
+    B, N, Hv, Dv, Dk = state_nodes.shape
+    if state.dtype != torch.float32 or state.shape != (B, Hv, Dv, Dk) or not state.is_contiguous():
+        raise ValueError("state must be a contiguous float32 [B, Hv, Dv, Dk] tensor")
+    _dev(x, "x", 3)
+    _dev(conv_state, "conv_state", 3)
+    C = x.shape[2]
+    if x.shape[:2] != (B, N) or conv_state.shape[0] != B or conv_state.shape[2] != C or conv_state.dtype != x.dtype:
+        raise ValueError("x must be [B, N, C] and conv_state [B, K-1, C] in one dtype")
+    for t, name in ((state_nodes, "state_nodes"), (x, "x"), (conv_state, "conv_state")):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    _i32(path, "path")
+    _i32(accept_len, "accept_len")
+    rc = lib.sv_recurrent_commit(B, N, Hv, Dk, Dv, _ptr(state_nodes), _state_code(state_nodes), _ptr(state), C,
+                                 conv_state.shape[1] + 1, _ptr(x), _ptr(conv_state), _dtype_code(x), _ptr(path),
+                                 _ptr(accept_len), _stream(x.device))
+    _check(rc, "sv_recurrent_commit")
 
 
 def set_option(option: int, value: int) -> int:

@@ -561,4 +561,115 @@ int sv_greedy_accept_compact(int batch, int n_nodes, int vocab,
     return SV_OK;
 }
 
+int sv_ssm_conv_tree(int batch, int n_nodes, int channels, int kernel_width,
+                     const void *x, const void *conv_state, int dtype,
+                     const float *weight, const float *bias, const int32_t *parent,
+                     int activation, void *out, void *stream) {
+    if (batch < 1 || batch > 65535 || n_nodes < 1 || n_nodes > 64) return SV_EINVAL;
+    if (channels < 4 || channels % 4 != 0 || kernel_width < 2 || kernel_width > 4) return SV_EINVAL;
+    if (dtype != SV_F32 && dtype != SV_BF16) return SV_EINVAL;
+    if (activation != 0 && activation != 1) return SV_EINVAL;
+    if (x == nullptr || conv_state == nullptr || weight == nullptr || out == nullptr) return SV_EINVAL;
+    if (!aligned(x, 16) || !aligned(conv_state, 16) || !aligned(out, 16) || !aligned(weight, 16)) return SV_EINVAL;
+    if (bias != nullptr && !aligned(bias, 16)) return SV_EINVAL;
+    if (parent != nullptr && !aligned(parent, 4)) return SV_EINVAL;
+    ConvTreeParams p{};
+    p.x = x;
+    p.conv_state = conv_state;
+    p.w = weight;
+    p.bias = bias;
+    p.parent = parent;
+    p.out = out;
+    p.B = batch;
+    p.N = n_nodes;
+    p.C = channels;
+    p.K = kernel_width;
+    p.silu = activation;
+    const hipError_t e = launch_conv_tree(p, dtype, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return SV_OK;
+}
+
+int sv_gated_delta_net_tree(int batch, int n_nodes, int n_k_heads, int n_v_heads, int k_dim, int v_dim,
+                            const void *q, const void *k, const void *v, int64_t qk_stride, int64_t v_stride,
+                            int dtype, const float *g, const float *beta, const float *state,
+                            const int32_t *parent, float scale, void *out, void *state_nodes, int state_dtype,
+                            void *stream) {
+    if (batch < 1 || batch > 65535 || n_nodes < 1 || n_nodes > 64) return SV_EINVAL;
+    if (n_k_heads < 1 || n_v_heads < 1 || n_v_heads > 65535 || n_v_heads % n_k_heads != 0) return SV_EINVAL;
+    if (k_dim != 64 && k_dim != 128) return SV_EUNSUPPORTED;
+    if (v_dim < 32 || v_dim % 32 != 0 || v_dim > 32 * 65535) return SV_EINVAL;
+    if (dtype != SV_F32 && dtype != SV_BF16) return SV_EINVAL;
+    if (state_dtype != SV_F32 && state_dtype != SV_F16) return SV_EINVAL;
+    if (q == nullptr || k == nullptr || v == nullptr || g == nullptr || beta == nullptr || state == nullptr ||
+        out == nullptr || state_nodes == nullptr)
+        return SV_EINVAL;
+    const int64_t qk_min = (int64_t)n_k_heads * k_dim, v_min = (int64_t)n_v_heads * v_dim;
+    if (qk_stride == 0) qk_stride = qk_min;
+    if (v_stride == 0) v_stride = v_min;
+    if (qk_stride < qk_min || v_stride < v_min || qk_stride % 8 != 0 || v_stride % 8 != 0) return SV_EINVAL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(state, 16) ||
+        !aligned(state_nodes, 16) || !aligned(g, 4) || !aligned(beta, 4) || !aligned(out, 4))
+        return SV_EINVAL;
+    if (parent != nullptr && !aligned(parent, 4)) return SV_EINVAL;
+    if (!isfinite(scale)) return SV_EINVAL;
+    DeltaParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.qk_stride = qk_stride;
+    p.v_stride = v_stride;
+    p.g = g;
+    p.beta = beta;
+    p.state = state;
+    p.parent = parent;
+    p.out = out;
+    p.state_nodes = state_nodes;
+    p.B = batch;
+    p.N = n_nodes;
+    p.Hk = n_k_heads;
+    p.Hv = n_v_heads;
+    p.Dv = v_dim;
+    p.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)k_dim);
+    const hipError_t e = launch_delta_tree(p, dtype, state_dtype, k_dim, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return SV_OK;
+}
+
+int sv_recurrent_commit(int batch, int n_nodes, int n_v_heads, int k_dim, int v_dim,
+                        const void *state_nodes, int state_dtype, float *state,
+                        int channels, int kernel_width, const void *x, void *conv_state, int dtype,
+                        const int32_t *path, const int32_t *accept_len, void *stream) {
+    if (batch < 1 || batch > 65535 || n_nodes < 1 || n_nodes > 64) return SV_EINVAL;
+    if (n_v_heads < 1 || (k_dim != 64 && k_dim != 128) || v_dim < 32 || v_dim % 32 != 0) return SV_EINVAL;
+    if (state_dtype != SV_F32 && state_dtype != SV_F16) return SV_EINVAL;
+    if (channels < 4 || channels % 4 != 0 || kernel_width < 2 || kernel_width > 4) return SV_EINVAL;
+    if (dtype != SV_F32 && dtype != SV_BF16) return SV_EINVAL;
+    if (state_nodes == nullptr || state == nullptr || x == nullptr || conv_state == nullptr || path == nullptr ||
+        accept_len == nullptr)
+        return SV_EINVAL;
+    if (!aligned(state_nodes, 16) || !aligned(state, 16) || !aligned(x, 16) || !aligned(conv_state, 16) ||
+        !aligned(path, 4) || !aligned(accept_len, 4))
+        return SV_EINVAL;
+    const int64_t elems = (int64_t)n_v_heads * v_dim * k_dim;
+    const int64_t blocks = (elems / 8 + 255) / 256;
+    if (blocks + (channels + 1023) / 1024 > (int64_t)INT32_MAX) return SV_EUNSUPPORTED;
+    CommitParams p{};
+    p.state_nodes = state_nodes;
+    p.state = state;
+    p.x = x;
+    p.conv_state = conv_state;
+    p.path = path;
+    p.accept_len = accept_len;
+    p.state_elems = elems;
+    p.B = batch;
+    p.N = n_nodes;
+    p.C = channels;
+    p.K = kernel_width;
+    p.state_blocks = (int)blocks;
+    const hipError_t e = launch_commit(p, state_dtype, dtype, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return SV_OK;
+}
+
 }  // extern "C"

@@ -75,6 +75,39 @@ struct AppendParams {
     int B, n, Hkv, D, max_ctx;
 };
 
+struct ConvTreeParams {
+    const void *x;                // [B][N][C]
+    const void *conv_state;       // [B][K-1][C]
+    const float *w;               // [C][K]
+    const float *bias;            // [C] or nullptr
+    const int32_t *parent;        // [B][N] or nullptr (chains)
+    void *out;                    // [B][N][C]
+    int B, N, C, K, silu;
+};
+
+struct DeltaParams {
+    const void *q, *k, *v;        // token (b, i) rows at (b * N + i) * stride
+    int64_t qk_stride, v_stride;  // elements
+    const float *g, *beta;        // [B][N][Hv]
+    const float *state;           // [B][Hv][Dv][Dk]
+    const int32_t *parent;        // [B][N] or nullptr (chains)
+    void *out;                    // [B][N][Hv][Dv]
+    void *state_nodes;            // [B][N][Hv][Dv][Dk]
+    int B, N, Hk, Hv, Dv;
+    float scale;
+};
+
+struct CommitParams {
+    const void *state_nodes;      // [B][N][Hv][Dv][Dk], fp32 or f16
+    float *state;                 // [B][Hv][Dv][Dk]
+    const void *x;                // [B][N][C]
+    void *conv_state;             // [B][K-1][C]
+    const int32_t *path, *accept_len;
+    int64_t state_elems;          // Hv * Dv * Dk
+    int B, N, C, K;
+    int state_blocks;             // workgroups per sequence on the state copy
+};
+
 // Kernel-side tile sizes (positions staged per iteration) -----------------
 constexpr int kMfmaTileElems = 16384;          // T * D bf16 elements per K (or V) tile
 constexpr int kValuTileElems = 8192;           // T * D fp32 elements per K (or V) tile
@@ -89,5 +122,8 @@ hipError_t launch_attn_merge(const AttnParams &p, int D, hipStream_t s);
 hipError_t launch_accept(const AcceptParams &p, hipStream_t s);
 hipError_t launch_compact(const CompactParams &p, hipStream_t s);
 hipError_t launch_append(const AppendParams &p, int src_dtype, int dst_dtype, hipStream_t s);
+hipError_t launch_conv_tree(const ConvTreeParams &p, int dtype, hipStream_t s);
+hipError_t launch_delta_tree(const DeltaParams &p, int dtype, int state_dtype, int Dk, hipStream_t s);
+hipError_t launch_commit(const CommitParams &p, int state_dtype, int dtype, hipStream_t s);
 
 }  // namespace sv

@@ -15,7 +15,10 @@
  *   sv_kv_append      the verify block's K/V rows written into the cache
  *                     (quantised at write time for a 4-bit cache);
  *   sv_verify_attn_window  the attention over a sliding window of keys;
- *   sv_sample_accept  stochastic verification at a temperature.
+ *   sv_sample_accept  stochastic verification at a temperature;
+ *   sv_ssm_conv_tree, sv_gated_delta_net_tree, sv_recurrent_commit
+ *                     the tree-aware recurrent state of a hybrid target's
+ *                     Gated DeltaNet layers.
  *
  * Sources (web pages on speculative decoding; citations name page and section):
  *   [DFN]  "Making Qwen3.5-27B token generation 6x faster on one RTX 3090"
@@ -71,6 +74,7 @@ extern "C" {
 #define SV_F32  0            /* IEEE binary32                                     */
 #define SV_BF16 1            /* bfloat16                                          */
 #define SV_Q4   2            /* 4-bit KV blocks: see sv_kv_cache                  */
+#define SV_F16  3            /* IEEE binary16 (per-node recurrent states)         */
 
 /*
  * KV cache descriptor (one layer is read by sv_verify_attn; sv_kv_compact walks
@@ -272,6 +276,77 @@ int sv_greedy_accept_compact(int batch, int n_nodes, int vocab,
                              int32_t *accept_len, int32_t *path, int32_t *tokens, int32_t *argmax,
                              const sv_kv_cache *kv, int n_layers, const int32_t *ctx_lens, int max_ctx,
                              int32_t *new_lens, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Recurrent layers of a hybrid target (tree-aware state)
+ * ------------------------------------------------------
+ * [DFN "Why we ran this test"]: 48 of the target's 64 layers are Gated
+ * DeltaNet layers, each keeping a recurrent state beside the KV cache.  [DFN
+ * "Key breakthroughs"]: verifying a tree needs every node's state after its
+ * root path; the conv windows follow parent chains, not the row order, and the
+ * per-node states are written straight into a persistent buffer (optionally
+ * f16) from which the accepted node's state is taken.  The rows are the N
+ * verify rows, parent[] as above (an entry outside [0, i) starts a new path
+ * from the committed state); parent NULL means a chain.
+ */
+
+/*
+ * sv_ssm_conv_tree -- the short causal depthwise convolution, per node.
+ *   out[b][i][c] = act(bias[c] + sum_{m=0}^{K-1} weight[c][K-1-m] * X_m[c])
+ * where X_0 = x[b][i], X_m = x[b][m-th ancestor of i] while the path lasts,
+ * then conv_state[b][K-2], conv_state[b][K-3], ... (the inputs before the
+ * block, oldest first).  act = identity (activation 0) or SiLU (1).
+ * x, out      device [batch][N][channels], dtype SV_F32 or SV_BF16 (out
+ *             rounded to nearest even); out must not overlap x or conv_state.
+ * conv_state  device [batch][kernel_width-1][channels], same dtype.
+ * weight      device float [channels][kernel_width]; bias device float
+ *             [channels] or NULL.  kernel_width 2, 3 or 4; channels a
+ *             multiple of 4; all arrays 16-byte aligned.
+ */
+int sv_ssm_conv_tree(int batch, int n_nodes, int channels, int kernel_width,
+                     const void *x, const void *conv_state, int dtype,
+                     const float *weight, const float *bias, const int32_t *parent,
+                     int activation, void *out, void *stream);
+
+/*
+ * sv_gated_delta_net_tree -- the gated delta rule over the tree, every node's
+ * state persisted.  The rule is that of Gated DeltaNet (Yang, Kautz,
+ * Hatamizadeh, ICLR 2025); per value head h (key head h / (Hv/Hk)) with state
+ * S (v_dim x k_dim, row-major), node i continues from its parent's state (the
+ * committed state S0 at the top of a path):
+ *   a = exp(g), S_i = a S_p + beta (v - a S_p k) k^T,  out_i = scale S_i q.
+ * q, k        device, token (b, i) at element (b*N + i) * qk_stride, key head
+ *             hk at + hk * k_dim; v likewise with v_stride and v_dim (strides
+ *             0 = packed; else >= heads * dim and a multiple of 8, so that q, k,
+ *             v may point into one packed conv output).  dtype SV_F32 or
+ *             SV_BF16; 16-byte aligned.
+ * g, beta     device float [batch][N][n_v_heads] (g the log decay).
+ * state       device float [batch][n_v_heads][v_dim][k_dim]: S0 (read only).
+ * out         device [batch][N][n_v_heads][v_dim] in dtype.
+ * state_nodes device [batch][N][n_v_heads][v_dim][k_dim] in state_dtype
+ *             (SV_F32, or SV_F16 rounded to nearest even): every node's state.
+ * scale <= 0 selects 1/sqrt(k_dim).  k_dim 64 or 128 (else SV_EUNSUPPORTED);
+ * v_dim a multiple of 32.  Arithmetic in fp32.
+ */
+int sv_gated_delta_net_tree(int batch, int n_nodes, int n_k_heads, int n_v_heads, int k_dim, int v_dim,
+                            const void *q, const void *k, const void *v, int64_t qk_stride, int64_t v_stride,
+                            int dtype, const float *g, const float *beta, const float *state,
+                            const int32_t *parent, float scale, void *out, void *state_nodes, int state_dtype,
+                            void *stream);
+
+/*
+ * sv_recurrent_commit -- after acceptance: state[b] <- state_nodes[b][path[b][a]]
+ * (widened to fp32) and conv_state[b] <- the last kernel_width-1 entries of
+ * (conv_state[b], x[b][path[b][0]], ..., x[b][path[b][a]]), a = accept_len[b].
+ * path / accept_len are sv_greedy_accept's outputs (device); a sequence whose
+ * entries are out of range (a outside [0, N-1], path[j] outside [j, N-1] for
+ * j <= a) keeps its state and conv state.  Shapes and dtypes as in the two
+ * calls above (x is the conv input of the block).
+ */
+int sv_recurrent_commit(int batch, int n_nodes, int n_v_heads, int k_dim, int v_dim,
+                        const void *state_nodes, int state_dtype, float *state,
+                        int channels, int kernel_width, const void *x, void *conv_state, int dtype,
+                        const int32_t *path, const int32_t *accept_len, void *stream);
 
 /* Static text for a return code. */
 const char *sv_error_string(int code);

@@ -189,6 +189,33 @@ def test_sample_accept_checks(lib):
     assert call(N=0) == -1 and call(ws=0) == -3
 
 
+def test_recurrent_checks(lib):
+    P = ctypes.c_void_p(FAKE)
+    I64 = ctypes.c_int64
+
+    def conv(B=1, N=22, C=10240, K=4, x=FAKE, dt=1, act=1, bias=None):
+        return lib.sv_ssm_conv_tree(B, N, C, K, ctypes.c_void_p(x), P, dt, P, bias, None, act, P, None)
+    assert conv(N=0) == -1 and conv(N=65) == -1 and conv(B=0) == -1
+    assert conv(C=10) == -1 and conv(K=1) == -1 and conv(K=5) == -1
+    assert conv(dt=2) == -1 and conv(act=2) == -1 and conv(x=0) == -1 and conv(x=FAKE + 8) == -1
+    assert conv(bias=ctypes.c_void_p(FAKE + 4)) == -1
+
+    def delta(N=22, Hk=16, Hv=48, Dk=128, Dv=128, qs=0, vs=0, dt=1, sdt=3, g=FAKE, scale=0.0, q=FAKE):
+        return lib.sv_gated_delta_net_tree(1, N, Hk, Hv, Dk, Dv, ctypes.c_void_p(q), P, P, I64(qs), I64(vs), dt,
+                                           ctypes.c_void_p(g), P, P, None, ctypes.c_float(scale), P, P, sdt, None)
+    assert delta(N=65) == -1 and delta(Hv=40) == -1            # value heads a multiple of key heads
+    assert delta(Dk=256) == -2 and delta(Dk=96) == -2          # key dims 64 and 128
+    assert delta(Dv=48) == -1 and delta(dt=2) == -1 and delta(sdt=1) == -1
+    assert delta(qs=2048 + 4) == -1 and delta(qs=1024) == -1 and delta(vs=6000) == -1
+    assert delta(g=0) == -1 and delta(q=FAKE + 8) == -1 and delta(scale=float("nan")) == -1
+
+    def commit(N=22, K=4, sdt=3, path=FAKE, Dk=128):
+        return lib.sv_recurrent_commit(1, N, 48, Dk, 128, P, sdt, P, 10240, K, P, P, 1, ctypes.c_void_p(path), P,
+                                       None)
+    assert commit(N=0) == -1 and commit(K=5) == -1 and commit(sdt=2) == -1
+    assert commit(path=0) == -1 and commit(Dk=32) == -1
+
+
 def test_options(lib):
     prev = lib.sv_set_option(1, 300)
     assert prev == 0
