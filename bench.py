@@ -113,6 +113,78 @@ def cpu_baseline(cfg_key, seconds):
                       f"compaction) in {dt:.1f} s, fp64 numpy"}
 
 
+def delta_algorithmic_bytes(cfg):
+    """Bytes one sv_gated_delta_net_tree call must move: the committed state read,
+    q, k, v, decay and beta read once, every node's state and output written."""
+    B, N, Hk, Hv, Dk, Dv = cfg.batch, cfg.n_nodes, cfg.n_k_heads, cfg.n_v_heads, cfg.k_dim, cfg.v_dim
+    e = 2 if cfg.dtype == "bf16" else 4
+    se = 2 if cfg.state_dtype == "f16" else 4
+    return (B * Hv * Dv * Dk * 4 + B * N * (2 * Hk * Dk + Hv * Dv) * e + B * N * Hv * 8
+            + B * N * Hv * Dv * e + B * N * Hv * Dv * Dk * se)
+
+
+def recurrent_bench(sv, dev, key, steps, rotate_bytes, capture, timed):
+    """Times the tree-aware recurrent state calls of one Gated DeltaNet layer
+    (conv, tree recurrence with every node's state persisted, commit) with the
+    committed and per-node states rotated over >= rotate_bytes of HBM."""
+    import torch
+    import workloads
+    cfg = workloads.DELTA_CONFIGS[key]
+    c = workloads.make_delta_case(cfg, seed=2)
+    B, N, Hv, Dk, Dv = cfg.batch, cfg.n_nodes, cfg.n_v_heads, cfg.k_dim, cfg.v_dim
+
+    def up(x, kind):
+        x = np.ascontiguousarray(x)
+        if kind == "bf16":
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x).to(dev)
+
+    kind = cfg.dtype
+    x, cs = up(c.x, kind), up(c.conv_state, kind)
+    w, bias = up(c.conv_weight, "f32"), up(c.conv_bias, "f32")
+    q, k, v = up(c.q, kind), up(c.k, kind), up(c.v, kind)
+    g, beta = up(c.g, "f32"), up(c.beta, "f32")
+    parent = up(c.parent, "i32") if cfg.tree != "chain" else None
+    path, alen = up(c.path, "i32"), up(c.accept_len, "i32")
+    sdt = torch.float16 if cfg.state_dtype == "f16" else torch.float32
+    state0 = up(c.state, "f32")
+    per = state0.numel() * 4 + B * N * Hv * Dv * Dk * (2 if sdt == torch.float16 else 4)
+    n_rot = max(1, int(np.ceil(rotate_bytes / per)))
+    states = [state0] + [state0.clone() for _ in range(n_rot - 1)]
+    nodes = [torch.empty((B, N, Hv, Dv, Dk), dtype=sdt, device=dev) for _ in range(n_rot)]
+    conv_out = torch.empty_like(x)
+    d_out = torch.empty((B, N, Hv, Dv), dtype=q.dtype, device=dev)
+    cs_c = cs.clone()
+
+    def conv(i):
+        sv.ssm_conv_tree(x, cs, w, bias, parent, activation="silu", out=conv_out)
+
+    def delta(i):
+        sv.gated_delta_net_tree(q, k, v, g, beta, states[i % n_rot], parent, out=d_out, state_nodes=nodes[i % n_rot])
+
+    def commit(i):
+        sv.recurrent_commit(nodes[i % n_rot], states[(i + 1) % n_rot], x, cs_c, path, alen)
+
+    for i in range(3):
+        conv(i), delta(i), commit(i)
+    torch.cuda.synchronize()
+    conv_us = timed(capture(conv)) / steps * 1e3
+    delta_us = timed(capture(delta)) / steps * 1e3
+    commit_us = timed(capture(commit)) / steps * 1e3
+    nbytes = delta_algorithmic_bytes(cfg)
+    achieved = nbytes / (delta_us * 1e-6) / 1e9
+    return {
+        "workload": f"{cfg.name}: batch {B}, {N} rows ({cfg.tree}), {cfg.n_k_heads} key / {Hv} value heads, "
+                    f"dims {Dk}/{Dv}, conv width {cfg.conv_width}, {cfg.dtype} inputs, {cfg.state_dtype} node states",
+        "breakdown_us": {"ssm_conv_tree": round(conv_us, 2), "gated_delta_net_tree": round(delta_us, 2),
+                         "recurrent_commit": round(commit_us, 2)},
+        "rotation_copies": n_rot,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "sv_gated_delta_net_tree", "algorithmic_bytes": int(nbytes)},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +197,8 @@ def main():
     ap.add_argument("--target-wgs", type=int, default=0, help="attention grid target (0: library default)")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding-window attention over the last W key rows (0: the whole key range)")
+    ap.add_argument("--recurrent", default="D2", choices=["none", "D1", "D2", "D3", "D4"],
+                    help="Gated DeltaNet tree-state workload timed beside the step (none: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run 5 device-to-device copies of BYTES bytes (reference kernel for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -316,6 +390,8 @@ def main():
                          "sample_accept T=0.8 (not in the step)": round(sample_us, 2)},
         "accepted_tokens_per_step": None,
     }
+    if args.recurrent != "none":
+        rec["recurrent"] = recurrent_bench(sv, dev, args.recurrent, args.steps, args.rotate_bytes, capture, timed)
     a_host = acc.cpu().numpy()
     rec["accepted_tokens_per_step"] = int(np.sum(a_host + 1))
     if not args.no_cpu_baseline:

@@ -16,17 +16,19 @@
 //                       the accepted path's last K-1 inputs into the conv state.
 //
 // delta_tree_kernel: one workgroup of 4 waves per (sequence, value head, block
-// of 32 value rows); lane (jr, rg) of a wave owns value row jr and 8*R/8 = R of
-// the key columns, in chunks of VEC contiguous columns spaced 8*VEC apart (so
-// the 8 lanes of a row store whole 128-byte lines of the per-node buffer).  The
-// state never leaves registers between a node and its first child.  Nodes are
+// of 16 value rows); lane (jr, rg) of a wave owns value row jr and R = Dk/16 of
+// the key columns, in chunks of VEC contiguous columns spaced 16*VEC apart (so
+// the 16 lanes of a row store the row's whole span of the per-node buffer), and
+// the row sums are DPP reductions within a 16-lane row.  The state never leaves
+// registers between a node and its first child.  Nodes are
 // visited in depth-first order with the children of each node sorted by
 // subtree size (largest last): a node with two or more children parks its
 // state in an LDS slot that its later children restore; along any root path a
 // slot is live only below a child that is not its parent's largest, so at most
-// floor(log2(N+1)) - 1 slots are ever live.  The order is computed per wave
+// floor(log2(N+1)) - 1 slots are ever live.  The order is computed by one wave
 // with one lane per node (ancestor sets by pointer doubling, subtree sizes,
-// sibling ranks), no host work.
+// sibling ranks) into one word per step, no host work; a step reads the next
+// node's operands and parked state from LDS while it computes.
 #include "device_common.h"
 
 namespace sv {
@@ -41,11 +43,12 @@ __device__ __forceinline__ float dpp_f(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 
-// sum over the 8 lanes 8m .. 8m+7 (result in all 8)
-__device__ __forceinline__ float sum8(float v) {
+// sum over the 16 lanes of a DPP row (result in all 16)
+__device__ __forceinline__ float sum16(float v) {
     v += dpp_f<0xB1>(v);      // quad_perm [1,0,3,2]
     v += dpp_f<0x4E>(v);      // quad_perm [2,3,0,1]
     v += dpp_f<0x141>(v);     // row_half_mirror
+    v += dpp_f<0x140>(v);     // row_mirror
     return v;
 }
 
@@ -69,10 +72,11 @@ __device__ __forceinline__ void store4(void *base, int64_t off, f32x4 v) {
     }
 }
 
+// two fp32 -> packed IEEE halves (lo in bits 0-15), round to nearest even
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-    const uint32_t l = __builtin_bit_cast(uint16_t, (_Float16)lo);   // round to nearest even
-    const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)hi);
-    return l | (h << 16);
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, f16x2_t));
 }
 
 // ---------------------------------------------------------------------------
@@ -133,58 +137,66 @@ struct SlotCount {
     static constexpr int value = NMAX <= 16 ? 3 : (NMAX <= 32 ? 4 : 5);   // floor(log2(NMAX+1)) - 1
 };
 
+template <int DT>
+struct Raw4 {
+    using type = f32x4;                               // fp32: the 4 values
+};
+template <>
+struct Raw4<SV_BF16> {
+    using type = u32x2;                               // bf16: the 4 values' bits
+};
+
+template <int DT>
+__device__ __forceinline__ typename Raw4<DT>::type load_raw4(const void *base, int64_t off) {
+    if constexpr (DT == SV_F32) return *(const f32x4 *)((const float *)base + off);
+    else return *(const u32x2 *)((const uint16_t *)base + off);
+}
+
+__device__ __forceinline__ f32x4 raw_f32(f32x4 r) { return r; }
+__device__ __forceinline__ f32x4 raw_f32(u32x2 u) {
+    return f32x4{bf16_bits_to_f32(u[0] & 0xFFFFu), bf16_bits_to_f32(u[0] >> 16),
+                 bf16_bits_to_f32(u[1] & 0xFFFFu), bf16_bits_to_f32(u[1] >> 16)};
+}
+
 template <int R, int NMAX, bool TREE, int DT, int SDT>
 __global__ __launch_bounds__(256) void delta_tree_kernel(DeltaParams p) {
-    constexpr int DK = 8 * R;
-    constexpr int VEC = SDT == SV_F16 ? 8 : 4;        // contiguous key columns per chunk
-    constexpr int NCH = R / VEC;                      // chunks per lane
+    constexpr int DK = 16 * R;
+    constexpr int VEC = (SDT == SV_F16 && R >= 8) ? 8 : 4;   // contiguous key columns per chunk
+    constexpr int NCH = R / VEC;                             // chunks per lane
     constexpr int NSLOT = TREE ? SlotCount<NMAX>::value : 0;
-    static_assert(R % VEC == 0, "chunking");
+    constexpr int QK_IT = (NMAX * DK / 4 + 255) / 256;
+    constexpr int V_IT = (NMAX * 4 + 255) / 256;
+    static_assert(R % VEC == 0 && R % 4 == 0, "chunking");
+    using Raw = typename Raw4<DT>::type;
 
     __shared__ __attribute__((aligned(16))) float k_s[NMAX * DK];
     __shared__ __attribute__((aligned(16))) float q_s[NMAX * DK];
-    __shared__ float v_s[NMAX * 32];
+    __shared__ __attribute__((aligned(16))) float v_s[NMAX * 16];
     __shared__ float a_s[NMAX], b_s[NMAX];
+    __shared__ int sched_s[TREE ? 64 : 1], cnt_s[TREE ? 64 : 1], part_s[TREE ? 256 : 1];
+    __shared__ float opart_s[NMAX * 4 * 16];            // [node][wave][row * 4 + quad]
     __shared__ __attribute__((aligned(16))) f32x4 slot_s[NSLOT > 0 ? NSLOT * 4 * (R / 4) * 64 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int jb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int N = p.N, Hv = p.Hv, Dv = p.Dv;
     const int hk = h / (Hv / p.Hk);
-    const int jr = lane >> 3, rg = lane & 7;
-    const int jrow = jb * 32 + wave * 8 + jr;         // this lane's value row
+    const int jr = lane >> 4, rg = lane & 15;
+    const int jloc = wave * 4 + jr;                   // this lane's value row in the block
+    const int jrow = jb * 16 + jloc;
     const int64_t bn = (int64_t)b * N;
 
-    // ---- stage q, k (all nodes, this key head), v (32 rows), decay, beta ----
-    // (all loads issued first; they land in LDS after the order is computed)
-    constexpr int QK_IT = (NMAX * DK / 4 + 255) / 256;
-    constexpr int V_IT = (NMAX * 8 + 255) / 256;
-    f32x4 qv[QK_IT], kv[QK_IT], vv[V_IT];
-    float gv = 0.f, bv = 0.f;
-#pragma unroll
-    for (int it = 0; it < QK_IT; ++it) {
-        const int e = tid + it * 256;
-        if (e < N * (DK / 4)) {
-            const int i = e / (DK / 4), c4 = e - i * (DK / 4);
-            const int64_t off = (bn + i) * p.qk_stride + (int64_t)hk * DK + 4 * c4;
-            qv[it] = load4<DT>(p.q, off);
-            kv[it] = load4<DT>(p.k, off);
+    // ---- loads, in the order they are needed: the tree, the committed
+    // state, then q, k (all nodes, this key head), v (16 rows), decay, beta
+    // (indices clamped into range; converted once the order is known) ----
+    int par = lane - 1;
+    if constexpr (TREE) {
+        par = -1;
+        if (lane < N) {
+            const int pr = p.parent[bn + lane];
+            par = (pr >= 0 && pr < lane) ? pr : -1;
         }
     }
-#pragma unroll
-    for (int it = 0; it < V_IT; ++it) {
-        const int e = tid + it * 256;
-        if (e < N * 8) {
-            const int i = e >> 3, c4 = e & 7;
-            vv[it] = load4<DT>(p.v, (bn + i) * p.v_stride + (int64_t)h * Dv + jb * 32 + 4 * c4);
-        }
-    }
-    if (tid < N) {
-        gv = p.g[(bn + tid) * Hv + h];
-        bv = p.beta[(bn + tid) * Hv + h];
-    }
-
-    // ---- committed state into registers ----
     float S[R];
     const float *s0 = p.state + (((int64_t)b * Hv + h) * Dv + jrow) * DK + rg * VEC;
     auto load_s0 = [&]() {
@@ -192,191 +204,270 @@ __global__ __launch_bounds__(256) void delta_tree_kernel(DeltaParams p) {
         for (int c = 0; c < NCH; ++c) {
 #pragma unroll
             for (int u = 0; u < VEC / 4; ++u) {
-                const f32x4 t = *(const f32x4 *)(s0 + c * 8 * VEC + 4 * u);
+                const f32x4 t = *(const f32x4 *)(s0 + c * 16 * VEC + 4 * u);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) S[c * VEC + 4 * u + e] = t[e];
             }
         }
     };
     load_s0();
+    Raw qr[QK_IT], kr[QK_IT], vr[V_IT];
+    const int nqk = N * (DK / 4);
+#pragma unroll
+    for (int it = 0; it < QK_IT; ++it) {
+        const int e = min(tid + it * 256, nqk - 1);
+        const int i = e / (DK / 4), c4 = e - i * (DK / 4);
+        const int64_t off = (bn + i) * p.qk_stride + (int64_t)hk * DK + 4 * c4;
+        qr[it] = load_raw4<DT>(p.q, off);
+        kr[it] = load_raw4<DT>(p.k, off);
+    }
+#pragma unroll
+    for (int it = 0; it < V_IT; ++it) {
+        const int e = min(tid + it * 256, N * 4 - 1);
+        const int i = e >> 2, c4 = e & 3;
+        vr[it] = load_raw4<DT>(p.v, (bn + i) * p.v_stride + (int64_t)h * Dv + jb * 16 + 4 * c4);
+    }
+    const int gi = min(tid, N - 1);
+    const float gv = p.g[(bn + gi) * Hv + h];
+    const float bv = p.beta[(bn + gi) * Hv + h];
 
-    // ---- depth-first order, one lane per node ----
-    int par = lane - 1, pos = lane, slot = 0, nch = 0;
+    // ---- depth-first order, one lane per node (the loops over nodes are
+    // split over the 4 waves) ----
     if constexpr (TREE) {
         const bool live = lane < N;
-        par = -1;
-        if (live) {
-            const int pr = p.parent[bn + lane];
-            par = (pr >= 0 && pr < lane) ? pr : -1;
-        }
-        // ancestor-or-self sets by pointer doubling (depth < 64)
-        uint64_t anc = live ? (1ull << lane) : 0ull;
-        int jp = par;
+        int pos = lane, slot = 0, nch = lane < N - 1 ? 1 : 0, pre = 0;
+        const bool is_chain = __ballot(live && par != lane - 1) == 0ull;   // the same in every wave
+        if (!is_chain) {
+            // ancestor-or-self sets by pointer doubling (depth < 64)
+            uint64_t anc = live ? (1ull << lane) : 0ull;
+            int jp = par;
 #pragma unroll 1
-        for (int r = 0; r < 6; ++r) {
-            if (__ballot(jp >= 0) == 0) break;
-            const int src = jp >= 0 ? jp : lane;
-            const uint32_t alo = (uint32_t)__shfl((int)(uint32_t)anc, src, 64);
-            const uint32_t ahi = (uint32_t)__shfl((int)(uint32_t)(anc >> 32), src, 64);
-            const int jp2 = __shfl(jp, src, 64);
-            if (jp >= 0) {
-                anc |= ((uint64_t)ahi << 32) | alo;
-                jp = jp2;
+            for (int r = 0; r < 6; ++r) {
+                if (__ballot(jp >= 0) == 0ull) break;
+                const int src = jp >= 0 ? jp : lane;
+                const uint32_t alo = (uint32_t)__shfl((int)(uint32_t)anc, src, 64);
+                const uint32_t ahi = (uint32_t)__shfl((int)(uint32_t)(anc >> 32), src, 64);
+                const int jp2 = __shfl(jp, src, 64);
+                if (jp >= 0) {
+                    anc |= ((uint64_t)ahi << 32) | alo;
+                    jp = jp2;
+                }
+            }
+            // subtree sizes and child counts: column counts of the ancestor sets
+#pragma unroll 1
+            for (int i = wave; i < N; i += 4) {
+                const int c1 = __popcll(__ballot(((anc >> i) & 1ull) != 0ull));
+                const int c2 = __popcll(__ballot(par == i));
+                if (lane == 0) cnt_s[i] = c1 | (c2 << 8);
+            }
+            __syncthreads();
+            const int cw = cnt_s[min(lane, N - 1)];
+            const int size = live ? (cw & 255) : 0;
+            nch = live ? (cw >> 8) : 0;
+            // siblings ordered by (subtree size, index), the largest last: the
+            // sizes of the siblings before this node, and whether one comes after
+            int prep = 0, later = 0;
+#pragma unroll 1
+            for (int j = wave; j < N; j += 4) {
+                const int pj = __builtin_amdgcn_readlane(par, j);
+                const int sj = __builtin_amdgcn_readlane(size, j);
+                const bool sib = pj == par && j != lane;
+                const bool before = sj < size || (sj == size && j < lane);
+                prep += (sib && before) ? sj : 0;
+                later |= (sib && !before) ? 1 : 0;
+            }
+            part_s[wave * 64 + lane] = prep | (later << 16);
+            __syncthreads();
+            int later_all = 0;
+#pragma unroll
+            for (int w2 = 0; w2 < 4; ++w2) {
+                const int v = part_s[w2 * 64 + lane];
+                pre += v & 0xFFFF;
+                later_all |= v >> 16;
+            }
+            // preorder position = sum of (1 + pre) along the root path, slot =
+            // number of non-largest children on it: path sums by pointer doubling
+            int aw = live ? 1 + pre : 0, al = (par >= 0 && later_all) ? 1 : 0;
+            jp = par;
+#pragma unroll 1
+            for (int r = 0; r < 6; ++r) {
+                if (__ballot(jp >= 0) == 0ull) break;
+                const int src = jp >= 0 ? jp : lane;
+                const int aw2 = __shfl(aw, src, 64);
+                const int al2 = __shfl(al, src, 64);
+                const int jp2 = __shfl(jp, src, 64);
+                if (jp >= 0) {
+                    aw += aw2;
+                    al += al2;
+                    jp = jp2;
+                }
+            }
+            pos = live ? aw - 1 : -1;
+            slot = al;
+        }
+        // one word per preorder position: node | restore << 8 | save << 16;
+        // restore 0: the parent's state is in registers (a first child comes
+        // right after its parent; the first top node starts from the committed
+        // state already loaded), 1: the committed state, 2 + s: slot s;
+        // save 1 + s: park the state in slot s
+        if (wave == 0) {
+            const int pslot = __shfl(slot, par >= 0 ? par : 0, 64);
+            if (live) {
+                const int rc = (pre == 0 && (par >= 0 || pos == 0)) ? 0 : (par < 0 ? 1 : 2 + pslot);
+                const int sc = nch >= 2 ? 1 + slot : 0;
+                sched_s[pos] = lane | (rc << 8) | (sc << 16);
             }
         }
-        // subtree sizes and child counts
-        int size = 0;
-#pragma unroll 1
-        for (int j = 0; j < N; ++j) {
-            const uint32_t alo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)anc, j);
-            const uint32_t ahi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(anc >> 32), j);
-            const uint64_t aj = ((uint64_t)ahi << 32) | alo;
-            size += (int)((aj >> lane) & 1ull);
-            nch += __builtin_amdgcn_readlane(par, j) == lane ? 1 : 0;
-        }
-        // siblings ordered by (subtree size, index); the last one is the largest
-        int pre = 0;
-        bool last = true;
-#pragma unroll 1
-        for (int j = 0; j < N; ++j) {
-            const int pj = __builtin_amdgcn_readlane(par, j);
-            const int sj = __builtin_amdgcn_readlane(size, j);
-            if (pj == par && j != lane) {
-                if (sj < size || (sj == size && j < lane)) pre += sj;
-                else last = false;
-            }
-        }
-        const int light = (par >= 0 && !last) ? 1 : 0;
-        // preorder position and slot index from the ancestors' ranks
-        pos = -1;
-#pragma unroll 1
-        for (int j = 0; j < N; ++j) {
-            const int pj = __builtin_amdgcn_readlane(pre, j);
-            const int lj = __builtin_amdgcn_readlane(light, j);
-            if ((anc >> j) & 1ull) {
-                pos += 1 + pj;
-                slot += lj;
-            }
-        }
-        if (!live) pos = -1;
     }
 
+    // ---- operands into LDS ----
 #pragma unroll
     for (int it = 0; it < QK_IT; ++it) {
         const int e = tid + it * 256;
-        if (e < N * (DK / 4)) {
-            *(f32x4 *)&q_s[4 * e] = qv[it];          // node e / (DK/4), columns 4 (e % (DK/4)) ..
-            *(f32x4 *)&k_s[4 * e] = kv[it];
+        if (e < nqk) {
+            *(f32x4 *)&q_s[4 * e] = raw_f32(qr[it]);      // node e / (DK/4), columns 4 (e % (DK/4)) ..
+            *(f32x4 *)&k_s[4 * e] = raw_f32(kr[it]);
         }
     }
 #pragma unroll
     for (int it = 0; it < V_IT; ++it) {
         const int e = tid + it * 256;
-        if (e < N * 8) *(f32x4 *)&v_s[4 * e] = vv[it];
+        if (e < N * 4) *(f32x4 *)&v_s[4 * e] = raw_f32(vr[it]);
     }
     if (tid < N) {
         a_s[tid] = expf(gv);
         b_s[tid] = bv;
     }
     __syncthreads();
+    int schedv = lane;                                 // word of preorder position `lane`
+    if constexpr (TREE) schedv = sched_s[min(lane, N - 1)];
 
-    // ---- the walk ----
+    // ---- the walk: the next node's operands (and parked parent state) are
+    // read from LDS during the step before ----
     const float scale = p.scale;
-    f32x4 *my_slot = slot_s + wave * (R / 4) * 64 + lane;           // + s * 4 * (R/4) * 64 + t * 64
-    int prev = -1;
-#pragma unroll 1
-    for (int ks = 0; ks < N; ++ks) {
-        int x = ks;
-        if constexpr (TREE) {
-            const uint64_t m = __ballot(pos == ks);
-            if (m == 0ull) break;                                   // not reached for a valid order
-            x = (int)__builtin_ctzll(m);
-            const int px = __builtin_amdgcn_readlane(par, x);
-            if (px != prev) {
-                if (px < 0) {
-                    load_s0();                                      // another root: the committed state
-                } else {
-                    const int sp = __builtin_amdgcn_readlane(slot, px);
-                    if (sp < NSLOT) {
-#pragma unroll
-                        for (int t = 0; t < R / 4; ++t) {
-                            const f32x4 v4 = my_slot[(sp * 4 * (R / 4) + t) * 64];
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) S[4 * t + e] = v4[e];
-                        }
-                    }
-                }
-            }
-        }
-        const float a = a_s[x], bt = b_s[x];
-        float kk[R], qq[R];
+    // node x's state row of this lane: st_base + x * node_elems + lane_off
+    const int64_t st_base = (bn * Hv + h) * (int64_t)Dv * DK + (int64_t)jb * 16 * DK;
+    const uint32_t node_elems = (uint32_t)Hv * (uint32_t)Dv * DK;
+    const uint32_t lane_off = (uint32_t)jloc * DK + rg * VEC;
+    f32x4 *my_slot = slot_s + wave * (R / 4) * 64 + lane;           // + (s * 4 * (R/4) + t) * 64
+    auto fetch = [&](int x, float (&kd)[R], float (&qd)[R], float &vd, float &ad, float &bd) {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
 #pragma unroll
             for (int u = 0; u < VEC / 4; ++u) {
-                const int col = c * 8 * VEC + rg * VEC + 4 * u;
+                const int col = c * 16 * VEC + rg * VEC + 4 * u;
                 const f32x4 k4 = *(const f32x4 *)&k_s[x * DK + col];
                 const f32x4 q4 = *(const f32x4 *)&q_s[x * DK + col];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    kk[c * VEC + 4 * u + e] = k4[e];
-                    qq[c * VEC + 4 * u + e] = q4[e];
+                    kd[c * VEC + 4 * u + e] = k4[e];
+                    qd[c * VEC + 4 * u + e] = q4[e];
+                }
+            }
+        }
+        vd = v_s[x * 16 + jloc];
+        ad = a_s[x];
+        bd = b_s[x];
+    };
+    float Sr[R];                                        // a parked state read ahead
+    auto step = [&](int ks, int word, const float (&kk)[R], const float (&qq)[R], float vx, float a, float bt,
+                    float (&kn)[R], float (&qn)[R], float &vn, float &an, float &bn_) -> int {
+        const int x = word & 63;
+        if constexpr (TREE) {
+            const int rc = (word >> 8) & 255;
+            if (rc == 1) {
+                load_s0();                                  // another root: the committed state
+            } else if (rc >= 2) {
+#pragma unroll
+                for (int t = 0; t < R; ++t) S[t] = Sr[t];
+            }
+        }
+        const int wn = ks + 1 < N ? __builtin_amdgcn_readlane(schedv, ks + 1) : word;
+        fetch(wn & 63, kn, qn, vn, an, bn_);
+        if constexpr (TREE) {
+            const int rcn = (wn >> 8) & 255;
+            // (a node followed by a restore is a leaf: it parks nothing)
+            if (rcn >= 2 && rcn - 2 < NSLOT) {
+#pragma unroll
+                for (int t = 0; t < R / 4; ++t) {
+                    const f32x4 v4 = my_slot[((rcn - 2) * 4 * (R / 4) + t) * 64];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Sr[4 * t + e] = v4[e];
                 }
             }
         }
         // u = beta (v - a S k);  S <- a S + u k^T;  o = scale S q
-        float d0 = 0.f, d1 = 0.f;
+        float d[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < R; t += 2) {
-            d0 = fmaf(S[t], kk[t], d0);
-            d1 = fmaf(S[t + 1], kk[t + 1], d1);
-        }
-        const float dot = sum8(d0 + d1);
-        const float u = (v_s[x * 32 + wave * 8 + jr] - a * dot) * bt;
+        for (int t = 0; t < R; ++t) d[t & 3] = fmaf(S[t], kk[t], d[t & 3]);
+        const float dot = sum16((d[0] + d[1]) + (d[2] + d[3]));
+        const float u = (vx - a * dot) * bt;
 #pragma unroll
         for (int t = 0; t < R; ++t) S[t] = fmaf(S[t], a, u * kk[t]);
-        float o0 = 0.f, o1 = 0.f;
+        float o4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < R; t += 2) {
-            o0 = fmaf(S[t], qq[t], o0);
-            o1 = fmaf(S[t + 1], qq[t + 1], o1);
-        }
-        const float o = sum8(o0 + o1) * scale;
-        const int64_t orow = (bn + x) * Hv + h;
-        if (rg == 0) {
-            if constexpr (DT == SV_F32) {
-                ((float *)p.out)[orow * Dv + jrow] = o;
-            } else {
-                ((uint16_t *)p.out)[orow * Dv + jrow] = (uint16_t)f32_to_bf16_bits(o);
-            }
-        }
-        // persist this node's state
-        const int64_t srow = (orow * Dv + jrow) * DK + rg * VEC;
+        for (int t = 0; t < R; ++t) o4[t & 3] = fmaf(S[t], qq[t], o4[t & 3]);
+        // quad sums of S q go to LDS; the 4 quads of a row are added after the walk
+        float oq = (o4[0] + o4[1]) + (o4[2] + o4[3]);
+        oq += dpp_f<0xB1>(oq);
+        oq += dpp_f<0x4E>(oq);
+        opart_s[(x * 4 + wave) * 16 + (lane >> 2)] = oq;
+        // persist this node's state (uniform node base + per-lane offset;
+        // streaming stores: the buffer is read back at most once, by the commit)
         if constexpr (SDT == SV_F32) {
-            float *dst = (float *)p.state_nodes + srow;
+            float *dst = (float *)p.state_nodes + st_base + (uint32_t)x * node_elems;
 #pragma unroll
             for (int c = 0; c < NCH; ++c)
-                *(f32x4 *)(dst + c * 32) = f32x4{S[4 * c], S[4 * c + 1], S[4 * c + 2], S[4 * c + 3]};
-        } else {
-            uint16_t *dst = (uint16_t *)p.state_nodes + srow;
+                __builtin_nontemporal_store(f32x4{S[4 * c], S[4 * c + 1], S[4 * c + 2], S[4 * c + 3]},
+                                            (f32x4 *)(dst + (lane_off + c * 64)));
+        } else if constexpr (VEC == 8) {
+            uint16_t *dst = (uint16_t *)p.state_nodes + st_base + (uint32_t)x * node_elems;
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
                 const float *sc = &S[8 * c];
-                *(u32x4 *)(dst + c * 64) = u32x4{pack_f16x2(sc[0], sc[1]), pack_f16x2(sc[2], sc[3]),
-                                                 pack_f16x2(sc[4], sc[5]), pack_f16x2(sc[6], sc[7])};
+                __builtin_nontemporal_store(u32x4{pack_f16x2(sc[0], sc[1]), pack_f16x2(sc[2], sc[3]),
+                                                  pack_f16x2(sc[4], sc[5]), pack_f16x2(sc[6], sc[7])},
+                                            (u32x4 *)(dst + (lane_off + c * 128)));
+            }
+        } else {
+            uint16_t *dst = (uint16_t *)p.state_nodes + st_base + (uint32_t)x * node_elems;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const float *sc = &S[4 * c];
+                __builtin_nontemporal_store(u32x2{pack_f16x2(sc[0], sc[1]), pack_f16x2(sc[2], sc[3])},
+                                            (u32x2 *)(dst + (lane_off + c * 64)));
             }
         }
         if constexpr (TREE) {
-            if (__builtin_amdgcn_readlane(nch, x) >= 2) {
-                const int sx = __builtin_amdgcn_readlane(slot, x);
-                if (sx < NSLOT) {
+            const int sc = word >> 16;
+            if (sc >= 1 && sc - 1 < NSLOT) {
 #pragma unroll
-                    for (int t = 0; t < R / 4; ++t)
-                        my_slot[(sx * 4 * (R / 4) + t) * 64] = f32x4{S[4 * t], S[4 * t + 1], S[4 * t + 2], S[4 * t + 3]};
-                }
+                for (int t = 0; t < R / 4; ++t)
+                    my_slot[((sc - 1) * 4 * (R / 4) + t) * 64] = f32x4{S[4 * t], S[4 * t + 1], S[4 * t + 2], S[4 * t + 3]};
             }
         }
-        prev = x;
+        return wn;
+    };
+    float kA[R], qA[R], kB[R], qB[R];
+    float vA = 0.f, aA = 0.f, bA = 0.f, vB = 0.f, aB = 0.f, bB = 0.f;
+    int word = __builtin_amdgcn_readlane(schedv, 0);
+    fetch(word & 63, kA, qA, vA, aA, bA);
+#pragma unroll 1
+    for (int ks = 0; ks < N; ks += 2) {
+        word = step(ks, word, kA, qA, vA, aA, bA, kB, qB, vB, aB, bB);
+        if (ks + 1 >= N) break;
+        word = step(ks + 1, word, kB, qB, vB, aB, bB, kA, qA, vA, aA, bA);
+    }
+
+    // ---- outputs: the 4 quad sums of each (node, row), coalesced rows of 16 ----
+    __syncthreads();
+    for (int e = tid; e < N * 16; e += 256) {
+        const int x = e >> 4, jl = e & 15;
+        const float *pq = &opart_s[(x * 4 + (jl >> 2)) * 16 + (jl & 3) * 4];
+        const float o = ((pq[0] + pq[1]) + (pq[2] + pq[3])) * scale;
+        const int64_t oi = ((bn + x) * Hv + h) * Dv + jb * 16 + jl;
+        if constexpr (DT == SV_F32) ((float *)p.out)[oi] = o;
+        else ((uint16_t *)p.out)[oi] = (uint16_t)f32_to_bf16_bits(o);
     }
 }
 
@@ -461,7 +552,7 @@ hipError_t launch_conv_k(const ConvTreeParams &p, hipStream_t st) {
 
 template <int R, int NMAX, bool TREE, int DT>
 hipError_t launch_delta_s(const DeltaParams &p, int sdt, hipStream_t st) {
-    const dim3 grid((unsigned)(p.Dv / 32), (unsigned)p.Hv, (unsigned)p.B);
+    const dim3 grid((unsigned)(p.Dv / 16), (unsigned)p.Hv, (unsigned)p.B);
     if (sdt == SV_F16)
         hipLaunchKernelGGL((delta_tree_kernel<R, NMAX, TREE, DT, SV_F16>), grid, dim3(256), 0, st, p);
     else
@@ -495,7 +586,7 @@ hipError_t launch_conv_tree(const ConvTreeParams &p, int dtype, hipStream_t st) 
 }
 
 hipError_t launch_delta_tree(const DeltaParams &p, int dtype, int state_dtype, int Dk, hipStream_t st) {
-    return Dk == 64 ? launch_delta_r<8>(p, dtype, state_dtype, st) : launch_delta_r<16>(p, dtype, state_dtype, st);
+    return Dk == 64 ? launch_delta_r<4>(p, dtype, state_dtype, st) : launch_delta_r<8>(p, dtype, state_dtype, st);
 }
 
 hipError_t launch_commit(const CommitParams &p, int state_dtype, int dtype, hipStream_t st) {

@@ -613,6 +613,7 @@ int sv_gated_delta_net_tree(int batch, int n_nodes, int n_k_heads, int n_v_heads
         return SV_EINVAL;
     if (parent != nullptr && !aligned(parent, 4)) return SV_EINVAL;
     if (!isfinite(scale)) return SV_EINVAL;
+    if ((uint64_t)n_nodes * n_v_heads * v_dim * k_dim > 0xFFFFFFFFull) return SV_EUNSUPPORTED;
     DeltaParams p{};
     p.q = q;
     p.k = k;

@@ -325,7 +325,8 @@ int sv_ssm_conv_tree(int batch, int n_nodes, int channels, int kernel_width,
  * out         device [batch][N][n_v_heads][v_dim] in dtype.
  * state_nodes device [batch][N][n_v_heads][v_dim][k_dim] in state_dtype
  *             (SV_F32, or SV_F16 rounded to nearest even): every node's state.
- * scale <= 0 selects 1/sqrt(k_dim).  k_dim 64 or 128 (else SV_EUNSUPPORTED);
+ * scale <= 0 selects 1/sqrt(k_dim).  k_dim 64 or 128, and N * n_v_heads * v_dim *
+ * k_dim below 2^32 (else SV_EUNSUPPORTED);
  * v_dim a multiple of 32.  Arithmetic in fp32.
  */
 int sv_gated_delta_net_tree(int batch, int n_nodes, int n_k_heads, int n_v_heads, int k_dim, int v_dim,
