@@ -500,26 +500,39 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitParams p) {
     const int a = ok_s;
     if (a < 0) return;
     if ((int)blockIdx.x < p.state_blocks) {
-        const int64_t e = ((int64_t)blockIdx.x * 256 + tid) * 8;
-        if (e >= p.state_elems) return;
-        const int64_t src = ((int64_t)b * N + path_s[a]) * p.state_elems + e;
-        float v[8];
-        if constexpr (SDT == SV_F32) {
-            const f32x4 x0 = *(const f32x4 *)((const float *)p.state_nodes + src);
-            const f32x4 x1 = *(const f32x4 *)((const float *)p.state_nodes + src + 4);
+        // the accepted node's state: 8 values per thread and round, 4 rounds in
+        // flight, the sequence's workgroups striding over it
+        const int64_t src0 = ((int64_t)b * N + path_s[a]) * p.state_elems;
+        float *dst0 = p.state + (int64_t)b * p.state_elems;
+        const int64_t stride = (int64_t)p.state_blocks * 256 * 8;
+        for (int64_t e0 = ((int64_t)blockIdx.x * 256 + tid) * 8; e0 < p.state_elems; e0 += 4 * stride) {
+            float v[4][8];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) { v[t] = x0[t]; v[4 + t] = x1[t]; }
-        } else {
-            const u32x4 h = *(const u32x4 *)((const uint16_t *)p.state_nodes + src);
+            for (int r = 0; r < 4; ++r) {
+                const int64_t e = min(e0 + r * stride, p.state_elems - 8);
+                if constexpr (SDT == SV_F32) {
+                    const f32x4 x0 = *(const f32x4 *)((const float *)p.state_nodes + src0 + e);
+                    const f32x4 x1 = *(const f32x4 *)((const float *)p.state_nodes + src0 + e + 4);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                v[2 * t] = fp16_bits_to_f32(h[t] & 0xFFFFu);
-                v[2 * t + 1] = fp16_bits_to_f32(h[t] >> 16);
+                    for (int t = 0; t < 4; ++t) { v[r][t] = x0[t]; v[r][4 + t] = x1[t]; }
+                } else {
+                    const u32x4 hv = *(const u32x4 *)((const uint16_t *)p.state_nodes + src0 + e);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        v[r][2 * t] = fp16_bits_to_f32(hv[t] & 0xFFFFu);
+                        v[r][2 * t + 1] = fp16_bits_to_f32(hv[t] >> 16);
+                    }
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t e = e0 + r * stride;
+                if (e < p.state_elems) {
+                    *(f32x4 *)(dst0 + e) = f32x4{v[r][0], v[r][1], v[r][2], v[r][3]};
+                    *(f32x4 *)(dst0 + e + 4) = f32x4{v[r][4], v[r][5], v[r][6], v[r][7]};
+                }
             }
         }
-        float *dst = p.state + (int64_t)b * p.state_elems + e;
-        *(f32x4 *)dst = f32x4{v[0], v[1], v[2], v[3]};
-        *(f32x4 *)(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
         return;
     }
     const int c0 = ((blockIdx.x - p.state_blocks) * 256 + tid) * 4;

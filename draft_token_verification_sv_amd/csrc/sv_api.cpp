@@ -653,7 +653,9 @@ int sv_recurrent_commit(int batch, int n_nodes, int n_v_heads, int k_dim, int v_
         !aligned(path, 4) || !aligned(accept_len, 4))
         return SV_EINVAL;
     const int64_t elems = (int64_t)n_v_heads * v_dim * k_dim;
-    const int64_t blocks = (elems / 8 + 255) / 256;
+    // workgroups per sequence on the state copy: about 1024 in all, each copying
+    // at least 2048 values
+    const int64_t blocks = std::min<int64_t>((elems / 8 + 255) / 256, std::max(8, 1024 / batch));
     if (blocks + (channels + 1023) / 1024 > (int64_t)INT32_MAX) return SV_EUNSUPPORTED;
     CommitParams p{};
     p.state_nodes = state_nodes;
