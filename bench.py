@@ -66,8 +66,9 @@ def source_hash():
 
 
 def measured_traffic(workload, per_launch_bytes):
-    """HBM bytes per attention call from the committed rocprofv3 counter runs,
-    if they were taken on the current kernel sources."""
+    """HBM bytes per call of the workload's dominant kernel (attention, or the
+    tree recurrence) from the committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources."""
     path = os.path.join(ROOT, "profiles", "attn_traffic.json")
     if not os.path.exists(path):
         return None
@@ -180,7 +181,7 @@ def recurrent_bench(sv, dev, key, steps, rotate_bytes, capture, timed):
                          "recurrent_commit": round(commit_us, 2)},
         "rotation_copies": n_rot,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(cfg.name, nbytes),
                      "kernel": "sv_gated_delta_net_tree", "algorithmic_bytes": int(nbytes)},
     }
 
