@@ -15,7 +15,8 @@ the stored inputs:
 * ``accept``: per-row argmax (lowest index wins ties), the greedy acceptance
   walk (longest accepted root path, plus the bonus token), and an
   independent brute-force version of the walk; the sampled variant (each
-  row's Gumbel-max sample at temperature T in place of its argmax);
+  row's Gumbel-max sample at temperature T, optionally over its top-k
+  tokens, in place of its argmax);
 * ``compact``: the post-acceptance KV compaction as a snapshot copy;
 * ``append``: writing the verify block's K/V rows into the cache, with the
   4-bit quantisation at write time;
@@ -41,7 +42,8 @@ Parity status: every function here is pinned by the CPU tests in
 """
 from .formats import widen_bf16, widen_fp16, widen_f32, q4_decode
 from .attention import ancestor_matrix, verify_mask, verify_attention_seq, verify_attention
-from .accept import argmax_first, accept_walk, accept_bruteforce, greedy_accept, sample_row, sample_accept
+from .accept import (argmax_first, accept_walk, accept_bruteforce, greedy_accept, sample_row, sample_accept,
+                     topk_threshold, sample_row_topk)
 from .compact import compact_cache
 from .append import bf16_round, q4_quantise, kv_append
 from .recurrent import tree_parent, root_path, conv_tree, delta_rule_step, delta_net_tree, recurrent_commit
@@ -50,6 +52,7 @@ __all__ = [
     "widen_bf16", "widen_fp16", "widen_f32", "q4_decode",
     "ancestor_matrix", "verify_mask", "verify_attention_seq", "verify_attention",
     "argmax_first", "accept_walk", "accept_bruteforce", "greedy_accept", "sample_row", "sample_accept",
+    "topk_threshold", "sample_row_topk",
     "compact_cache", "bf16_round", "q4_quantise", "kv_append",
     "tree_parent", "root_path", "conv_tree", "delta_rule_step", "delta_net_tree", "recurrent_commit",
 ]

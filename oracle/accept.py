@@ -136,11 +136,33 @@ def sample_row(logits32, gumbel32, temperature) -> int:
     return int(np.argmax(keys))            # first occurrence of the maximum
 
 
-def sample_accept(logits32, gumbel32, temperature, draft_ids, parent):
+def topk_threshold(logits32, top_k):
+    """The k-th largest value of a row (values compared in fp32, so -0 ties
+    +0); every token whose logit is >= it stays in the top-k set, ties at the
+    k-th value included."""
+    l32 = np.asarray(logits32, dtype=np.float32)
+    return np.sort(l32.astype(np.float64))[::-1][top_k - 1]
+
+
+def sample_row_topk(logits32, gumbel32, temperature, top_k) -> int:
+    """Top-k sampling at temperature T: the Gumbel-max sample over the tokens
+    whose logit is at least the row's k-th largest (renormalised softmax of
+    l / T over that set; top_k <= 0 or >= V keeps every token)."""
+    l32 = np.asarray(logits32, dtype=np.float32)
+    if top_k <= 0 or top_k >= l32.size:
+        return sample_row(l32, gumbel32, temperature)
+    keep = l32.astype(np.float64) >= topk_threshold(l32, top_k)
+    keys = (l32 / np.float32(temperature)).astype(np.float32) + np.asarray(gumbel32, dtype=np.float32)
+    keys = np.where(keep, keys, np.float32(-np.inf))
+    return int(np.argmax(keys))
+
+
+def sample_accept(logits32, gumbel32, temperature, draft_ids, parent, top_k=0):
     """Whole batch.  ``logits32``: float32 ``[B, N, V]`` (exact widening of the
-    stored logits); ``gumbel32``: float32 ``[B, N, V]``.  Returns ``sampled
-    [B, N]``, ``accept_len [B]``, ``path [B, N]``, ``tokens [B, N]`` -- the
-    greedy walk with every row's argmax replaced by its sample."""
+    stored logits); ``gumbel32``: float32 ``[B, N, V]``; ``top_k`` > 0
+    restricts each row to its top-k tokens.  Returns ``sampled [B, N]``,
+    ``accept_len [B]``, ``path [B, N]``, ``tokens [B, N]`` -- the greedy walk
+    with every row's argmax replaced by its sample."""
     B, N, _ = logits32.shape
     ys = np.empty((B, N), dtype=np.int32)
     acc = np.empty(B, dtype=np.int32)
@@ -148,6 +170,6 @@ def sample_accept(logits32, gumbel32, temperature, draft_ids, parent):
     tok = np.empty((B, N), dtype=np.int32)
     for b in range(B):
         for i in range(N):
-            ys[b, i] = sample_row(logits32[b, i], gumbel32[b, i], temperature)
+            ys[b, i] = sample_row_topk(logits32[b, i], gumbel32[b, i], temperature, top_k)
         acc[b], path[b], tok[b] = accept_walk(ys[b], draft_ids[b], parent[b])
     return ys, acc, path, tok
