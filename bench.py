@@ -301,6 +301,10 @@ def main():
         sv.sample_accept(copies[i % n_copies]["logits"], gumbel, 0.8, drafts, parent, workspace=ws_g,
                          outputs=(acc, path, tok, None))
 
+    def sample_topk(i):
+        sv.sample_accept(copies[i % n_copies]["logits"], gumbel, 0.8, drafts, parent, workspace=ws_g,
+                         outputs=(acc, path, tok, None), top_k=50)
+
     def append(i):
         sv.kv_append(kvs[i % n_copies], new_rows[0], new_rows[1], ctx, max_ctx)
 
@@ -352,6 +356,8 @@ def main():
     accept_compact_us = timed(g_ac) / args.steps * 1e3
     g_smp = capture(sample)
     sample_us = timed(g_smp) / args.steps * 1e3
+    g_stk = capture(sample_topk)
+    sample_topk_us = timed(g_stk) / args.steps * 1e3
     g_app = capture(append)                 # last: it rewrites the draft rows of the rotated caches
     append_us = timed(g_app) / args.steps * 1e3
     attn_ms = np.array([attn_total_ms / args.steps])
@@ -388,7 +394,8 @@ def main():
         "breakdown_us": {"verify_attn": round(attn_us, 2), "greedy_accept": round(accept_us, 2),
                          "kv_compact": round(compact_us, 2), "greedy_accept_compact": round(accept_compact_us, 2),
                          "kv_append (not in the step)": round(append_us, 2),
-                         "sample_accept T=0.8 (not in the step)": round(sample_us, 2)},
+                         "sample_accept T=0.8 (not in the step)": round(sample_us, 2),
+                         "sample_accept_topk k=50 T=0.8 (not in the step)": round(sample_topk_us, 2)},
         "accepted_tokens_per_step": None,
     }
     if args.recurrent != "none":

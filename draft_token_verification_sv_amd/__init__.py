@@ -84,6 +84,9 @@ lib.sv_kv_append.argtypes = [ctypes.POINTER(_KvDesc), _I, _I, _P, _I, _P, _P, _I
 lib.sv_greedy_accept_compact.restype = _I
 lib.sv_greedy_accept_compact.argtypes = [_I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P,
                                          ctypes.POINTER(_KvDesc), _I, _P, _I, _P, _P, ctypes.c_size_t, _P]
+lib.sv_sample_accept_topk.restype = _I
+lib.sv_sample_accept_topk.argtypes = [_I, _I, _I, _P, _I, _P, ctypes.c_float, _I, _P, _P, _P, _P, _P, _P, _P,
+                                      ctypes.c_size_t, _P]
 lib.sv_ssm_conv_tree.restype = _I
 lib.sv_ssm_conv_tree.argtypes = [_I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _I, _P, _P]
 lib.sv_gated_delta_net_tree.restype = _I
@@ -306,9 +309,10 @@ def greedy_accept(logits: torch.Tensor, draft_ids: torch.Tensor, parent: torch.T
 
 def sample_accept(logits: torch.Tensor, gumbel: torch.Tensor, temperature: float, draft_ids: torch.Tensor,
                   parent: torch.Tensor, want_samples: bool = True, workspace: Optional[torch.Tensor] = None,
-                  outputs=None):
+                  outputs=None, top_k: int = 0):
     """Stochastic verification at ``temperature`` with the caller's standard
-    Gumbel noise ``gumbel`` (float32, the shape of ``logits``).
+    Gumbel noise ``gumbel`` (float32, the shape of ``logits``); ``top_k`` > 0
+    samples among each row's top-k tokens.
 
     Returns ``(accept_len [B], path [B, N], tokens [B, N], samples [B, N] or None)``.
     """
@@ -330,6 +334,13 @@ def sample_accept(logits: torch.Tensor, gumbel: torch.Tensor, temperature: float
     need = int(lib.sv_greedy_accept_workspace_size(B, N, V))
     if workspace is None:
         workspace = _workspace("accept", dev, need, zero=True)
+    if top_k:
+        rc = lib.sv_sample_accept_topk(B, N, V, _ptr(logits), _dtype_code(logits), _ptr(gumbel), float(temperature),
+                                       int(top_k), _ptr(draft_ids), _ptr(parent), _ptr(acc), _ptr(path), _ptr(tok),
+                                       _ptr(ys), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                       _stream(dev))
+        _check(rc, "sv_sample_accept_topk")
+        return acc, path, tok, ys
     rc = lib.sv_sample_accept(B, N, V, _ptr(logits), _dtype_code(logits), _ptr(gumbel), float(temperature),
                               _ptr(draft_ids), _ptr(parent), _ptr(acc), _ptr(path), _ptr(tok), _ptr(ys),
                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))

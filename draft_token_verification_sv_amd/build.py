@@ -15,7 +15,7 @@ OUT = os.path.join(PKG, "libsv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["sv_api.cpp", "attn_dma.hip", "attn_mfma.hip", "attn_valu.hip", "accept.hip", "compact.hip",
-           "append.hip", "recurrent.hip"]
+           "append.hip", "recurrent.hip", "topk.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

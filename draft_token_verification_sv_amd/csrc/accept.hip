@@ -25,48 +25,10 @@
 // Fused form (acceptance + compaction): the last workgroup of sequence b then
 // moves the accepted rows' KV itself with all of its threads, so the sequence
 // needs no second launch (the standalone compaction kernel is compact.hip).
-#include "device_common.h"
+#include "accept_walk.h"
 
 namespace sv {
 namespace {
-
-__device__ __forceinline__ unsigned long long make_key(float v, uint32_t idx) {
-    uint32_t u = __float_as_uint(v);
-    if (u == 0x80000000u) u = 0u;                      // -0 ties with +0
-    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((unsigned long long)ord << 32) | (unsigned long long)(0xFFFFFFFFu - idx);
-}
-
-__device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) {
-    return a > b ? a : b;
-}
-
-// one DPP step of a 64-bit running maximum: lanes outside the move's source
-// range (and rows outside `rmask`) contribute the identity 0
-#define SV_DPP_MAX64(k, ctrl, rmask)                                                                      \
-    do {                                                                                               \
-        const uint32_t lo_ = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k), ctrl, rmask, 0xf, false); \
-        const uint32_t hi_ = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)((k) >> 32), ctrl, rmask, 0xf, false); \
-        k = umax64(k, ((unsigned long long)hi_ << 32) | lo_);                                         \
-    } while (0)
-
-// maximum over the 64 lanes (row shifts 1, 2, 4, 8, then the broadcasts of
-// lanes 15 and 31 leave the running maximum of all lanes in lane 63)
-__device__ __forceinline__ unsigned long long wave_max64(unsigned long long k) {
-    SV_DPP_MAX64(k, 0x111, 0xf);
-    SV_DPP_MAX64(k, 0x112, 0xf);
-    SV_DPP_MAX64(k, 0x114, 0xf);
-    SV_DPP_MAX64(k, 0x118, 0xf);
-    SV_DPP_MAX64(k, 0x142, 0xa);
-    SV_DPP_MAX64(k, 0x143, 0xc);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, 63);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 63);
-    return ((unsigned long long)hi << 32) | lo;
-}
-
-// vmcnt(0): every vector memory operation of this wave (the atomics above
-// included, their results returned) has completed
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 constexpr int kCompactLds = 32768;      // staging bytes of the fused compaction
 
@@ -239,54 +201,7 @@ __global__ __launch_bounds__(256) void argmax_accept_kernel(AcceptParams p) {
     if constexpr (COMPACT) {
         if (lane == 0) cinfo_s[0] = clamp_ctx(p.cp.ctx_lens[b], p.cp.max_ctx);
     }
-    if (lane < N) {
-        const unsigned long long k =
-            __hip_atomic_exchange(&p.keys[(int64_t)b * N + lane], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        am_s[lane] = (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
-        dr_s[lane] = p.draft[(int64_t)b * N + lane];
-        par_s[lane] = p.parent[(int64_t)b * N + lane];
-    }
-    __builtin_amdgcn_s_waitcnt(0);           // the LDS writes of all lanes (one wave: no barrier)
-    __builtin_amdgcn_wave_barrier();
-
-    // node `lane`: accepted iff every edge of its root path is accepted
-    int acc = 0, depth = 0;
-    if (lane < N) {
-        acc = 1;
-        int j = lane;
-#pragma unroll 1
-        for (int step = 0; step < 64 && j > 0; ++step) {
-            const int pj = par_s[j];
-            if (pj < 0 || pj >= j) { acc = 0; break; }
-            if (dr_s[j] != am_s[pj]) acc = 0;
-            ++depth;
-            j = pj;
-        }
-    }
-    // deepest accepted node, ties to the smallest index (node 0 always qualifies)
-    unsigned int key = acc ? (((unsigned)depth << 8) | (unsigned)(255 - lane)) : 0u;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) key = max(key, (unsigned)__shfl_xor((int)key, m, 64));
-    const int best_node = 255 - (int)(key & 255u);
-    const int a = (int)(key >> 8);
-
-    int32_t *path = p.path + (int64_t)b * N;
-    int32_t *tok = p.tokens + (int64_t)b * N;
-    if (lane == 0) {
-        int j = best_node;
-        for (int d = a; d >= 0; --d) {
-            path[d] = j;
-            if constexpr (COMPACT) path_s[d] = j;
-            if (d > 0) tok[d - 1] = dr_s[j];
-            j = (j > 0) ? par_s[j] : 0;
-        }
-        tok[a] = am_s[best_node];
-        p.accept_len[b] = a;
-    }
-    if (lane < N && lane > a) {
-        path[lane] = -1;
-        tok[lane] = -1;
-    }
+    const int a = walk_sequence<COMPACT>(p, b, lane, am_s, dr_s, par_s, path_s);
     if (p.argmax != nullptr && lane < N) p.argmax[(int64_t)b * N + lane] = am_s[lane];
     if constexpr (COMPACT) {
         // the moving rows j in [1, a] (path[j] > j), in increasing order

@@ -543,6 +543,29 @@ int sv_sample_accept(int batch, int n_nodes, int vocab,
     return SV_OK;
 }
 
+int sv_sample_accept_topk(int batch, int n_nodes, int vocab,
+                          const void *logits, int logits_dtype, const float *gumbel, float temperature, int top_k,
+                          const int32_t *draft_ids, const int32_t *parent,
+                          int32_t *accept_len, int32_t *path, int32_t *tokens, int32_t *sampled,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    if (top_k <= 0 || top_k >= vocab)
+        return sv_sample_accept(batch, n_nodes, vocab, logits, logits_dtype, gumbel, temperature, draft_ids, parent,
+                                accept_len, path, tokens, sampled, workspace, workspace_bytes, stream);
+    AcceptParams p;
+    const int rc = accept_params(batch, n_nodes, vocab, logits, logits_dtype, draft_ids, parent, accept_len, path,
+                                 tokens, sampled, workspace, workspace_bytes, p);
+    if (rc != SV_OK) return rc;
+    if (gumbel == nullptr || !aligned(gumbel, 4)) return SV_EINVAL;
+    if (!(temperature > 0.f) || !isfinite(temperature)) return SV_EINVAL;
+    if (top_k > 1024) return SV_EUNSUPPORTED;
+    p.gumbel = gumbel;
+    p.temperature = temperature;
+    p.top_k = top_k;
+    const hipError_t e = launch_topk_accept(p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return SV_OK;
+}
+
 int sv_greedy_accept_compact(int batch, int n_nodes, int vocab,
                              const void *logits, int logits_dtype,
                              const int32_t *draft_ids, const int32_t *parent,

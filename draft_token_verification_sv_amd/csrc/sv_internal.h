@@ -66,6 +66,7 @@ struct AcceptParams {
     CompactParams cp;
     const float *gumbel;          // [B][N][V] noise: sample at `temperature` instead of the argmax (or null)
     float temperature;
+    int top_k;                    // > 0: sample among each row's top_k logits (launch_topk_accept)
 };
 
 struct AppendParams {
@@ -120,6 +121,7 @@ int attn_dma_max_split_pages();
 hipError_t launch_attn_valu(const AttnParams &p, int dtype, int D, hipStream_t s);
 hipError_t launch_attn_merge(const AttnParams &p, int D, hipStream_t s);
 hipError_t launch_accept(const AcceptParams &p, hipStream_t s);
+hipError_t launch_topk_accept(const AcceptParams &p, hipStream_t s);
 hipError_t launch_compact(const CompactParams &p, hipStream_t s);
 hipError_t launch_append(const AppendParams &p, int src_dtype, int dst_dtype, hipStream_t s);
 hipError_t launch_conv_tree(const ConvTreeParams &p, int dtype, hipStream_t s);

@@ -15,7 +15,8 @@
  *   sv_kv_append      the verify block's K/V rows written into the cache
  *                     (quantised at write time for a 4-bit cache);
  *   sv_verify_attn_window  the attention over a sliding window of keys;
- *   sv_sample_accept  stochastic verification at a temperature;
+ *   sv_sample_accept  stochastic verification at a temperature (and
+ *                     sv_sample_accept_topk over each row's top-k tokens);
  *   sv_ssm_conv_tree, sv_gated_delta_net_tree, sv_recurrent_commit
  *                     the tree-aware recurrent state of a hybrid target's
  *                     Gated DeltaNet layers.
@@ -237,6 +238,23 @@ int sv_sample_accept(int batch, int n_nodes, int vocab,
                      const int32_t *draft_ids, const int32_t *parent,
                      int32_t *accept_len, int32_t *path, int32_t *tokens, int32_t *sampled,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sv_sample_accept_topk -- sv_sample_accept restricted to each row's top-k
+ * tokens [DFN "Next steps": temperature and top-k sampling planned for the
+ * verify path].  Token v of row (b, i) competes in the Gumbel-max sample only
+ * if its logit is >= the row's k-th largest logit (values compared as fp32,
+ * -0 == +0; ties at the k-th value stay in).  top_k <= 0 or >= vocab is
+ * sv_sample_accept; 1 <= top_k <= 1024 runs one workgroup per row (k-th
+ * largest by radix selection over LDS candidates); larger k: SV_EUNSUPPORTED.
+ * Arguments, outputs, workspace and errors as sv_sample_accept (the gumbel
+ * rows are read only at the candidate tokens).
+ */
+int sv_sample_accept_topk(int batch, int n_nodes, int vocab,
+                          const void *logits, int logits_dtype, const float *gumbel, float temperature, int top_k,
+                          const int32_t *draft_ids, const int32_t *parent,
+                          int32_t *accept_len, int32_t *path, int32_t *tokens, int32_t *sampled,
+                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * sv_kv_append -- write the verify block's K/V rows into the cache, quantising

@@ -188,6 +188,12 @@ def test_sample_accept_checks(lib):
     assert call(g=0) == -1 and call(g=FAKE + 2) == -1
     assert call(N=0) == -1 and call(ws=0) == -3
 
+    def topk(k, T=0.8, g=FAKE):
+        return lib.sv_sample_accept_topk(1, 8, 151936, P, 1, ctypes.c_void_p(g), ctypes.c_float(T), k, P, P, P, P,
+                                         P, None, P, ctypes.c_size_t(1 << 30), None)
+    assert topk(1025) == -2 and topk(151935) == -2            # 1 <= k <= 1024 on the top-k kernel
+    assert topk(50, T=0.0) == -1 and topk(50, g=0) == -1 and topk(0, g=0) == -1
+
 
 def test_recurrent_checks(lib):
     P = ctypes.c_void_p(FAKE)

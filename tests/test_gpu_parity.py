@@ -367,6 +367,54 @@ def test_sample_accept(sv, label, cfg, T):
     np.testing.assert_array_equal(tok.cpu().numpy(), r_tok)
 
 
+TOPK_CASES = [
+    # (label, config, temperature, top_k, special rows)
+    ("C2 k=50 T1", _small("C2", ctx=8, vocab=151936), 1.0, 50, False),
+    ("C3 tree22 k=1 ties", _small("C3", ctx=8, vocab=151936), 0.7, 1, False),
+    ("C5 batch8 k=20 T1.3", _small("C5", ctx=8, ctx_hi=20, vocab=151936), 1.3, 20, False),
+    ("C2 k=1024", _small("C2", ctx=8, vocab=151936), 0.9, 1024, False),
+    ("flat and tied rows (whole-row path)", _small("C2", ctx=8, vocab=151936), 1.0, 40, True),
+    ("odd vocab f32 k=7", workloads.Config("oddv", 3, 2, 1, 64, 7, "f32", "f32", "f32", 4099, 8,
+                                           tree="ddtree", draft_rule="tree"), 2.0, 7, True),
+    ("odd vocab bf16 k=300", workloads.Config("oddb", 2, 2, 1, 64, 64, "bf16", "bf16", "bf16", 12345, 8,
+                                              tree="ddtree", draft_rule="tree"), 0.3, 300, False),
+]
+
+
+@pytest.mark.parametrize("label,cfg,T,k,special", TOPK_CASES, ids=[c[0] for c in TOPK_CASES])
+def test_sample_accept_topk(sv, label, cfg, T, k, special):
+    """Top-k stochastic verification: samples, accept length, path and tokens
+    equal the oracle's bit for bit.  Special rows: one all-equal row (every
+    logit ties at the k-th value: the candidate list overflows and the
+    whole-row passes decide) and one row whose largest value is shared by a
+    quarter of the vocabulary."""
+    say(f"[sample-topk] {label}")
+    rng = np.random.default_rng(43)
+    case = workloads.make_case(cfg, seed=6)
+    logits = case.logits.copy()
+    if special:
+        V = logits.shape[-1]
+        logits[0, 0, :] = logits[0, 0, 0]
+        ties = rng.choice(V, V // 4, replace=False)
+        logits[0, 1, ties] = logits[0, 1].max()
+    lg32 = (oracle.widen_bf16(logits) if cfg.logits_dtype == "bf16" else logits.astype(np.float64)).astype(np.float32)
+    g = (-np.log(-np.log(rng.random(logits.shape)))).astype(np.float32)
+    B, N = case.draft_ids.shape
+    ys = np.array([[oracle.sample_row_topk(lg32[b, i], g[b, i], T, k) for i in range(N)] for b in range(B)])
+    par = np.maximum(case.parent, 0)
+    drafts = np.where(rng.random((B, N)) < 0.8, ys[np.arange(B)[:, None], par], case.draft_ids).astype(np.int32)
+    from sv_harness import dev_tensor
+    acc, path, tok, y = sv.sample_accept(dev_tensor(logits, cfg.logits_dtype), dev_tensor(g, "f32"), T,
+                                         dev_tensor(drafts, "i32"), dev_tensor(case.parent, "i32"), top_k=k)
+    torch.cuda.synchronize()
+    r_y, r_acc, r_path, r_tok = oracle.sample_accept(lg32, g, T, drafts, case.parent, top_k=k)
+    np.testing.assert_array_equal(y.cpu().numpy(), r_y)
+    np.testing.assert_array_equal(acc.cpu().numpy(), r_acc)
+    np.testing.assert_array_equal(path.cpu().numpy(), r_path)
+    np.testing.assert_array_equal(tok.cpu().numpy(), r_tok)
+    say(f"    accept_len={r_acc.tolist()}")
+
+
 # ---------------------------------------------------------------------------
 # compaction
 # ---------------------------------------------------------------------------
