@@ -80,6 +80,15 @@ def measured_traffic(workload, per_launch_bytes):
     return ent.get("bytes_per_call")
 
 
+def _blas_threads():
+    """Threads numpy's BLAS may use (the oracle's only parallel part)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:
+        return int(os.environ.get("OMP_NUM_THREADS", "1"))
+
+
 def cpu_baseline(cfg_key, seconds):
     """The oracle (unchanged) on a sample of the same workload: whole verify
     steps on the host cores, repeated for about `seconds`."""
@@ -103,15 +112,44 @@ def cpu_baseline(cfg_key, seconds):
             break
     dt = time.perf_counter() - t0
     drafts = cfg.batch * (cfg.n_nodes - 1)
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        blas = int(os.environ.get("OMP_NUM_THREADS", "1"))
-    return {"value": drafts * steps / dt, "unit": "verified draft tokens/s", "cores": int(blas),
+    return {"value": drafts * steps / dt, "unit": "verified draft tokens/s", "cores": _blas_threads(),
             "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
             "sample": f"{steps} whole verify steps of the {cfg.name} workload (attention, argmax + walk, "
                       f"compaction) in {dt:.1f} s, fp64 numpy"}
+
+
+def recurrent_cpu_baseline(key, seconds):
+    """The oracle (unchanged) on a sample of the recurrent workload: the tree
+    conv, the tree recurrence and the commit of one layer over the first value
+    heads (a key head's worth at a time), repeated for about `seconds`; the
+    time is scaled to all heads."""
+    import oracle
+    import workloads
+    cfg = workloads.DELTA_CONFIGS[key]
+    c = workloads.make_delta_case(cfg, seed=2)
+    f64 = (lambda a: oracle.widen_bf16(a)) if cfg.dtype == "bf16" else (lambda a: np.asarray(a, np.float64))
+    rep = cfg.n_v_heads // cfg.n_k_heads
+    q, k, v = f64(c.q)[:, :, :1], f64(c.k)[:, :, :1], f64(c.v)[:, :, :rep]
+    par = c.parent if cfg.tree != "chain" else None
+    x, cs = f64(c.x), f64(c.conv_state)
+    t0 = time.perf_counter()
+    oracle.conv_tree(x, cs, c.conv_weight, c.conv_bias, par)           # every channel, once
+    t_conv = time.perf_counter() - t0
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        o, st = oracle.delta_net_tree(q, k, v, c.g[:, :, :rep], c.beta[:, :, :rep], c.state[:, :rep], par)
+        oracle.recurrent_commit(st, c.state[:, :rep], c.x, c.conv_state, c.path, c.accept_len)
+        calls += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    per_call = t_conv + dt / calls * (cfg.n_v_heads / rep)
+    return {"value": round(per_call * 1e6, 1), "unit": "us per layer call (conv + tree recurrence + commit)",
+            "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"the conv over all channels once ({t_conv * 1e3:.1f} ms), then {calls} tree recurrences + "
+                      f"commits on {rep} of {cfg.n_v_heads} value heads in {dt:.1f} s, scaled x{cfg.n_v_heads // rep} "
+                      f"to all heads; fp64 numpy"}
 
 
 def delta_algorithmic_bytes(cfg):
@@ -400,6 +438,8 @@ def main():
     }
     if args.recurrent != "none":
         rec["recurrent"] = recurrent_bench(sv, dev, args.recurrent, args.steps, args.rotate_bytes, capture, timed)
+        if not args.no_cpu_baseline:
+            rec["recurrent"]["cpu_baseline"] = recurrent_cpu_baseline(args.recurrent, min(5.0, args.cpu_seconds))
     a_host = acc.cpu().numpy()
     rec["accepted_tokens_per_step"] = int(np.sum(a_host + 1))
     if not args.no_cpu_baseline:
