@@ -24,7 +24,7 @@ __all__ = [
     "verify_attn", "verify_attn_workspace_size", "greedy_accept", "greedy_accept_workspace_size",
     "kv_compact", "greedy_accept_compact", "kv_append", "sample_accept", "set_option", "SV_OPT_ATTN_TARGET_WGS", "SV_OPT_ARGMAX_CHUNK", "SV_OPT_ATTN_ROWBLOCKS",
     "SV_OPT_ATTN_POSGROUPS", "SV_OPT_ATTN_OCCUPANCY", "SV_F16",
-    "ssm_conv_tree", "gated_delta_net_tree", "recurrent_commit",
+    "ssm_conv_tree", "gated_delta_net_tree", "recurrent_commit", "tree_schedule",
 ]
 
 SV_F32, SV_BF16, SV_Q4, SV_F16 = 0, 1, 2, 3
@@ -91,7 +91,9 @@ lib.sv_ssm_conv_tree.restype = _I
 lib.sv_ssm_conv_tree.argtypes = [_I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _I, _P, _P]
 lib.sv_gated_delta_net_tree.restype = _I
 lib.sv_gated_delta_net_tree.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, ctypes.c_int64, ctypes.c_int64, _I,
-                                        _P, _P, _P, _P, ctypes.c_float, _P, _P, _I, _P]
+                                        _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _I, _P]
+lib.sv_tree_schedule.restype = _I
+lib.sv_tree_schedule.argtypes = [_I, _I, _P, _P, _P]
 lib.sv_recurrent_commit.restype = _I
 lib.sv_recurrent_commit.argtypes = [_I, _I, _I, _I, _I, _P, _I, _P, _I, _I, _P, _P, _I, _P, _P, _P]
 lib.sv_error_string.restype = ctypes.c_char_p
@@ -474,10 +476,22 @@ def _token_stride(t: torch.Tensor, name: str) -> int:
     return s[1]
 
 
+def tree_schedule(parent: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The visiting order words of every tree in ``parent [B, N]`` (int32 ``[B, 64]``),
+    shared by the recurrent layers of one verify step."""
+    _i32(parent, "parent")
+    B, N = parent.shape
+    if out is None:
+        out = torch.empty((B, 64), dtype=torch.int32, device=parent.device)
+    rc = lib.sv_tree_schedule(B, N, _ptr(parent), _ptr(out), _stream(parent.device))
+    _check(rc, "sv_tree_schedule")
+    return out
+
+
 def gated_delta_net_tree(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
                          state: torch.Tensor, parent: Optional[torch.Tensor] = None, scale: float = 0.0,
                          state_dtype: torch.dtype = torch.float16, out: Optional[torch.Tensor] = None,
-                         state_nodes: Optional[torch.Tensor] = None):
+                         state_nodes: Optional[torch.Tensor] = None, schedule: Optional[torch.Tensor] = None):
     """Gated delta rule over the verify tree: returns ``(out [B, N, Hv, Dv],
     state_nodes [B, N, Hv, Dv, Dk])``.  ``q``/``k`` ``[B, N, Hk, Dk]`` and ``v``
     ``[B, N, Hv, Dv]`` (fp32 or bf16; views into one packed buffer are fine),
@@ -496,6 +510,10 @@ def gated_delta_net_tree(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: t
         raise ValueError("state must be a contiguous float32 [B, Hv, Dv, Dk] tensor")
     if parent is not None:
         _i32(parent, "parent")
+    if schedule is not None:
+        _i32(schedule, "schedule")
+        if schedule.shape != (B, 64):
+            raise ValueError("schedule must be int32 [B, 64] from tree_schedule")
     if out is None:
         out = torch.empty((B, N, Hv, Dv), dtype=q.dtype, device=q.device)
     if state_nodes is None:
@@ -503,7 +521,8 @@ def gated_delta_net_tree(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: t
     if state_nodes.shape != (B, N, Hv, Dv, Dk) or not state_nodes.is_contiguous():
         raise ValueError("state_nodes must be a contiguous [B, N, Hv, Dv, Dk] tensor")
     rc = lib.sv_gated_delta_net_tree(B, N, Hk, Hv, Dk, Dv, _ptr(q), _ptr(k), _ptr(v), sq, sv_, _dtype_code(q),
-                                     _ptr(g), _ptr(beta), _ptr(state), _ptr(parent), float(scale), _ptr(out),
+                                     _ptr(g), _ptr(beta), _ptr(state), _ptr(parent), _ptr(schedule), float(scale),
+                                     _ptr(out),
                                      _ptr(state_nodes), _state_code(state_nodes), _stream(q.device))
     _check(rc, "sv_gated_delta_net_tree")
     return out, state_nodes

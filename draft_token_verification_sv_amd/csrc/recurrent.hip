@@ -15,8 +15,9 @@
 //   commit_kernel       the accepted node's state into the committed state and
 //                       the accepted path's last K-1 inputs into the conv state.
 //
-// delta_tree_kernel: one workgroup of 4 waves per (sequence, value head, block
-// of 16 value rows); lane (jr, rg) of a wave owns value row jr and R = Dk/16 of
+// delta_tree_kernel: one workgroup of 8 waves (4 for trees of more than 32
+// nodes) per (sequence, value head, block of 4 value rows per wave); lane
+// (jr, rg) of a wave owns value row jr and R = Dk/16 of
 // the key columns, in chunks of VEC contiguous columns spaced 16*VEC apart (so
 // the 16 lanes of a row store the row's whole span of the per-node buffer), and
 // the row sums are DPP reductions within a 16-lane row.  The state never leaves
@@ -132,6 +133,10 @@ __global__ __launch_bounds__(256) void conv_tree_kernel(ConvTreeParams p) {
 // gated delta rule over the tree, every node's state persisted
 // ---------------------------------------------------------------------------
 
+// wavefronts per workgroup (4 value rows each): 8, or 4 for trees of up to
+// 64 nodes (whose q / k staging and parked states fill the LDS)
+constexpr int delta_waves(int nmax) { return nmax <= 32 ? 8 : 4; }
+
 template <int NMAX>
 struct SlotCount {
     static constexpr int value = NMAX <= 16 ? 3 : (NMAX <= 32 ? 4 : 5);   // floor(log2(NMAX+1)) - 1
@@ -158,24 +163,119 @@ __device__ __forceinline__ f32x4 raw_f32(u32x2 u) {
                  bf16_bits_to_f32(u[1] & 0xFFFFu), bf16_bits_to_f32(u[1] >> 16)};
 }
 
+// The visiting order of one tree, one lane per node (par: this lane's valid
+// parent or -1), by all `nw` wavefronts of the workgroup together (every
+// thread calls it; the loops over nodes are split over the wavefronts):
+// depth-first, each node's children by subtree size with the largest last.
+// Wavefront 0 writes one word per preorder position into sched_s:
+// node | restore << 8 | save << 16.  cnt_s: 64 ints, part_s: 64 * nw ints.
+__device__ void tree_order(int par, int N, int *cnt_s, int *part_s, int *sched_s) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const bool live = lane < N;
+    int pos = lane, slot = 0, nch = lane < N - 1 ? 1 : 0, pre = 0;
+    const bool is_chain = __ballot(live && par != lane - 1) == 0ull;   // the same in every wavefront
+    if (!is_chain) {
+        // ancestor-or-self sets by pointer doubling (depth < 64)
+        uint64_t anc = live ? (1ull << lane) : 0ull;
+        int jp = par;
+#pragma unroll 1
+        for (int r = 0; r < 6; ++r) {
+            if (__ballot(jp >= 0) == 0ull) break;
+            const int src = jp >= 0 ? jp : lane;
+            const uint32_t alo = (uint32_t)__shfl((int)(uint32_t)anc, src, 64);
+            const uint32_t ahi = (uint32_t)__shfl((int)(uint32_t)(anc >> 32), src, 64);
+            const int jp2 = __shfl(jp, src, 64);
+            if (jp >= 0) {
+                anc |= ((uint64_t)ahi << 32) | alo;
+                jp = jp2;
+            }
+        }
+        // subtree sizes and child counts: column counts of the ancestor sets
+#pragma unroll 1
+        for (int i = wave; i < N; i += nw) {
+            const int c1 = __popcll(__ballot(((anc >> i) & 1ull) != 0ull));
+            const int c2 = __popcll(__ballot(par == i));
+            if (lane == 0) cnt_s[i] = c1 | (c2 << 8);
+        }
+        __syncthreads();
+        const int cw = cnt_s[min(lane, N - 1)];
+        const int size = live ? (cw & 255) : 0;
+        nch = live ? (cw >> 8) : 0;
+        // siblings ordered by (subtree size, index), the largest last: the
+        // sizes of the siblings before this node, and whether one comes after
+        int prep = 0, later = 0;
+#pragma unroll 1
+        for (int j = wave; j < N; j += nw) {
+            const int pj = __builtin_amdgcn_readlane(par, j);
+            const int sj = __builtin_amdgcn_readlane(size, j);
+            const bool sib = pj == par && j != lane;
+            const bool before = sj < size || (sj == size && j < lane);
+            prep += (sib && before) ? sj : 0;
+            later |= (sib && !before) ? 1 : 0;
+        }
+        part_s[wave * 64 + lane] = prep | (later << 16);
+        __syncthreads();
+        int later_all = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < nw; ++w2) {
+            const int v = part_s[w2 * 64 + lane];
+            pre += v & 0xFFFF;
+            later_all |= v >> 16;
+        }
+        // preorder position = sum of (1 + pre) along the root path, slot =
+        // number of non-largest children on it: path sums by pointer doubling
+        int aw = live ? 1 + pre : 0, al = (par >= 0 && later_all) ? 1 : 0;
+        jp = par;
+#pragma unroll 1
+        for (int r = 0; r < 6; ++r) {
+            if (__ballot(jp >= 0) == 0ull) break;
+            const int src = jp >= 0 ? jp : lane;
+            const int aw2 = __shfl(aw, src, 64);
+            const int al2 = __shfl(al, src, 64);
+            const int jp2 = __shfl(jp, src, 64);
+            if (jp >= 0) {
+                aw += aw2;
+                al += al2;
+                jp = jp2;
+            }
+        }
+        pos = live ? aw - 1 : -1;
+        slot = al;
+    }
+    // one word per preorder position: node | restore << 8 | save << 16;
+    // restore 0: the parent's state is in registers (a first child comes
+    // right after its parent; the first top node starts from the committed
+    // state already loaded), 1: the committed state, 2 + s: slot s;
+    // save 1 + s: park the state in slot s
+    if (wave == 0) {
+        const int pslot = __shfl(slot, par >= 0 ? par : 0, 64);
+        if (live) {
+            const int rc = (pre == 0 && (par >= 0 || pos == 0)) ? 0 : (par < 0 ? 1 : 2 + pslot);
+            const int sc = nch >= 2 ? 1 + slot : 0;
+            sched_s[pos] = lane | (rc << 8) | (sc << 16);
+        }
+    }
+}
+
 template <int R, int NMAX, bool TREE, int DT, int SDT>
-__global__ __launch_bounds__(256) void delta_tree_kernel(DeltaParams p) {
+__global__ __launch_bounds__(64 * delta_waves(NMAX)) void delta_tree_kernel(DeltaParams p) {
     constexpr int DK = 16 * R;
     constexpr int VEC = (SDT == SV_F16 && R >= 8) ? 8 : 4;   // contiguous key columns per chunk
     constexpr int NCH = R / VEC;                             // chunks per lane
     constexpr int NSLOT = TREE ? SlotCount<NMAX>::value : 0;
-    constexpr int QK_IT = (NMAX * DK / 4 + 255) / 256;
-    constexpr int V_IT = (NMAX * 4 + 255) / 256;
+    constexpr int WAVES = delta_waves(NMAX), NT = 64 * WAVES, RPB = 4 * WAVES;   // threads, value rows per workgroup
+    constexpr int QK_IT = (NMAX * DK / 4 + NT - 1) / NT;
+    constexpr int V_IT = (NMAX * RPB / 4 + NT - 1) / NT;
     static_assert(R % VEC == 0 && R % 4 == 0, "chunking");
     using Raw = typename Raw4<DT>::type;
 
     __shared__ __attribute__((aligned(16))) float k_s[NMAX * DK];
     __shared__ __attribute__((aligned(16))) float q_s[NMAX * DK];
-    __shared__ __attribute__((aligned(16))) float v_s[NMAX * 16];
+    __shared__ __attribute__((aligned(16))) float v_s[NMAX * RPB];
     __shared__ float a_s[NMAX], b_s[NMAX];
-    __shared__ int sched_s[TREE ? 64 : 1], cnt_s[TREE ? 64 : 1], part_s[TREE ? 256 : 1];
-    __shared__ float opart_s[NMAX * 4 * 16];            // [node][wave][row * 4 + quad]
-    __shared__ __attribute__((aligned(16))) f32x4 slot_s[NSLOT > 0 ? NSLOT * 4 * (R / 4) * 64 : 1];
+    __shared__ int sched_s[TREE ? 64 : 1], cnt_s[TREE ? 64 : 1], part_s[TREE ? NT : 1];
+    __shared__ float opart_s[NMAX * RPB * 4];           // [node][wave][row * 4 + quad]
+    __shared__ __attribute__((aligned(16))) f32x4 slot_s[NSLOT > 0 ? NSLOT * WAVES * (R / 4) * 64 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int jb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -183,16 +283,18 @@ __global__ __launch_bounds__(256) void delta_tree_kernel(DeltaParams p) {
     const int hk = h / (Hv / p.Hk);
     const int jr = lane >> 4, rg = lane & 15;
     const int jloc = wave * 4 + jr;                   // this lane's value row in the block
-    const int jrow = jb * 16 + jloc;
+    const int jrow = jb * RPB + jloc;
     const int64_t bn = (int64_t)b * N;
 
     // ---- loads, in the order they are needed: the tree, the committed
     // state, then q, k (all nodes, this key head), v (16 rows), decay, beta
     // (indices clamped into range; converted once the order is known) ----
-    int par = lane - 1;
+    int par = lane - 1, sched_g = lane;
     if constexpr (TREE) {
         par = -1;
-        if (lane < N) {
+        if (p.sched != nullptr) {
+            sched_g = p.sched[(int64_t)b * 64 + min(lane, N - 1)];
+        } else if (lane < N) {
             const int pr = p.parent[bn + lane];
             par = (pr >= 0 && pr < lane) ? pr : -1;
         }
@@ -215,7 +317,7 @@ __global__ __launch_bounds__(256) void delta_tree_kernel(DeltaParams p) {
     const int nqk = N * (DK / 4);
 #pragma unroll
     for (int it = 0; it < QK_IT; ++it) {
-        const int e = min(tid + it * 256, nqk - 1);
+        const int e = min(tid + it * NT, nqk - 1);
         const int i = e / (DK / 4), c4 = e - i * (DK / 4);
         const int64_t off = (bn + i) * p.qk_stride + (int64_t)hk * DK + 4 * c4;
         qr[it] = load_raw4<DT>(p.q, off);
@@ -223,107 +325,24 @@ __global__ __launch_bounds__(256) void delta_tree_kernel(DeltaParams p) {
     }
 #pragma unroll
     for (int it = 0; it < V_IT; ++it) {
-        const int e = min(tid + it * 256, N * 4 - 1);
-        const int i = e >> 2, c4 = e & 3;
-        vr[it] = load_raw4<DT>(p.v, (bn + i) * p.v_stride + (int64_t)h * Dv + jb * 16 + 4 * c4);
+        const int e = min(tid + it * NT, N * (RPB / 4) - 1);
+        const int i = e / (RPB / 4), c4 = e % (RPB / 4);
+        vr[it] = load_raw4<DT>(p.v, (bn + i) * p.v_stride + (int64_t)h * Dv + jb * RPB + 4 * c4);
     }
     const int gi = min(tid, N - 1);
     const float gv = p.g[(bn + gi) * Hv + h];
     const float bv = p.beta[(bn + gi) * Hv + h];
 
-    // ---- depth-first order, one lane per node (the loops over nodes are
-    // split over the 4 waves) ----
+    // ---- depth-first order: precomputed (one word per step), or computed
+    // here by the 4 wavefronts ----
     if constexpr (TREE) {
-        const bool live = lane < N;
-        int pos = lane, slot = 0, nch = lane < N - 1 ? 1 : 0, pre = 0;
-        const bool is_chain = __ballot(live && par != lane - 1) == 0ull;   // the same in every wave
-        if (!is_chain) {
-            // ancestor-or-self sets by pointer doubling (depth < 64)
-            uint64_t anc = live ? (1ull << lane) : 0ull;
-            int jp = par;
-#pragma unroll 1
-            for (int r = 0; r < 6; ++r) {
-                if (__ballot(jp >= 0) == 0ull) break;
-                const int src = jp >= 0 ? jp : lane;
-                const uint32_t alo = (uint32_t)__shfl((int)(uint32_t)anc, src, 64);
-                const uint32_t ahi = (uint32_t)__shfl((int)(uint32_t)(anc >> 32), src, 64);
-                const int jp2 = __shfl(jp, src, 64);
-                if (jp >= 0) {
-                    anc |= ((uint64_t)ahi << 32) | alo;
-                    jp = jp2;
-                }
-            }
-            // subtree sizes and child counts: column counts of the ancestor sets
-#pragma unroll 1
-            for (int i = wave; i < N; i += 4) {
-                const int c1 = __popcll(__ballot(((anc >> i) & 1ull) != 0ull));
-                const int c2 = __popcll(__ballot(par == i));
-                if (lane == 0) cnt_s[i] = c1 | (c2 << 8);
-            }
-            __syncthreads();
-            const int cw = cnt_s[min(lane, N - 1)];
-            const int size = live ? (cw & 255) : 0;
-            nch = live ? (cw >> 8) : 0;
-            // siblings ordered by (subtree size, index), the largest last: the
-            // sizes of the siblings before this node, and whether one comes after
-            int prep = 0, later = 0;
-#pragma unroll 1
-            for (int j = wave; j < N; j += 4) {
-                const int pj = __builtin_amdgcn_readlane(par, j);
-                const int sj = __builtin_amdgcn_readlane(size, j);
-                const bool sib = pj == par && j != lane;
-                const bool before = sj < size || (sj == size && j < lane);
-                prep += (sib && before) ? sj : 0;
-                later |= (sib && !before) ? 1 : 0;
-            }
-            part_s[wave * 64 + lane] = prep | (later << 16);
-            __syncthreads();
-            int later_all = 0;
-#pragma unroll
-            for (int w2 = 0; w2 < 4; ++w2) {
-                const int v = part_s[w2 * 64 + lane];
-                pre += v & 0xFFFF;
-                later_all |= v >> 16;
-            }
-            // preorder position = sum of (1 + pre) along the root path, slot =
-            // number of non-largest children on it: path sums by pointer doubling
-            int aw = live ? 1 + pre : 0, al = (par >= 0 && later_all) ? 1 : 0;
-            jp = par;
-#pragma unroll 1
-            for (int r = 0; r < 6; ++r) {
-                if (__ballot(jp >= 0) == 0ull) break;
-                const int src = jp >= 0 ? jp : lane;
-                const int aw2 = __shfl(aw, src, 64);
-                const int al2 = __shfl(al, src, 64);
-                const int jp2 = __shfl(jp, src, 64);
-                if (jp >= 0) {
-                    aw += aw2;
-                    al += al2;
-                    jp = jp2;
-                }
-            }
-            pos = live ? aw - 1 : -1;
-            slot = al;
-        }
-        // one word per preorder position: node | restore << 8 | save << 16;
-        // restore 0: the parent's state is in registers (a first child comes
-        // right after its parent; the first top node starts from the committed
-        // state already loaded), 1: the committed state, 2 + s: slot s;
-        // save 1 + s: park the state in slot s
-        if (wave == 0) {
-            const int pslot = __shfl(slot, par >= 0 ? par : 0, 64);
-            if (live) {
-                const int rc = (pre == 0 && (par >= 0 || pos == 0)) ? 0 : (par < 0 ? 1 : 2 + pslot);
-                const int sc = nch >= 2 ? 1 + slot : 0;
-                sched_s[pos] = lane | (rc << 8) | (sc << 16);
-            }
-        }
+        if (p.sched == nullptr) tree_order(par, N, cnt_s, part_s, sched_s);
     }
 
     // ---- operands into LDS ----
 #pragma unroll
     for (int it = 0; it < QK_IT; ++it) {
-        const int e = tid + it * 256;
+        const int e = tid + it * NT;
         if (e < nqk) {
             *(f32x4 *)&q_s[4 * e] = raw_f32(qr[it]);      // node e / (DK/4), columns 4 (e % (DK/4)) ..
             *(f32x4 *)&k_s[4 * e] = raw_f32(kr[it]);
@@ -331,8 +350,8 @@ __global__ __launch_bounds__(256) void delta_tree_kernel(DeltaParams p) {
     }
 #pragma unroll
     for (int it = 0; it < V_IT; ++it) {
-        const int e = tid + it * 256;
-        if (e < N * 4) *(f32x4 *)&v_s[4 * e] = raw_f32(vr[it]);
+        const int e = tid + it * NT;
+        if (e < N * (RPB / 4)) *(f32x4 *)&v_s[4 * e] = raw_f32(vr[it]);
     }
     if (tid < N) {
         a_s[tid] = expf(gv);
@@ -340,16 +359,16 @@ __global__ __launch_bounds__(256) void delta_tree_kernel(DeltaParams p) {
     }
     __syncthreads();
     int schedv = lane;                                 // word of preorder position `lane`
-    if constexpr (TREE) schedv = sched_s[min(lane, N - 1)];
+    if constexpr (TREE) schedv = p.sched != nullptr ? sched_g : sched_s[min(lane, N - 1)];
 
     // ---- the walk: the next node's operands (and parked parent state) are
     // read from LDS during the step before ----
     const float scale = p.scale;
     // node x's state row of this lane: st_base + x * node_elems + lane_off
-    const int64_t st_base = (bn * Hv + h) * (int64_t)Dv * DK + (int64_t)jb * 16 * DK;
+    const int64_t st_base = (bn * Hv + h) * (int64_t)Dv * DK + (int64_t)jb * RPB * DK;
     const uint32_t node_elems = (uint32_t)Hv * (uint32_t)Dv * DK;
     const uint32_t lane_off = (uint32_t)jloc * DK + rg * VEC;
-    f32x4 *my_slot = slot_s + wave * (R / 4) * 64 + lane;           // + (s * 4 * (R/4) + t) * 64
+    f32x4 *my_slot = slot_s + wave * (R / 4) * 64 + lane;           // + (s * waves * (R/4) + t) * 64
     auto fetch = [&](int x, float (&kd)[R], float (&qd)[R], float &vd, float &ad, float &bd) {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
@@ -365,14 +384,14 @@ __global__ __launch_bounds__(256) void delta_tree_kernel(DeltaParams p) {
                 }
             }
         }
-        vd = v_s[x * 16 + jloc];
+        vd = v_s[x * RPB + jloc];
         ad = a_s[x];
         bd = b_s[x];
     };
     float Sr[R];                                        // a parked state read ahead
     auto step = [&](int ks, int word, const float (&kk)[R], const float (&qq)[R], float vx, float a, float bt,
                     float (&kn)[R], float (&qn)[R], float &vn, float &an, float &bn_) -> int {
-        const int x = word & 63;
+        const int x = min(word & 63, N - 1);
         if constexpr (TREE) {
             const int rc = (word >> 8) & 255;
             if (rc == 1) {
@@ -383,14 +402,14 @@ __global__ __launch_bounds__(256) void delta_tree_kernel(DeltaParams p) {
             }
         }
         const int wn = ks + 1 < N ? __builtin_amdgcn_readlane(schedv, ks + 1) : word;
-        fetch(wn & 63, kn, qn, vn, an, bn_);
+        fetch(min(wn & 63, N - 1), kn, qn, vn, an, bn_);
         if constexpr (TREE) {
             const int rcn = (wn >> 8) & 255;
             // (a node followed by a restore is a leaf: it parks nothing)
             if (rcn >= 2 && rcn - 2 < NSLOT) {
 #pragma unroll
                 for (int t = 0; t < R / 4; ++t) {
-                    const f32x4 v4 = my_slot[((rcn - 2) * 4 * (R / 4) + t) * 64];
+                    const f32x4 v4 = my_slot[((rcn - 2) * WAVES * (R / 4) + t) * 64];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) Sr[4 * t + e] = v4[e];
                 }
@@ -411,7 +430,7 @@ __global__ __launch_bounds__(256) void delta_tree_kernel(DeltaParams p) {
         float oq = (o4[0] + o4[1]) + (o4[2] + o4[3]);
         oq += dpp_f<0xB1>(oq);
         oq += dpp_f<0x4E>(oq);
-        opart_s[(x * 4 + wave) * 16 + (lane >> 2)] = oq;
+        opart_s[(x * WAVES + wave) * 16 + (lane >> 2)] = oq;
         // persist this node's state (uniform node base + per-lane offset;
         // streaming stores: the buffer is read back at most once, by the commit)
         if constexpr (SDT == SV_F32) {
@@ -443,7 +462,7 @@ __global__ __launch_bounds__(256) void delta_tree_kernel(DeltaParams p) {
             if (sc >= 1 && sc - 1 < NSLOT) {
 #pragma unroll
                 for (int t = 0; t < R / 4; ++t)
-                    my_slot[((sc - 1) * 4 * (R / 4) + t) * 64] = f32x4{S[4 * t], S[4 * t + 1], S[4 * t + 2], S[4 * t + 3]};
+                    my_slot[((sc - 1) * WAVES * (R / 4) + t) * 64] = f32x4{S[4 * t], S[4 * t + 1], S[4 * t + 2], S[4 * t + 3]};
             }
         }
         return wn;
@@ -451,7 +470,7 @@ __global__ __launch_bounds__(256) void delta_tree_kernel(DeltaParams p) {
     float kA[R], qA[R], kB[R], qB[R];
     float vA = 0.f, aA = 0.f, bA = 0.f, vB = 0.f, aB = 0.f, bB = 0.f;
     int word = __builtin_amdgcn_readlane(schedv, 0);
-    fetch(word & 63, kA, qA, vA, aA, bA);
+    fetch(min(word & 63, N - 1), kA, qA, vA, aA, bA);
 #pragma unroll 1
     for (int ks = 0; ks < N; ks += 2) {
         word = step(ks, word, kA, qA, vA, aA, bA, kB, qB, vB, aB, bB);
@@ -461,11 +480,11 @@ __global__ __launch_bounds__(256) void delta_tree_kernel(DeltaParams p) {
 
     // ---- outputs: the 4 quad sums of each (node, row), coalesced rows of 16 ----
     __syncthreads();
-    for (int e = tid; e < N * 16; e += 256) {
-        const int x = e >> 4, jl = e & 15;
-        const float *pq = &opart_s[(x * 4 + (jl >> 2)) * 16 + (jl & 3) * 4];
+    for (int e = tid; e < N * RPB; e += NT) {
+        const int x = e / RPB, jl = e % RPB;
+        const float *pq = &opart_s[(x * WAVES + (jl >> 2)) * 16 + (jl & 3) * 4];
         const float o = ((pq[0] + pq[1]) + (pq[2] + pq[3])) * scale;
-        const int64_t oi = ((bn + x) * Hv + h) * Dv + jb * 16 + jl;
+        const int64_t oi = ((bn + x) * Hv + h) * Dv + jb * RPB + jl;
         if constexpr (DT == SV_F32) ((float *)p.out)[oi] = o;
         else ((uint16_t *)p.out)[oi] = (uint16_t)f32_to_bf16_bits(o);
     }
@@ -556,6 +575,21 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitParams p) {
     }
 }
 
+// One workgroup of 4 wavefronts per sequence: the order words of its tree,
+// for every recurrent layer of the verify step to share.
+__global__ __launch_bounds__(256) void tree_schedule_kernel(const int32_t *parent, int N, int32_t *sched) {
+    __shared__ int cnt_s[64], part_s[256], sched_s[64];
+    const int b = blockIdx.x, lane = threadIdx.x & 63;
+    int par = -1;
+    if (lane < N) {
+        const int pr = parent[(int64_t)b * N + lane];
+        par = (pr >= 0 && pr < lane) ? pr : -1;
+    }
+    tree_order(par, N, cnt_s, part_s, sched_s);
+    __syncthreads();
+    if (threadIdx.x < 64) sched[(int64_t)b * 64 + lane] = lane < N ? sched_s[lane] : 0;
+}
+
 template <int DT, int K>
 hipError_t launch_conv_k(const ConvTreeParams &p, hipStream_t st) {
     const dim3 grid((unsigned)((p.C + 1023) / 1024), (unsigned)p.N, (unsigned)p.B);
@@ -565,11 +599,12 @@ hipError_t launch_conv_k(const ConvTreeParams &p, hipStream_t st) {
 
 template <int R, int NMAX, bool TREE, int DT>
 hipError_t launch_delta_s(const DeltaParams &p, int sdt, hipStream_t st) {
-    const dim3 grid((unsigned)(p.Dv / 16), (unsigned)p.Hv, (unsigned)p.B);
+    constexpr int W = delta_waves(NMAX);
+    const dim3 grid((unsigned)(p.Dv / (4 * W)), (unsigned)p.Hv, (unsigned)p.B);
     if (sdt == SV_F16)
-        hipLaunchKernelGGL((delta_tree_kernel<R, NMAX, TREE, DT, SV_F16>), grid, dim3(256), 0, st, p);
+        hipLaunchKernelGGL((delta_tree_kernel<R, NMAX, TREE, DT, SV_F16>), grid, dim3(64 * W), 0, st, p);
     else
-        hipLaunchKernelGGL((delta_tree_kernel<R, NMAX, TREE, DT, SV_F32>), grid, dim3(256), 0, st, p);
+        hipLaunchKernelGGL((delta_tree_kernel<R, NMAX, TREE, DT, SV_F32>), grid, dim3(64 * W), 0, st, p);
     return hipGetLastError();
 }
 
@@ -581,7 +616,7 @@ hipError_t launch_delta_d(const DeltaParams &p, int dt, int sdt, hipStream_t st)
 
 template <int R>
 hipError_t launch_delta_r(const DeltaParams &p, int dt, int sdt, hipStream_t st) {
-    const bool tree = p.parent != nullptr;
+    const bool tree = p.parent != nullptr || p.sched != nullptr;
     if (p.N <= 16) return tree ? launch_delta_d<R, 16, true>(p, dt, sdt, st) : launch_delta_d<R, 16, false>(p, dt, sdt, st);
     if (p.N <= 32) return tree ? launch_delta_d<R, 32, true>(p, dt, sdt, st) : launch_delta_d<R, 32, false>(p, dt, sdt, st);
     return tree ? launch_delta_d<R, 64, true>(p, dt, sdt, st) : launch_delta_d<R, 64, false>(p, dt, sdt, st);
@@ -596,6 +631,11 @@ hipError_t launch_conv_tree(const ConvTreeParams &p, int dtype, hipStream_t st) 
     }
     return p.K == 2 ? launch_conv_k<SV_BF16, 2>(p, st) : p.K == 3 ? launch_conv_k<SV_BF16, 3>(p, st)
                                                                   : launch_conv_k<SV_BF16, 4>(p, st);
+}
+
+hipError_t launch_tree_schedule(const int32_t *parent, int B, int N, int32_t *sched, hipStream_t st) {
+    hipLaunchKernelGGL(tree_schedule_kernel, dim3((unsigned)B), dim3(256), 0, st, parent, N, sched);
+    return hipGetLastError();
 }
 
 hipError_t launch_delta_tree(const DeltaParams &p, int dtype, int state_dtype, int Dk, hipStream_t st) {

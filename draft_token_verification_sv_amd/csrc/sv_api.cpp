@@ -613,11 +613,19 @@ int sv_ssm_conv_tree(int batch, int n_nodes, int channels, int kernel_width,
     return SV_OK;
 }
 
+int sv_tree_schedule(int batch, int n_nodes, const int32_t *parent, int32_t *schedule, void *stream) {
+    if (batch < 1 || batch > 65535 || n_nodes < 1 || n_nodes > 64) return SV_EINVAL;
+    if (parent == nullptr || schedule == nullptr || !aligned(parent, 4) || !aligned(schedule, 4)) return SV_EINVAL;
+    const hipError_t e = launch_tree_schedule(parent, batch, n_nodes, schedule, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return SV_OK;
+}
+
 int sv_gated_delta_net_tree(int batch, int n_nodes, int n_k_heads, int n_v_heads, int k_dim, int v_dim,
                             const void *q, const void *k, const void *v, int64_t qk_stride, int64_t v_stride,
                             int dtype, const float *g, const float *beta, const float *state,
-                            const int32_t *parent, float scale, void *out, void *state_nodes, int state_dtype,
-                            void *stream) {
+                            const int32_t *parent, const int32_t *schedule, float scale, void *out,
+                            void *state_nodes, int state_dtype, void *stream) {
     if (batch < 1 || batch > 65535 || n_nodes < 1 || n_nodes > 64) return SV_EINVAL;
     if (n_k_heads < 1 || n_v_heads < 1 || n_v_heads > 65535 || n_v_heads % n_k_heads != 0) return SV_EINVAL;
     if (k_dim != 64 && k_dim != 128) return SV_EUNSUPPORTED;
@@ -635,6 +643,7 @@ int sv_gated_delta_net_tree(int batch, int n_nodes, int n_k_heads, int n_v_heads
         !aligned(state_nodes, 16) || !aligned(g, 4) || !aligned(beta, 4) || !aligned(out, 4))
         return SV_EINVAL;
     if (parent != nullptr && !aligned(parent, 4)) return SV_EINVAL;
+    if (schedule != nullptr && !aligned(schedule, 4)) return SV_EINVAL;
     if (!isfinite(scale)) return SV_EINVAL;
     if ((uint64_t)n_nodes * n_v_heads * v_dim * k_dim > 0xFFFFFFFFull) return SV_EUNSUPPORTED;
     DeltaParams p{};
@@ -647,6 +656,7 @@ int sv_gated_delta_net_tree(int batch, int n_nodes, int n_k_heads, int n_v_heads
     p.beta = beta;
     p.state = state;
     p.parent = parent;
+    p.sched = schedule;
     p.out = out;
     p.state_nodes = state_nodes;
     p.B = batch;

@@ -92,6 +92,7 @@ struct DeltaParams {
     const float *g, *beta;        // [B][N][Hv]
     const float *state;           // [B][Hv][Dv][Dk]
     const int32_t *parent;        // [B][N] or nullptr (chains)
+    const int32_t *sched;         // [B][64] order words from tree_schedule_kernel, or nullptr
     void *out;                    // [B][N][Hv][Dv]
     void *state_nodes;            // [B][N][Hv][Dv][Dk]
     int B, N, Hk, Hv, Dv;
@@ -127,5 +128,6 @@ hipError_t launch_append(const AppendParams &p, int src_dtype, int dst_dtype, hi
 hipError_t launch_conv_tree(const ConvTreeParams &p, int dtype, hipStream_t s);
 hipError_t launch_delta_tree(const DeltaParams &p, int dtype, int state_dtype, int Dk, hipStream_t s);
 hipError_t launch_commit(const CommitParams &p, int state_dtype, int dtype, hipStream_t s);
+hipError_t launch_tree_schedule(const int32_t *parent, int B, int N, int32_t *sched, hipStream_t s);
 
 }  // namespace sv

@@ -343,6 +343,9 @@ int sv_ssm_conv_tree(int batch, int n_nodes, int channels, int kernel_width,
  * out         device [batch][N][n_v_heads][v_dim] in dtype.
  * state_nodes device [batch][N][n_v_heads][v_dim][k_dim] in state_dtype
  *             (SV_F32, or SV_F16 rounded to nearest even): every node's state.
+ * schedule    device int32 [batch][64] from sv_tree_schedule for the same
+ *             parent array, or NULL (the kernel then derives the visiting
+ *             order from parent itself; with a schedule, parent is not read).
  * scale <= 0 selects 1/sqrt(k_dim).  k_dim 64 or 128, and N * n_v_heads * v_dim *
  * k_dim below 2^32 (else SV_EUNSUPPORTED);
  * v_dim a multiple of 32.  Arithmetic in fp32.
@@ -350,8 +353,19 @@ int sv_ssm_conv_tree(int batch, int n_nodes, int channels, int kernel_width,
 int sv_gated_delta_net_tree(int batch, int n_nodes, int n_k_heads, int n_v_heads, int k_dim, int v_dim,
                             const void *q, const void *k, const void *v, int64_t qk_stride, int64_t v_stride,
                             int dtype, const float *g, const float *beta, const float *state,
-                            const int32_t *parent, float scale, void *out, void *state_nodes, int state_dtype,
-                            void *stream);
+                            const int32_t *parent, const int32_t *schedule, float scale, void *out,
+                            void *state_nodes, int state_dtype, void *stream);
+
+/*
+ * sv_tree_schedule -- the visiting order sv_gated_delta_net_tree uses for a
+ * tree, computed once per verify step and shared by every recurrent layer
+ * (the tree is the same in all of them).  schedule: device int32
+ * [batch][64]; entry t of a sequence is the t-th node of a depth-first walk
+ * (children by subtree size, the largest last) | (where its parent's state
+ * is: 0 registers, 1 the committed state, 2 + s parked slot s) << 8 | (the
+ * slot to park its own state in, plus 1, or 0) << 16.  parent as above.
+ */
+int sv_tree_schedule(int batch, int n_nodes, const int32_t *parent, int32_t *schedule, void *stream);
 
 /*
  * sv_recurrent_commit -- after acceptance: state[b] <- state_nodes[b][path[b][a]]

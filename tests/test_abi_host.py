@@ -206,14 +206,17 @@ def test_recurrent_checks(lib):
     assert conv(dt=2) == -1 and conv(act=2) == -1 and conv(x=0) == -1 and conv(x=FAKE + 8) == -1
     assert conv(bias=ctypes.c_void_p(FAKE + 4)) == -1
 
-    def delta(N=22, Hk=16, Hv=48, Dk=128, Dv=128, qs=0, vs=0, dt=1, sdt=3, g=FAKE, scale=0.0, q=FAKE):
+    def delta(N=22, Hk=16, Hv=48, Dk=128, Dv=128, qs=0, vs=0, dt=1, sdt=3, g=FAKE, scale=0.0, q=FAKE, sched=0):
         return lib.sv_gated_delta_net_tree(1, N, Hk, Hv, Dk, Dv, ctypes.c_void_p(q), P, P, I64(qs), I64(vs), dt,
-                                           ctypes.c_void_p(g), P, P, None, ctypes.c_float(scale), P, P, sdt, None)
+                                           ctypes.c_void_p(g), P, P, None, ctypes.c_void_p(sched),
+                                           ctypes.c_float(scale), P, P, sdt, None)
     assert delta(N=65) == -1 and delta(Hv=40) == -1            # value heads a multiple of key heads
     assert delta(Dk=256) == -2 and delta(Dk=96) == -2          # key dims 64 and 128
     assert delta(Dv=48) == -1 and delta(dt=2) == -1 and delta(sdt=1) == -1
     assert delta(qs=2048 + 4) == -1 and delta(qs=1024) == -1 and delta(vs=6000) == -1
     assert delta(g=0) == -1 and delta(q=FAKE + 8) == -1 and delta(scale=float("nan")) == -1
+    assert delta(sched=FAKE + 2) == -1
+    assert lib.sv_tree_schedule(1, 65, P, P, None) == -1 and lib.sv_tree_schedule(1, 22, None, P, None) == -1
 
     def commit(N=22, K=4, sdt=3, path=FAKE, Dk=128):
         return lib.sv_recurrent_commit(1, N, 48, Dk, 128, P, sdt, P, 10240, K, P, P, 1, ctypes.c_void_p(path), P,

@@ -240,3 +240,52 @@ def test_recurrent_commit(sv, case_):
     got_c = cs.cpu().view(torch.int16).numpy().view(np.uint16) if cfg.dtype == "bf16" else cs.cpu().numpy()
     assert np.array_equal(got_c, ref_c)
     say(f"    accept_len={alen.tolist()} bit-exact")
+
+
+SCHED_KINDS = [("D2 ddtree22", D["D2"], "case"), ("N=64 binary", dataclasses.replace(D["D2"], n_nodes=64), "binary"),
+               ("N=16 star", dataclasses.replace(D["D3"], n_nodes=16), "star"),
+               ("N=23 forest", dataclasses.replace(D["D2"], n_nodes=23), "forest"),
+               ("chain as array", D["D3"], "chain"), ("N=1", dataclasses.replace(D["D3"], n_nodes=1), "chain"),
+               ("batch3 trees N=40", dataclasses.replace(D["D2"], batch=3, n_nodes=40), "case")]
+
+
+def _check_schedule_words(words, parent_row):
+    """The words visit every node once, each from its parent's state: replay
+    them with symbolic states (node ids) and bounded slots."""
+    N = len(parent_row)
+    par = [int(p) if 0 <= int(p) < i else -1 for i, p in enumerate(parent_row)]
+    nodes = [int(w) & 63 for w in words[:N]]
+    assert sorted(nodes) == list(range(N))
+    reg, slots = -1, {}
+    for t, w in enumerate(words[:N]):
+        x, rc, sc = int(w) & 63, (int(w) >> 8) & 255, int(w) >> 16
+        if rc == 1:
+            reg = -1
+        elif rc >= 2:
+            reg = slots[rc - 2]
+        assert reg == par[x], (t, x, reg, par[x])
+        reg = x
+        if sc:
+            assert sc - 1 < 5
+            slots[sc - 1] = x
+
+
+@pytest.mark.parametrize("case_", SCHED_KINDS, ids=[c[0] for c in SCHED_KINDS])
+def test_tree_schedule_shared_by_layers(sv, case_):
+    """sv_tree_schedule's words are a valid walk of each tree, and the recurrence
+    driven by them gives the same bits as the order computed in the kernel."""
+    label, cfg, kind = case_
+    say(f"[schedule] {label}")
+    c = workloads.make_delta_case(cfg, 49)
+    par = _parents(kind, c)
+    pd = dev_tensor(par, "i32")
+    sched = sv.tree_schedule(pd)
+    torch.cuda.synchronize()
+    words = sched.cpu().numpy()
+    for b in range(cfg.batch):
+        _check_schedule_words(words[b], par[b])
+    o1, s1 = _delta_run(sv, c, par, "f16")
+    o2, s2 = _delta_run(sv, c, par, "f16", schedule=sched)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(s1.view(torch.int16), s2.view(torch.int16))
