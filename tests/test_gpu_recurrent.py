@@ -289,3 +289,49 @@ def test_tree_schedule_shared_by_layers(sv, case_):
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(s1.view(torch.int16), s2.view(torch.int16))
+
+
+def test_recurrent_calls_replay_in_a_graph(sv):
+    """The schedule, conv, tree recurrence and commit captured in one HIP graph
+    and replayed three times, with eager work between the replays, give the
+    eager results every time (the calls launch kernels only: no memsets)."""
+    cfg = D["D2"]
+    c = workloads.make_delta_case(cfg, 51)
+    x, cs0 = dev_tensor(c.x, cfg.dtype), dev_tensor(c.conv_state, cfg.dtype)
+    w, bias = dev_tensor(c.conv_weight, "f32"), dev_tensor(c.conv_bias, "f32")
+    q, k, v = (dev_tensor(a, cfg.dtype) for a in (c.q, c.k, c.v))
+    g, beta, st0 = (dev_tensor(a, "f32") for a in (c.g, c.beta, c.state))
+    pd, path, alen = dev_tensor(c.parent, "i32"), dev_tensor(c.path, "i32"), dev_tensor(c.accept_len, "i32")
+    B, N, Hv, Dv, Dk = cfg.batch, cfg.n_nodes, cfg.n_v_heads, cfg.v_dim, cfg.k_dim
+    sched = torch.empty((B, 64), dtype=torch.int32, device="cuda")
+    conv_out = torch.empty_like(x)
+    d_out = torch.empty((B, N, Hv, Dv), dtype=q.dtype, device="cuda")
+    nodes = torch.empty((B, N, Hv, Dv, Dk), dtype=torch.float16, device="cuda")
+    st, cs = st0.clone(), cs0.clone()
+
+    def calls():
+        sv.tree_schedule(pd, out=sched)
+        sv.ssm_conv_tree(x, cs, w, bias, pd, out=conv_out)
+        sv.gated_delta_net_tree(q, k, v, g, beta, st, pd, out=d_out, state_nodes=nodes, schedule=sched)
+        sv.recurrent_commit(nodes, st, x, cs, path, alen)
+
+    calls()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (sched, conv_out, d_out, nodes, st, cs)]
+    st.copy_(st0)
+    cs.copy_(cs0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        st.copy_(st0)                                   # eager work between the replays
+        cs.copy_(cs0)
+        conv_out.zero_()
+        d_out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((sched, conv_out, d_out, nodes, st, cs), ref):
+            assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), rep
