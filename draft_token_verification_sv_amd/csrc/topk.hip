@@ -35,7 +35,10 @@ __device__ __forceinline__ uint32_t order_key(float v) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// the value of an order key; keys below that of -inf (a bound truncated from
+// the maximum of a thread that saw no logit) read as -inf
 __device__ __forceinline__ float key_value(uint32_t k) {
+    if (k <= 0x007FFFFFu) return -INFINITY;
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 

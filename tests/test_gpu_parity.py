@@ -378,6 +378,8 @@ TOPK_CASES = [
                                            tree="ddtree", draft_rule="tree"), 2.0, 7, True),
     ("odd vocab bf16 k=300", workloads.Config("oddb", 2, 2, 1, 64, 64, "bf16", "bf16", "bf16", 12345, 8,
                                               tree="ddtree", draft_rule="tree"), 0.3, 300, False),
+    # 625 16-byte groups for 1024 threads: k above the threads that see a logit
+    ("vocab 5000 k=700", workloads.Config("v5k", 1, 2, 1, 64, 3, "bf16", "bf16", "bf16", 5000, 8), 1.0, 700, False),
 ]
 
 
