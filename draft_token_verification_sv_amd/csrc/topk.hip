@@ -117,13 +117,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_sample_accept_kernel(Accept
 
     // every logit of this thread's slice: f(value, index)
     auto each_logit = [&](auto f) {
-        for (int gi = tid; gi < nfull; gi += 4 * kTopkThreads) {
-            u32x4 v[4];
+        // batches of 4 loads per thread, the next batch in flight while one is used
+        auto load4 = [&](int gi, u32x4 (&v)[4]) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int g = min(gi + u * kTopkThreads, nfull - 1);
                 v[u] = *(const u32x4 *)(base + (int64_t)g * 16);
             }
+        };
+        auto use4 = [&](int gi, const u32x4 (&v)[4]) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int g = gi + u * kTopkThreads;
@@ -138,6 +140,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_sample_accept_kernel(Accept
                         }
                     }
                 }
+            }
+        };
+        if (tid < nfull) {
+            u32x4 va[4], vb[4];
+            load4(tid, va);
+            for (int gi = tid; gi < nfull; gi += 8 * kTopkThreads) {
+                const int g2 = gi + 4 * kTopkThreads;
+                if (g2 < nfull) load4(g2, vb);
+                use4(gi, va);
+                if (g2 >= nfull) break;
+                if (g2 + 4 * kTopkThreads < nfull) load4(g2 + 4 * kTopkThreads, va);
+                use4(g2, vb);
             }
         }
         for (int e = nfull * EPL + tid; e < V; e += kTopkThreads) {      // tail (V not a multiple of EPL)
@@ -183,7 +197,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_sample_accept_kernel(Accept
             [&](auto f) {
                 for (int s = tid; s < ncand; s += kTopkThreads) f(ckey[s]);
             },
-            k, 4, hist, sh);
+            k, F32 ? 4 : 2, hist, sh);                  // bf16 logits: the keys' low 16 bits are zero
         for (int s = tid; s < ncand; s += kTopkThreads) {
             if (ckey[s] >= kth) {
                 const int e = cidx[s];
