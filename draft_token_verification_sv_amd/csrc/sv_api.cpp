@@ -129,10 +129,12 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
     // Two workgroups per CU on the pipelined kernel (half-size rings, stages of
     // <= 32 KB, one row tile per wavefront): twice the units balance uneven
     // sequences better and each workgroup's start overlaps the other's work.
-    // Default for batches (8 paged sequences of 1K-16K positions: -3 %); a
-    // single sequence is split evenly anyway and loses (one of 4K: +10 %).
-    auto occupancy2 = [&]() {
-        const bool want = g_attn_occupancy == 2 || (g_attn_occupancy == 0 && B > 1);
+    // Default for batches (8 paged sequences of 1K-16K positions: -3 %) and
+    // for single sequences regrouped into one-tile-per-wavefront blocks
+    // (below); other single sequences are split evenly anyway (one of 4K with
+    // 3 row tiles: within the run-to-run spread).
+    auto occupancy2 = [&](bool single_pair) {
+        const bool want = g_attn_occupancy == 2 || (g_attn_occupancy == 0 && (B > 1 || single_pair));
         if (!want || pl.kind != kMfmaDma || q4 || pl.nt != 1) return;
         pl.occ = 2;
         pl.pg = std::min(pl.pg, std::max(1, std::min(2, 32768 / (128 * D))));
@@ -152,12 +154,23 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
             pl.nt = 1;
             pl.rows_per_block = 16;
             pl.n_rowblocks = 1;
-            occupancy2();
+            occupancy2(false);
             splits_for(B * Hkv, pl.split_len, pl.n_splits);
         } else {
             pl.pg = 1;
             int nrb = (RT + max_tiles - 1) / max_tiles;
             if (g_attn_rowblocks > 0) nrb = std::max(nrb, std::min(g_attn_rowblocks, RT));
+            // One sequence with more row tiles than wavefronts, context up to
+            // 64K: blocks of <= 4 tiles (one per wavefront) at two workgroups
+            // per CU, so each SIMD runs two wavefronts whose matrix and vector
+            // instructions interleave; each block reads the split's KV rows
+            // (from L2 after the first).  Measured on the 24/4-head, dim-256
+            // tree at 32K: 9 tiles in one block 52.9 us, in 3 blocks 47.9 us;
+            // at 8K 38.1 -> 25.8 us; at 128K it loses (135 -> 147 us), where
+            // the prologue is amortised and the single block reads KV once.
+            const bool single_pair = pl.kind == kMfmaDma && !q4 && B == 1 && RT > 4 && L <= 65536 &&
+                                     g_attn_rowblocks == 0 && g_attn_occupancy != 1;
+            if (single_pair) nrb = (RT + 3) / 4;
             // More row blocks (each reads the same KV tiles, from L2 after the
             // first) shorten the per-split work but multiply the splits, whose
             // fp32 partials the merge reads back.  Added while the partials
@@ -165,7 +178,7 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
             // (whose per-stage cost grows with the tiles per wave), 15% on the
             // register-staged one (measured on the workloads of the bench).
             const double max_part = pl.kind == kMfmaDma ? 0.35 : 0.15;
-            for (; g_attn_rowblocks == 0;) {
+            for (; g_attn_rowblocks == 0 && !single_pair;) {
                 const int tpb = (RT + nrb - 1) / nrb;
                 splits_for(B * Hkv * nrb, pl.split_len, pl.n_splits);
                 const double part = (double)pl.n_splits * R * (D + 2) * 4.0;
@@ -183,7 +196,7 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
                 const int pg_rows = tpb == 1 ? 4 : (tpb == 2 ? 2 : 1);
                 pl.pg = std::min(std::min(g_attn_posgroups, pg_rows), std::min(4, 65536 / (128 * D)));
             }
-            occupancy2();
+            occupancy2(single_pair);
             splits_for(B * Hkv * pl.n_rowblocks, pl.split_len, pl.n_splits);
         }
     } else {
