@@ -129,16 +129,19 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
     // Two workgroups per CU on the pipelined kernel (half-size rings, stages of
     // <= 32 KB, one row tile per wavefront): twice the units balance uneven
     // sequences better and each workgroup's start overlaps the other's work.
-    // Default for batches (8 paged sequences of 1K-16K positions: -3 %) and
-    // for single sequences regrouped into one-tile-per-wavefront blocks
-    // (below); other single sequences are split evenly anyway (one of 4K with
-    // 3 row tiles: within the run-to-run spread).
-    auto occupancy2 = [&](bool single_pair) {
-        const bool want = g_attn_occupancy == 2 || (g_attn_occupancy == 0 && (B > 1 || single_pair));
+    // Default for batches (8 paged sequences of 1K-16K positions: -3 %), for
+    // single sequences regrouped into one-tile-per-wavefront blocks (below),
+    // and for single sequences of <= 6K keys at the one-per-CU grid (the
+    // shallower ring lets the first chunk start once one stage has landed:
+    // 24/4 heads, dim 256, 8-row chain at 1K-4K keys -2 to -4 %; at 8K-32K
+    // within the spread, at 128K +3.5 %).
+    auto occupancy2 = [&](bool single_pair, bool single_short) {
+        const bool want = g_attn_occupancy == 2 ||
+                          (g_attn_occupancy == 0 && (B > 1 || single_pair || single_short));
         if (!want || pl.kind != kMfmaDma || q4 || pl.nt != 1) return;
         pl.occ = 2;
         pl.pg = std::min(pl.pg, std::max(1, std::min(2, 32768 / (128 * D))));
-        if (g_attn_target_wgs == 0) target = 512;
+        if (g_attn_target_wgs == 0 && !(single_short && !single_pair && g_attn_occupancy == 0)) target = 512;
     };
 
     if (mfma) {
@@ -154,7 +157,7 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
             pl.nt = 1;
             pl.rows_per_block = 16;
             pl.n_rowblocks = 1;
-            occupancy2(false);
+            occupancy2(false, false);
             splits_for(B * Hkv, pl.split_len, pl.n_splits);
         } else {
             pl.pg = 1;
@@ -196,7 +199,7 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
                 const int pg_rows = tpb == 1 ? 4 : (tpb == 2 ? 2 : 1);
                 pl.pg = std::min(std::min(g_attn_posgroups, pg_rows), std::min(4, 65536 / (128 * D)));
             }
-            occupancy2(single_pair);
+            occupancy2(single_pair, B == 1 && L <= 6144);
             splits_for(B * Hkv * pl.n_rowblocks, pl.split_len, pl.n_splits);
         }
     } else {
