@@ -136,12 +136,14 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
     // 24/4 heads, dim 256, 8-row chain at 1K-4K keys -2 to -4 %; at 8K-32K
     // within the spread, at 128K +3.5 %).
     auto occupancy2 = [&](bool single_pair, bool single_short) {
-        const bool want = g_attn_occupancy == 2 ||
-                          (g_attn_occupancy == 0 && (B > 1 || single_pair || single_short));
-        if (!want || pl.kind != kMfmaDma || q4 || pl.nt != 1) return;
+        const bool planned = g_attn_occupancy == 0 && (B > 1 || single_pair || single_short);
+        if (!(planned || g_attn_occupancy == 2) || pl.kind != kMfmaDma || q4 || pl.nt != 1) return;
         pl.occ = 2;
         pl.pg = std::min(pl.pg, std::max(1, std::min(2, 32768 / (128 * D))));
-        if (g_attn_target_wgs == 0 && !(single_short && !single_pair && g_attn_occupancy == 0)) target = 512;
+        // a batch and the regrouped blocks fill two workgroups per CU; a short
+        // single sequence keeps the one-per-CU grid
+        const bool keep_grid = planned && B == 1 && !single_pair;
+        if (g_attn_target_wgs == 0 && !keep_grid) target = 512;
     };
 
     if (mfma) {
