@@ -265,7 +265,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
-              "the verify path shards by sequence or KV head with no exchange, see the design notes",
+              "the verify path would shard by sequence or by KV head with no exchange between GPUs",
               file=sys.stderr)
         sys.exit(2)
 
