@@ -199,24 +199,29 @@ def test_attention_two_per_cu(sv, label, target):
 
 
 PLAN_EDGES = [
-    # (label, Hq, Hkv, N, tree, ctx): one sequence, bf16, head dim 256, at the
+    # (label, Hq, Hkv, D, N, tree, ctx, paged): one sequence, bf16, at the
     # planner's thresholds -- <= 6144 keys with <= 4 row tiles (half-size
     # rings at one workgroup per CU) and <= 65536 keys with > 4 row tiles
-    # (blocks of <= 4 tiles, two workgroups per CU); L = ctx + N keys
-    ("short ring, L = 6144", 24, 4, 8, "chain", 6136),
-    ("full ring, L = 6145", 24, 4, 8, "chain", 6137),
-    ("5 tiles in 2 blocks", 6, 1, 12, "ddtree", 3000),
-    ("tree 22 blocks, L = 65536", 6, 1, 22, "ddtree", 65514),
-    ("tree 22 one block, L = 65537", 6, 1, 22, "ddtree", 65515),
+    # (blocks of <= 4 tiles, two workgroups per CU); L = ctx + N keys; and
+    # the same plans over a paged cache (static schedule, page ids in LDS)
+    ("short ring, L = 6144", 24, 4, 256, 8, "chain", 6136, False),
+    ("full ring, L = 6145", 24, 4, 256, 8, "chain", 6137, False),
+    ("5 tiles in 2 blocks", 6, 1, 256, 12, "ddtree", 3000, False),
+    ("tree 22 blocks, L = 65536", 6, 1, 256, 22, "ddtree", 65514, False),
+    ("tree 22 one block, L = 65537", 6, 1, 256, 22, "ddtree", 65515, False),
+    ("paged one tile", 32, 8, 128, 4, "chain", 2000, True),
+    ("paged short ring", 24, 4, 256, 8, "chain", 3000, True),
+    ("paged tree 22 blocks", 12, 2, 128, 22, "ddtree", 5000, True),
+    ("paged full ring", 24, 4, 256, 8, "chain", 7000, True),
 ]
 
 
 @pytest.mark.parametrize("edge", PLAN_EDGES, ids=[e[0] for e in PLAN_EDGES])
 def test_attention_plan_edges(sv, edge):
     """Launch plans on both sides of each planner threshold against the oracle."""
-    label, Hq, Hkv, N, tree, ctx = edge
+    label, Hq, Hkv, D, N, tree, ctx, paged = edge
     say(f"[attn plan edge] {label}")
-    cfg = workloads.Config(label, 1, Hq, Hkv, 256, N, "bf16", "bf16", "f32", 50, ctx, tree=tree,
+    cfg = workloads.Config(label, 1, Hq, Hkv, D, N, "bf16", "bf16", "f32", 50, ctx, tree=tree, paged=paged,
                            q_std=0.5, kv_std=0.5, draft_rule="tree" if tree == "ddtree" else "geometric")
     case = workloads.make_case(cfg, seed=41, variant="peaked")
     out, lse = DeviceCase(case).attn()
