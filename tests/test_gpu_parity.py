@@ -215,6 +215,28 @@ PLAN_EDGES = [
     ("paged full ring", 24, 4, 256, 8, "chain", 7000, True),
 ]
 
+Q4_SINGLE = [
+    # (label, Hq, Hkv, N, tree, ctx, paged, window): one sequence, 4-bit cache
+    # of head dim 256 (pipelined kernel, static schedule)
+    ("q4 paged 6 tiles", 24, 4, 16, "chain", 1500, True, 0),
+    ("q4 paged tree 9 tiles", 24, 4, 22, "ddtree", 900, True, 0),
+    ("q4 paged one tile windowed", 8, 2, 4, "chain", 3000, True, 700),
+    ("q4 contiguous 6 tiles windowed", 24, 4, 16, "chain", 2500, False, 1000),
+]
+
+
+@pytest.mark.parametrize("case_", Q4_SINGLE, ids=[c[0] for c in Q4_SINGLE])
+def test_attention_q4_single_sequence(sv, case_):
+    """One sequence over a 4-bit cache, paged or windowed, against the oracle."""
+    label, Hq, Hkv, N, tree, ctx, paged, window = case_
+    say(f"[attn q4 single] {label}")
+    cfg = workloads.Config(label, 1, Hq, Hkv, 256, N, "bf16", "q4", "f32", 50, ctx, tree=tree, paged=paged,
+                           q_std=0.5, kv_std=0.5, draft_rule="tree" if tree == "ddtree" else "geometric")
+    case = workloads.make_case(cfg, seed=43)
+    out, lse = DeviceCase(case).attn(window=window)
+    torch.cuda.synchronize()
+    check_attention(case, out, lse, ref=oracle.verify_attention(case, window=window))
+
 
 @pytest.mark.parametrize("edge", PLAN_EDGES, ids=[e[0] for e in PLAN_EDGES])
 def test_attention_plan_edges(sv, edge):
