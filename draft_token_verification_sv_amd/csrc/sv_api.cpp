@@ -181,15 +181,17 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
             pl.pg = 1;
             int nrb = (RT + max_tiles - 1) / max_tiles;
             if (g_attn_rowblocks > 0) nrb = std::max(nrb, std::min(g_attn_rowblocks, RT));
-            // One sequence with more row tiles than wavefronts, context up to
-            // 64K: blocks of <= 4 tiles (one per wavefront) at two workgroups
+            // One sequence with more row tiles than wavefronts, 4K-64K keys:
+            // blocks of <= 4 tiles (one per wavefront) at two workgroups
             // per CU, so each SIMD runs two wavefronts whose matrix and vector
             // instructions interleave; each block reads the split's KV rows
             // (from L2 after the first).  Measured on the 24/4-head, dim-256
             // tree at 32K: 9 tiles in one block 52.9 us, in 3 blocks 47.9 us;
             // at 8K 38.1 -> 25.8 us; at 128K it loses (135 -> 147 us), where
-            // the prologue is amortised and the single block reads KV once.
-            const bool single_pair = pl.kind == kMfmaDma && !q4 && B == 1 && RT > 4 && L <= 65536 &&
+            // the prologue is amortised and the single block reads KV once,
+            // and below 4K too (2K: 18.6 -> 22.7 us), where the splits are few
+            // positions long and the extra row blocks only add prologues.
+            const bool single_pair = pl.kind == kMfmaDma && !q4 && B == 1 && RT > 4 && L > 4096 && L <= 65536 &&
                                      g_attn_rowblocks == 0 && g_attn_occupancy != 1;
             if (single_pair) nrb = (RT + 3) / 4;
             // More row blocks (each reads the same KV tiles, from L2 after the

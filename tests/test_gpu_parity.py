@@ -206,7 +206,9 @@ PLAN_EDGES = [
     # the same plans over a paged cache (static schedule, page ids in LDS)
     ("short ring, L = 6144", 24, 4, 256, 8, "chain", 6136, False),
     ("full ring, L = 6145", 24, 4, 256, 8, "chain", 6137, False),
-    ("5 tiles in 2 blocks", 6, 1, 256, 12, "ddtree", 3000, False),
+    ("5 tiles in 2 blocks", 6, 1, 256, 12, "ddtree", 5000, False),
+    ("tree 22 one block, L = 4096", 6, 1, 256, 22, "ddtree", 4074, False),
+    ("tree 22 blocks, L = 4097", 6, 1, 256, 22, "ddtree", 4075, False),
     ("tree 22 blocks, L = 65536", 6, 1, 256, 22, "ddtree", 65514, False),
     ("tree 22 one block, L = 65537", 6, 1, 256, 22, "ddtree", 65515, False),
     ("paged one tile", 32, 8, 128, 4, "chain", 2000, True),
