@@ -42,7 +42,7 @@ The pages give neither the recurrence nor its sizes.  The readings used here:
 Everything is float64 from the exact widening of the stored inputs.
 
 Parity status: pinned in ``tests/test_oracle_recurrent.py`` (hand-worked
-examples in ``tests/golden/delta_net_tiny.json``, torch's depthwise conv1d
+examples in ``tests/golden/recurrent_tiny.json``, torch's depthwise conv1d
 in float64, the textbook matrix form of the delta rule, brute force over each
 node's root path, closed forms of the decay-only and write-only cases, and the
 replay of the accepted tokens one at a time).
