@@ -23,13 +23,14 @@ __all__ = [
     "SV_F32", "SV_BF16", "SV_Q4", "SVError", "KVCache", "lib", "library_path",
     "verify_attn", "verify_attn_workspace_size", "greedy_accept", "greedy_accept_workspace_size",
     "kv_compact", "greedy_accept_compact", "kv_append", "sample_accept", "set_option", "SV_OPT_ATTN_TARGET_WGS", "SV_OPT_ARGMAX_CHUNK", "SV_OPT_ATTN_ROWBLOCKS",
-    "SV_OPT_ATTN_POSGROUPS", "SV_OPT_ATTN_OCCUPANCY", "SV_F16",
+    "SV_OPT_ATTN_POSGROUPS", "SV_OPT_ATTN_OCCUPANCY", "SV_OPT_ATTN_Q4_KERNEL", "SV_F16",
     "ssm_conv_tree", "gated_delta_net_tree", "recurrent_commit", "tree_schedule",
 ]
 
 SV_F32, SV_BF16, SV_Q4, SV_F16 = 0, 1, 2, 3
 SV_OPT_ATTN_TARGET_WGS, SV_OPT_ARGMAX_CHUNK, SV_OPT_ATTN_ROWBLOCKS, SV_OPT_ATTN_POSGROUPS = 1, 2, 3, 4
 SV_OPT_ATTN_OCCUPANCY = 5
+SV_OPT_ATTN_Q4_KERNEL = 6
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsv.so")
 if not os.path.exists(library_path):

@@ -14,8 +14,8 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libsv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["sv_api.cpp", "attn_dma.hip", "attn_mfma.hip", "attn_valu.hip", "accept.hip", "compact.hip",
-           "append.hip", "recurrent.hip", "topk.hip"]
+SOURCES = ["sv_api.cpp", "attn_dma.hip", "attn_mfma.hip", "attn_valu.hip", "attn_q4.hip", "accept.hip",
+           "compact.hip", "append.hip", "recurrent.hip", "topk.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -25,11 +25,18 @@ FLAGS = [
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function",
 ]
+# extra flags per source: the cooperative 4-bit kernel keeps no NaN semantics
+# in its maxima (inputs are finite; masked scores are -inf, which stays exact)
+# (and keeps its matrix accumulators in the accumulation registers, which
+# leaves the architectural ones to the queries and the prefetched fragments)
+EXTRA = {"attn_q4.hip": ["-fno-honor-nans"]}
+NO_VGPR_FORM = {"attn_q4.hip"}
 
 
 def _compile(src: str, obj_dir: str) -> str:
     obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS]
+    flags = [f for f in FLAGS if not (src in NO_VGPR_FORM and f in ("-mllvm", "-amdgpu-mfma-vgpr-form=1"))]
+    cmd = [HIPCC, *flags, *EXTRA.get(src, [])]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]

@@ -1,0 +1,673 @@
+// Split-KV verify attention over a 4-bit KV cache of head dim 256 on gfx950:
+// a cooperative four-wave schedule on fp16 matrix cores.
+//
+// The 4-bit cache [single-RTX-3090 DFlash note, "128K context in 24 GB": the
+// KV cache kept in 4 bits so that 128K tokens of context fit] is read by the
+// same direct-to-LDS stages as the bf16 pipeline: a stage is 128 positions of
+// raw codes and fp16 scales (36 KB, 9 one-KB DMA instructions per wave).
+//
+// Work split.  One workgroup (4 waves) handles one (sequence, KV head, row
+// block, key split); a row block is 2 * NTS tiles of 16 packed rows (r = node
+// * G + g, the verify rows of every query head of the GQA group).  Per
+// 32-position chunk:
+//   S^T = K Q^T  wave w computes position tile w & 1 (16 positions) for row
+//                tiles (w >> 1) * NTS .. + NTS - 1: every S tile is computed
+//                once and the four waves carry equal matrix work;
+//   O^T += V^T P^T  wave w owns head-dim slice [64 w, 64 w + 64) of every row
+//                tile: again equal work, and every V element is read by one
+//                wave.
+// The probabilities cross waves through LDS (P is written by the wave that
+// computed S and read by all four).  The online-softmax reference maximum of a
+// row must be the same in every wave (each holds a slice of the row's O), so
+// the waves publish their per-tile row maxima and all apply the same lazy
+// rule: the reference moves only when a chunk's maximum exceeds it by more
+// than 2^8 (numerator and denominator share it, so this is exact).
+//
+// Dequantisation.  value = d * (code - 8) with d the block's fp16 scale.  The
+// 256 threads turn each staged chunk into fp16 rows in LDS with packed fp16
+// arithmetic: the codes are placed in the mantissa of 1024.0 (code n at bits
+// 0-3 gives 1024 + n, at bits 4-7 gives 1024 + 16 n), one packed add or fma
+// makes n - 8 exactly, one packed multiply by d rounds d (n - 8) to nearest
+// fp16.  The eight values of a 32-bit code word come out in the order
+// (0, 4, 2, 6, 1, 5, 3, 7); the query fragments are permuted the same way
+// (a permutation of the contraction index), and the output head-dim index is
+// mapped back when the partials are stored.  The queries are converted to
+// fp16 after scaling each row by a power of two that puts its largest
+// magnitude in [2^14, 2^15) (exact for bf16 values in the normal range; the
+// scale is folded back into the softmax exponent).
+//
+// Pipeline per chunk g (two barriers): after the first, every wave applies
+// the published row maxima of S(g); then the matrix instructions of S(g + 1)
+// run while the vector units take the exponentials of P(g) and dequantise
+// V(g + 1); after the second, the matrix instructions of O += V^T P(g)^T run
+// while the vector units take the row maxima of S(g + 1) and dequantise
+// K(g + 2).  Each matrix instruction is followed by its share of the vector
+// work, in that order (one wave per SIMD: the overlap comes from the
+// instruction stream).  K and V staging and P are double-buffered by chunk
+// parity; cross-lane row reductions use the permlane swaps.
+//
+// Tree mask [DFN "From autoregressive to DDTree"; for chains the causal mask
+// aligned to the end of the keys, xdnf.cn notes section 5.3]: 64-bit ancestor
+// sets in LDS, applied on chunks that reach the draft rows or the split end.
+// Output: unnormalised partials (O, m, l) per row for the split merge.
+#include "attn_sched.h"
+
+namespace sv {
+namespace {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int D = 256;
+constexpr int T = 128;                      // positions per DMA stage
+constexpr int CROW = D / 2;                 // code bytes per row
+constexpr int SROW = D / 16;                // scale bytes per row
+constexpr int STAGE = 2 * T * (CROW + SROW);
+constexpr int NKB = STAGE / 1024;           // 1 KB DMA instructions per stage
+constexpr int LPW = NKB / 4;                // per wave
+constexpr int KCI = T * CROW / 1024, KSI = T * SROW / 1024;
+constexpr int CPS = T / 32;                 // 32-position chunks per stage
+constexpr int FROW = D * 2;                 // fp16 staging row bytes
+constexpr int FST = 32 * FROW;              // one staged chunk of K or V
+constexpr int PROW = 80;                    // P row bytes (32 fp16 + 16 padding)
+constexpr int kMaxPages = 512;
+static_assert(NKB % 4 == 0 && KCI * 1024 == T * CROW && KSI * 1024 == T * SROW, "stage layout");
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void dma16(uint32_t lds_base, const void *gptr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds_base), "v"(gptr)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma16s(uint32_t lds_base, const void *sbase, uint32_t voff) {
+    const uint64_t a = (uint64_t)(uintptr_t)sbase;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint64_t u = ((uint64_t)hi << 32) | (uint64_t)lo;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"(u)
+                 : "memory", "m0");
+}
+
+// (w & m) | c in one instruction
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t m, uint32_t c) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "v"(m), "v"(c));
+    return r;
+}
+
+// Eight 4-bit codes (one 32-bit word, value 2t in the low nibble of byte t)
+// times the block scale s (both halves), as fp16 in the order
+// (0, 4, 2, 6, 1, 5, 3, 7).
+__device__ __forceinline__ u32x4 dequant_word(uint32_t w, h2 s, uint32_t m_lo, uint32_t m_hi, uint32_t magic) {
+    const h2 off = {(_Float16)-1032.f, (_Float16)-1032.f};   // 1024 + n -> n - 8
+    const h2 sx = {(_Float16)0.0625f, (_Float16)0.0625f};     // (1024 + 16 n) / 16 - 72 -> n - 8
+    const h2 o2 = {(_Float16)-72.f, (_Float16)-72.f};
+    const uint32_t w8 = w >> 8;
+    const h2 a = __builtin_bit_cast(h2, and_or(w, m_lo, magic));     // values 0, 4
+    const h2 b = __builtin_bit_cast(h2, and_or(w, m_hi, magic));     // values 1, 5
+    const h2 c = __builtin_bit_cast(h2, and_or(w8, m_lo, magic));    // values 2, 6
+    const h2 d = __builtin_bit_cast(h2, and_or(w8, m_hi, magic));    // values 3, 7
+    u32x4 r;
+    r[0] = __builtin_bit_cast(uint32_t, (a + off) * s);
+    r[1] = __builtin_bit_cast(uint32_t, (c + off) * s);
+    r[2] = __builtin_bit_cast(uint32_t, (b * sx + o2) * s);
+    r[3] = __builtin_bit_cast(uint32_t, (d * sx + o2) * s);
+    return r;
+}
+
+// Matrix instructions with their operands placed explicitly: the queries (B
+// of S^T) and the O accumulators stay in the accumulation registers for the
+// whole split, which leaves the architectural registers to the prefetched
+// fragments and the vector work.  Every operand here is produced by an LDS
+// read, by another matrix instruction accumulating in place, or long before
+// (the queries, the sequence's last instructions before a barrier), so no
+// extra wait states are needed between them and their producers; the
+// destination never overlaps a source (early clobber), and vector reads of
+// results wait behind mfma_drain().
+__device__ __forceinline__ f32x4 mfma_s0(h8 a, h8 b_acc) {
+    f32x4 d;
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b_acc));
+    return d;
+}
+__device__ __forceinline__ void mfma_s(f32x4 &c, h8 a, h8 b_acc) {
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b_acc));
+}
+__device__ __forceinline__ void mfma_o(f32x4 &acc, h8 a, h8 b) {
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// wait states before vector instructions read accumulators that the last
+// matrix instructions wrote
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
+template <int NTS, bool PAGED>
+__global__ __launch_bounds__(256, 1) void attn_q4c_kernel(AttnParams p) {
+    constexpr int RB = 2 * NTS;                 // row tiles per block
+    constexpr int ROWS = 16 * RB;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t kst[2 * FST];
+    __shared__ __attribute__((aligned(1024))) uint8_t vst[2 * FST];
+    __shared__ __attribute__((aligned(16))) uint8_t pbuf[2 * ROWS * PROW];
+    __shared__ __attribute__((aligned(16))) float mxb[2 * ROWS * 2];
+    __shared__ float lsx[ROWS];
+    __shared__ int par_s[64];
+    __shared__ uint64_t anc_s[64];
+    __shared__ int pages_s[PAGED ? kMaxPages : 1];
+    __shared__ SchedLds sched_s;
+
+    // ---- unit: (b, kv head, row block, split); the row blocks of one unit get
+    // ids 8 apart (same XCD, shared L2) ------------------------------------------
+    const int id = blockIdx.x;
+    const int xcd = id & 7, k8 = id >> 3;
+    const int rb = k8 % p.n_rowblocks;
+    AttnUnit wu;
+    if (!attn_unit(p, (k8 / p.n_rowblocks) * 8 + xcd, rb == 0, sched_s, wu)) return;
+    const int b = __builtin_amdgcn_readfirstlane(wu.b), kvh = __builtin_amdgcn_readfirstlane(wu.kvh);
+    const int N = p.N, G = p.G, R = p.R;
+    const int ctx = __builtin_amdgcn_readfirstlane(wu.ctx);
+    const int p0 = __builtin_amdgcn_readfirstlane(wu.p0), p1 = __builtin_amdgcn_readfirstlane(wu.p1);
+    const int n_st = (p1 - p0 + T - 1) / T;
+    const int NCH = (p1 - p0 + 31) / 32;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pt = wave & 1, hh = wave >> 1;
+    const int l16 = lane & 15, qd = lane >> 4;
+
+    // ---- tree (splits that reach the draft rows) and page ids --------------
+    const bool has_draft = p1 > ctx;
+    if (has_draft && tid < N) par_s[tid] = p.parent[(int64_t)b * N + tid];
+    int first_page = 0;
+    if constexpr (PAGED) {
+        first_page = p0 / p.kv.page_size;
+        const int last_page = (p1 - 1) / p.kv.page_size;
+        for (int e = tid; e <= last_page - first_page; e += 256) {
+            const int pgid = p.kv.page_table[(int64_t)b * p.kv.max_pages + first_page + e];
+            pages_s[e] = (pgid < 0 || pgid >= p.kv.capacity) ? -1 : pgid;
+        }
+    }
+    __syncthreads();
+    if (has_draft && tid < N) anc_s[tid] = ancestor_bits(par_s, tid);   // visible after the next barrier
+
+    // ---- DMA issue ---------------------------------------------------------------
+    // Instruction j of this wave covers 1 KB of the stage [K codes][V codes]
+    // [K scales][V scales]: lane offset within the array's part of the stage,
+    // the array (wave-uniform) and its log2 row bytes.
+    const uint8_t *arr_base[4] = {(const uint8_t *)p.kv.k, (const uint8_t *)p.kv.v, (const uint8_t *)p.kv.ks,
+                                  (const uint8_t *)p.kv.vs};
+    uint32_t dma_off[LPW];
+    const uint8_t *dma_gb[LPW];
+    int dma_rsh[LPW];
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+        const int kbi = wave * LPW + j;
+        const int arr = kbi < KCI ? 0 : (kbi < 2 * KCI ? 1 : (kbi < 2 * KCI + KSI ? 2 : 3));
+        const int start = arr == 0 ? 0 : (arr == 1 ? KCI : (arr == 2 ? 2 * KCI : 2 * KCI + KSI));
+        dma_off[j] = (uint32_t)((kbi - start) * 1024 + lane * 16);
+        dma_gb[j] = arr_base[arr];
+        dma_rsh[j] = arr < 2 ? 7 : 4;                  // 128 code bytes / 16 scale bytes per row
+    }
+    const int64_t head_row0 = ((int64_t)b * p.Hkv + kvh) * p.kv.capacity;
+    const uint32_t ring_u32 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)ring;
+
+    // Stage st = positions p0 + 128 st .. + 127; rows past the split's end
+    // repeat its last row (their scores are masked).  Paged rows whose page is
+    // outside the pool fetch row 0 of the array (no out-of-range access) and
+    // are replaced by zero rows when dequantised.
+    auto issue = [&](int st) {
+        const int tb = p0 + st * T;
+        const uint32_t slot = ring_u32 + (uint32_t)((st & 1) * STAGE + wave * LPW * 1024);
+        if constexpr (!PAGED) {
+            if (tb + T <= p1) {
+#pragma unroll
+                for (int j = 0; j < LPW; ++j)
+                    dma16s(__builtin_amdgcn_readfirstlane(slot + (uint32_t)(j * 1024)),
+                           dma_gb[j] + ((head_row0 + tb) << dma_rsh[j]), dma_off[j]);
+            } else {
+                const int lim = p1 - 1 - tb;
+#pragma unroll
+                for (int j = 0; j < LPW; ++j) {
+                    const int rsh = dma_rsh[j];
+                    const int row = (int)(dma_off[j] >> rsh);
+                    const uint32_t col = dma_off[j] & ((1u << rsh) - 1u);
+                    dma16s(__builtin_amdgcn_readfirstlane(slot + (uint32_t)(j * 1024)),
+                           dma_gb[j] + ((head_row0 + tb) << rsh), ((uint32_t)min(row, lim) << rsh) | col);
+                }
+            }
+        } else {
+            const int ps = p.kv.page_size;
+#pragma unroll
+            for (int j = 0; j < LPW; ++j) {
+                const int rsh = dma_rsh[j];
+                const int row = (int)(dma_off[j] >> rsh);
+                const uint32_t col = dma_off[j] & ((1u << rsh) - 1u);
+                const int pos = min(tb + row, p1 - 1);
+                const int pq = pos / ps, pr = pos - pq * ps;
+                const int pg = pages_s[pq - first_page];
+                const int64_t ri = pg < 0 ? 0 : ((int64_t)pg * p.Hkv + kvh) * ps + pr;
+                dma16(__builtin_amdgcn_readfirstlane(slot + (uint32_t)(j * 1024)), dma_gb[j] + (ri << rsh) + col);
+            }
+        }
+    };
+
+    // ---- prologue: stage 0, the queries, stage 1 --------------------------------
+    issue(0);
+
+    const int row0 = rb * p.rows_per_block;
+    const int rows_here = min(p.rows_per_block, R - row0);
+    // S rows of this lane: tile hh * NTS + i, row l16
+    h8 qf[NTS][8];
+    float sl2[NTS];
+    int node_of[NTS];
+#pragma unroll
+    for (int i = 0; i < NTS; ++i) {
+        const int rl = 16 * (hh * NTS + i) + l16;
+        const bool ok = rl < rows_here;
+        const int r = row0 + rl;
+        node_of[i] = ok ? r / G : -1;
+        bf16x8 raw[8];
+        if (ok) {
+            const int n = r / G, g = r % G;
+            const __bf16 *qp = (const __bf16 *)p.q + (((int64_t)b * N + n) * p.Hq + (int64_t)kvh * G + g) * D + qd * 8;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) raw[k] = *(const bf16x8 *)(qp + 32 * k);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const bf16x8 z = {};
+                raw[k] = z;
+            }
+        }
+        // row maximum magnitude (the row's 256 values sit in the 4 lanes l16 + 16 qd)
+        float amax = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf((float)raw[k][j]));
+        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        // 2^kq * amax in [2^14, 2^15): frexp gives amax = m 2^e, m in [0.5, 1)
+        int kq = 0;
+        if (amax > 0.f) {
+            kq = 15 - __builtin_amdgcn_frexp_expf(amax);
+            kq = kq > 100 ? 100 : (kq < -110 ? -110 : kq);
+        }
+        sl2[i] = ldexpf(p.scale_log2, -kq);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            // slot j holds value pi(j), pi = (0, 4, 2, 6, 1, 5, 3, 7)
+            const int pi[8] = {0, 4, 2, 6, 1, 5, 3, 7};
+            h8 v;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = (_Float16)ldexpf((float)raw[k][pi[j]], kq);
+            qf[i][k] = v;
+            asm volatile("" : "+a"(qf[i][k]));           // held in the accumulation registers
+        }
+    }
+    if (n_st > 1) issue(1);
+
+    f32x4 o[RB][4];
+    float m_ref[RB], l_s[NTS];
+#pragma unroll
+    for (int t = 0; t < RB; ++t) {
+        m_ref[t] = -INFINITY;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < NTS; ++i) l_s[i] = 0.f;
+
+    // ---- LDS layout of a staged fp16 chunk of K or V: the 16-byte unit of
+    // logical head-dim chunk c (8 values) and position p sits at
+    // c * 512 + (p ^ 4 (c & 1)) * 16.  With it the dequantisation writes, the K
+    // fragment reads and the transposed V reads are free of bank conflicts.
+    // K fragment, position tile pt, k-step k: chunk 4 k + qd, position 16 pt + l16
+    const int k_lane = qd * 512 + ((16 * pt + l16) ^ (4 * (qd & 1))) * 16;          // + 2048 k
+    // V^T fragment of 16-wide head-dim tile dg, half h: lane reads the 4-value
+    // run r = l16 & 3 of position 8 qd + l16 / 4 + 4 h in chunk 2 dg + r / 2
+    const int vsel = (l16 & 3) >> 1;
+    const int va = 8 * qd + (l16 >> 2);
+    const int v_lane0 = vsel * 512 + (va + 4 * vsel) * 16 + (l16 & 1) * 8;         // + 1024 dg
+    const int v_lane1 = vsel * 512 + (va + 4 - 4 * vsel) * 16 + (l16 & 1) * 8;
+    // P rows of this lane (PV operand): 8 positions 8 qd .. 8 qd + 7 of row 16 t + l16
+    const int p_lane = l16 * PROW + 16 * qd;
+
+    // Dequantisation: thread (row, 32-value block) of a chunk, laid out so that
+    // the 8 threads of each LDS access group take 8 different rows (mod 8) and
+    // 8 different blocks: their code reads and their fp16 writes both spread
+    // over all banks.
+    const int di = tid & 7, dj = tid >> 3;
+    const int drow = 8 * (dj & 3) + di, dblk = (di + (dj >> 2)) & 7;
+    const int dsrc = drow * CROW + dblk * 16, dssrc = drow * SROW + dblk * 2;
+    const int ddst0 = (4 * dblk) * 512 + drow * 16;             // words m = 0, 2: + 1024 (m / 2)
+    const int ddst1 = (4 * dblk + 1) * 512 + (drow ^ 4) * 16;   // words m = 1, 3
+    const uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u, magic = 0x64006400u;
+    struct Codes {
+        u32x4 w;
+        h2 s;
+    };
+    // codes and scale of chunk g of K (which = 0) or V (1) from the ring
+    auto dq_load = [&](int which, int g) {
+        const uint8_t *stg = ring + ((g / CPS) & 1) * STAGE + (g % CPS) * 32 * CROW;
+        Codes c;
+        c.w = *(const u32x4 *)(stg + which * T * CROW + dsrc);
+        const uint32_t sb = *(const uint16_t *)(ring + ((g / CPS) & 1) * STAGE + 2 * T * CROW + which * T * SROW +
+                                                (g % CPS) * 32 * SROW + dssrc);
+        c.s = __builtin_bit_cast(h2, sb * 0x10001u);
+        if constexpr (PAGED) {
+            // a page outside the pool reads as a zero row
+            const int pos = min(p0 + 32 * g + drow, p1 - 1);
+            if (pages_s[pos / p.kv.page_size - first_page] < 0) c.s = h2{(_Float16)0.f, (_Float16)0.f};
+        }
+        return c;
+    };
+    auto dq_word = [&](int which, int g, const Codes &c, int m) {
+        uint8_t *dst = (which ? vst : kst) + (g & 1) * FST + ((m & 1) ? ddst1 : ddst0) + (m >> 1) * 1024;
+        *(u32x4 *)dst = dequant_word(c.w[m], c.s, m_lo, m_hi, magic);
+    };
+    auto kread = [&](int g, int k) { return *(const h8 *)(kst + (g & 1) * FST + k_lane + 2048 * k); };
+
+    // row maxima of one S tile (log2 units) into the exchange buffer; the 4
+    // lanes of a row all hold the row's value after the swaps and all store it
+    auto xmax = [](float x, bool by32) {
+        const auto r = by32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false)
+                            : __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    };
+    // exchange buffer layout [row l16][row tile][position tile]: a lane's 2 RB
+    // values are contiguous
+    auto row_max = [&](const f32x4 &sc, int i, float *mxw) {
+        float c = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        c = xmax(xmax(c, false), true);
+        mxw[(l16 * RB + hh * NTS + i) * 2 + pt] = c * sl2[i];
+    };
+    // tree / split-end mask of chunk g on an S tile set (lane: positions pos0 .. pos0 + 3)
+    auto apply_mask = [&](int g, f32x4 (&sc)[NTS]) {
+        const int cb = p0 + 32 * g;
+        if (cb + 32 > ctx || cb + 32 > p1) {
+            const int pos0 = cb + 16 * pt + 4 * qd;
+#pragma unroll
+            for (int i = 0; i < NTS; ++i) {
+                const uint64_t anc = node_of[i] >= 0 ? anc_s[node_of[i]] : 0ull;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int pos = pos0 + j;
+                    bool vis = pos < p1;
+                    if (pos >= ctx) vis = vis && (((anc >> ((pos - ctx) & 63)) & 1ull) != 0ull);
+                    sc[i][j] = vis ? sc[i][j] : -INFINITY;
+                }
+            }
+        }
+    };
+
+    // ---- prologue: stage 0 landed (stage 1 may be in flight) -----------------
+    if (n_st > 1) wait_vm<LPW>();
+    else wait_vm<0>();
+    __syncthreads();
+    {
+        const Codes k0 = dq_load(0, 0), v0 = dq_load(1, 0), k1 = dq_load(0, min(1, NCH - 1));
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            dq_word(0, 0, k0, m);
+            dq_word(1, 0, v0, m);
+            dq_word(0, 1, k1, m);
+        }
+    }
+    __syncthreads();
+
+    f32x4 sacc[NTS];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const h8 kf = kread(0, k);
+#pragma unroll
+        for (int i = 0; i < NTS; ++i) {
+            if (k == 0) sacc[i] = mfma_s0(kf, qf[i][k]);
+            else mfma_s(sacc[i], kf, qf[i][k]);
+        }
+    }
+    mfma_drain();
+    apply_mask(0, sacc);
+#pragma unroll
+    for (int i = 0; i < NTS; ++i) row_max(sacc[i], i, mxb);
+
+    constexpr int MC = 8 * NTS;             // matrix instructions per phase
+    constexpr int TCC = NTS + 4;            // vector tasks of phase (c): P tiles, V words
+    constexpr int TCE = NTS + 4;            // of phase (e): row maxima, K words
+
+    h8 kf[8];
+
+    // Chunks past the last one are still dequantised and multiplied (into
+    // buffers nobody reads afterwards; the ring reads stay in bounds), so that
+    // the matrix and vector instruction streams below have no branches.  Each
+    // matrix instruction is followed by its share of vector work, and
+    // scheduling barriers keep that order.  A chunk whose row maximum moves a
+    // reference leaves the inner loop; the outer loop rescales the
+    // accumulators and re-enters at the same chunk, so the matrix
+    // accumulators are only ever written by matrix instructions inside the
+    // inner loop.
+    int g = 0;
+    bool resumed = false;
+#pragma unroll 1
+    while (true) {
+#pragma unroll 1
+        for (; g < NCH; ++g) {
+            if (!resumed) {
+                // ---- barrier 1: maxima of S(g) published; the ring slot of stage
+                // s + 1 is free once every wave has dequantised chunk 4 s + 3 ------
+                __syncthreads();
+                if (((g + 1) & (CPS - 1)) == 0) {
+                    const int st = (g + 1) / CPS + 1;
+                    if (st < n_st) issue(st);
+                }
+            }
+            resumed = false;
+            // K fragments of S(g + 1): dequantised by every thread before this
+            // barrier; their latency hides behind (b)
+            {
+                const int gs = g + 1 < NCH ? g + 1 : g;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) kf[k] = kread(gs, k);
+            }
+
+            // ---- (b) does a reference maximum move? (the same rule in every wave)
+            const float *mxr = mxb + (g & 1) * ROWS * 2 + l16 * RB * 2;
+            bool grow = false;
+#pragma unroll
+            for (int t = 0; t < RB; ++t) {
+                const float cm = fmaxf(mxr[2 * t], mxr[2 * t + 1]);
+                grow = grow || (cm > m_ref[t] + 8.f);
+            }
+            if (__builtin_expect(__any(grow), 0)) break;
+
+            // ---- (c) S(g + 1) on the matrix cores; P(g) and V(g + 1) on the
+            // vector units --------------------------------------------------------
+            f32x4 sacc_n[NTS];
+            {
+                uint8_t *pw = pbuf + (g & 1) * ROWS * PROW;
+                const Codes cv = dq_load(1, g + 1);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+#pragma unroll
+                    for (int i = 0; i < NTS; ++i) {
+                        const int idx = NTS * k + i;
+                        if (k == 0) sacc_n[i] = mfma_s0(kf[k], qf[i][k]);
+                        else mfma_s(sacc_n[i], kf[k], qf[i][k]);
+#pragma unroll
+                        for (int t = 0; t < TCC; ++t) {
+                            if (idx != (t * MC) / TCC) continue;
+                            if (t < NTS) {
+                                // P of tile t: exponentials, row sums, fp16 to LDS
+                                const float mr = hh ? m_ref[NTS + t] : m_ref[t];
+                                const float mu = mr == -INFINITY ? 0.f : mr;
+                                float pr[4];
+#pragma unroll
+                                for (int j = 0; j < 4; ++j)
+                                    pr[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][j], sl2[t], -mu));
+                                l_s[t] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+                                typedef float f32x2_t __attribute__((ext_vector_type(2)));
+                                u32x2 pk;
+                                pk[0] = __builtin_bit_cast(uint32_t,
+                                                           __builtin_convertvector((f32x2_t){pr[0], pr[1]}, h2));
+                                pk[1] = __builtin_bit_cast(uint32_t,
+                                                           __builtin_convertvector((f32x2_t){pr[2], pr[3]}, h2));
+                                *(u32x2 *)(pw + (16 * (hh * NTS + t) + l16) * PROW + (16 * pt + 4 * qd) * 2) = pk;
+                            } else {
+                                dq_word(1, g + 1, cv, t - NTS);
+                            }
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+            }
+
+            // stage (g + 2) / 4 is needed from here on: this wave's part landed
+            if (((g + 2) & (CPS - 1)) == 0 && g + 2 < NCH) wait_vm<0>();
+
+            // ---- barrier 2: P(g) published; V(g + 1) staged; K(g + 2)'s stage landed
+            __syncthreads();
+
+            // ---- (e) O^T += V^T P(g)^T on the matrix cores; the row maxima of
+            // S(g + 1) and K(g + 2) on the vector units; then the K fragments of
+            // S(g + 2) ------------------------------------------------------------
+            mfma_drain();                                  // S(g + 1) complete before the vector reads
+            apply_mask(g + 1, sacc_n);
+            {
+                float *mxw = mxb + ((g + 1) & 1) * ROWS * 2;
+                const int gk = g + 2 < NCH ? g + 2 : g;
+                const Codes ck = dq_load(0, gk);
+                const uint8_t *vp = vst + (g & 1) * FST;
+                const uint8_t *prd = pbuf + (g & 1) * ROWS * PROW + p_lane;
+                h8 vf[4];
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                    const int dg = 4 * wave + dt;            // 16-wide head-dim tile
+                    const s16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4 *)(__attribute__((address_space(3))) uint8_t *)(
+                            vp + v_lane0 + 1024 * dg));
+                    const s16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4 *)(__attribute__((address_space(3))) uint8_t *)(
+                            vp + v_lane1 + 1024 * dg));
+                    const short __attribute__((ext_vector_type(8))) w8 = {h0[0], h0[1], h0[2], h0[3],
+                                                                          h1[0], h1[1], h1[2], h1[3]};
+                    vf[dt] = __builtin_bit_cast(h8, w8);
+                }
+                h8 pf[RB];
+#pragma unroll
+                for (int t = 0; t < RB; ++t) pf[t] = *(const h8 *)(prd + 16 * t * PROW);
+#pragma unroll
+                for (int t = 0; t < RB; ++t) {
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt) {
+                        const int idx = 4 * t + dt;
+                        mfma_o(o[t][dt], vf[dt], pf[t]);
+#pragma unroll
+                        for (int u = 0; u < TCE; ++u) {
+                            if (idx != (u * MC) / TCE) continue;
+                            if (u < NTS) row_max(sacc_n[u], u, mxw);
+                            else dq_word(0, gk, ck, u - NTS);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < NTS; ++i) sacc[i] = sacc_n[i];
+        }
+        if (g >= NCH) break;
+        // ---- a reference maximum moves at chunk g: rescale, re-enter --------
+        {
+            mfma_drain();
+            const float *mxr = mxb + (g & 1) * ROWS * 2 + l16 * RB * 2;
+            float alpha[RB];
+#pragma unroll
+            for (int t = 0; t < RB; ++t) {
+                const float cm = fmaxf(mxr[2 * t], mxr[2 * t + 1]);
+                const bool need = cm > m_ref[t] + 8.f;
+                alpha[t] = need ? __builtin_amdgcn_exp2f(m_ref[t] - cm) : 1.f;
+                m_ref[t] = need ? cm : m_ref[t];
+            }
+#pragma unroll
+            for (int t = 0; t < RB; ++t)
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) o[t][dt] *= alpha[t];
+#pragma unroll
+            for (int i = 0; i < NTS; ++i) l_s[i] *= hh ? alpha[NTS + i] : alpha[i];
+            resumed = true;
+        }
+    }
+
+    mfma_drain();
+    // ---- row sums: lanes of a row, then the two position-tile waves -----------
+#pragma unroll
+    for (int i = 0; i < NTS; ++i) {
+        l_s[i] += __shfl_xor(l_s[i], 16, 64);
+        l_s[i] += __shfl_xor(l_s[i], 32, 64);
+        if (pt == 1 && qd == 0) lsx[16 * (hh * NTS + i) + l16] = l_s[i];
+    }
+    __syncthreads();
+
+    // ---- partials of this split --------------------------------------------------
+    const int64_t part = wu.part;
+#pragma unroll
+    for (int t = 0; t < RB; ++t) {
+        const int rl = 16 * t + l16;
+        if (rl >= rows_here) continue;
+        float *op = p.part_o + (part * R + row0 + rl) * D;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            // slot s = 64 wave + 16 dt + 4 qd + j holds head-dim 8 (s / 8) + pi(s % 8)
+            const int s0 = 64 * wave + 16 * dt + 4 * qd;
+            const int base = s0 & ~7;
+            const int odd = (s0 >> 2) & 1;               // slots 4..7 of the group of 8
+            // pi(0..3) = 0, 4, 2, 6;  pi(4..7) = 1, 5, 3, 7
+            op[base + (odd ? 1 : 0)] = o[t][dt][0];
+            op[base + (odd ? 5 : 4)] = o[t][dt][1];
+            op[base + (odd ? 3 : 2)] = o[t][dt][2];
+            op[base + (odd ? 7 : 6)] = o[t][dt][3];
+        }
+    }
+    if (pt == 0 && qd == 0) {
+#pragma unroll
+        for (int i = 0; i < NTS; ++i) {
+            const int rl = 16 * (hh * NTS + i) + l16;
+            if (rl >= rows_here) continue;
+            const float mr = hh ? m_ref[NTS + i] : m_ref[i];
+            p.part_ml[(part * R + row0 + rl) * 2 + 0] = mr;
+            p.part_ml[(part * R + row0 + rl) * 2 + 1] = l_s[i] + lsx[rl];
+        }
+    }
+}
+
+template <int NTS, bool PAGED>
+hipError_t launch_t(const AttnParams &p, hipStream_t st) {
+    const int grid = ((p.n_units + 7) / 8) * 8 * p.n_rowblocks;
+    hipLaunchKernelGGL((attn_q4c_kernel<NTS, PAGED>), dim3(grid), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+template <bool PAGED>
+hipError_t launch_p(const AttnParams &p, int nts, hipStream_t st) {
+    if (nts == 1) return launch_t<1, PAGED>(p, st);
+    if (nts == 2) return launch_t<2, PAGED>(p, st);
+    if (nts == 3) return launch_t<3, PAGED>(p, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int attn_q4c_max_split_pages() { return kMaxPages; }
+
+hipError_t launch_attn_q4c(const AttnParams &p, int nts, hipStream_t st) {
+    return p.kv.page_table != nullptr ? launch_p<true>(p, nts, st) : launch_p<false>(p, nts, st);
+}
+
+}  // namespace sv

@@ -18,6 +18,7 @@ int g_argmax_chunk = 16384;
 int g_attn_rowblocks = 0;      // 0: planner's choice
 int g_attn_posgroups = 0;      // 0: planner's choice
 int g_attn_occupancy = 0;      // 0: planner's choice
+int g_attn_q4_kernel = 0;      // 0: cooperative 4-bit kernel (head dim 256), 1: pipelined bf16-staging kernel
 
 int hip_fail(hipError_t e) {
     g_last_hip_error = (int)e;
@@ -70,7 +71,7 @@ KvView view_of(const sv_kv_cache *kv) {
     return v;
 }
 
-enum AttnKind { kValu = 0, kMfmaStaged = 1, kMfmaDma = 2 };
+enum AttnKind { kValu = 0, kMfmaStaged = 1, kMfmaDma = 2, kQ4Coop = 3 };
 
 struct AttnPlan {
     int kind;
@@ -106,17 +107,20 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
     // head dim 256; other 4-bit caches go to the register-staged kernel
     const bool q4 = kv_dtype == SV_Q4;
     pl.kind = !mfma ? kValu : ((kv_dtype == SV_BF16 || (q4 && D == 256)) ? kMfmaDma : kMfmaStaged);
-    int target = g_attn_target_wgs > 0 ? g_attn_target_wgs : (pl.kind == kMfmaDma ? 256 : 512);
+    if (pl.kind == kMfmaDma && q4 && g_attn_q4_kernel == 0) pl.kind = kQ4Coop;
+    int target = g_attn_target_wgs > 0 ? g_attn_target_wgs : ((pl.kind == kMfmaDma || pl.kind == kQ4Coop) ? 256 : 512);
     pl.occ = 1;
     const double pos_bytes = kv_dtype == SV_F32 ? D * 8.0 : (kv_dtype == SV_BF16 ? D * 4.0 : D * 1.125);
     // the pipelined kernel keeps a split's page ids in LDS
     const int64_t max_split = (pl.kind == kMfmaDma && page_size > 0)
                                   ? (int64_t)(attn_dma_max_split_pages() - 1) * page_size
-                                  : ((int64_t)1 << 40);
+                                  : ((pl.kind == kQ4Coop && page_size > 0)
+                                         ? (int64_t)(attn_q4c_max_split_pages() - 1) * page_size
+                                         : ((int64_t)1 << 40));
 
     // static split lengths: multiples of 8 positions, of the 128-position stage
     // for the pipelined kernel's 4-bit cache
-    const int64_t squant = (pl.kind == kMfmaDma && q4) ? 128 : 8;
+    const int64_t squant = ((pl.kind == kMfmaDma && q4) || pl.kind == kQ4Coop) ? 128 : 8;
     auto splits_for = [&](int units, int &split_len, int &n_splits) {
         const int64_t want = std::max<int64_t>(1, target / std::max(units, 1));
         int64_t sl = round_up(std::max<int64_t>(ceil_div(L, want), 8), squant);
@@ -161,7 +165,24 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
         pl.n_splits = (int)ceil_div(L, lo);
     };
 
-    if (mfma) {
+    if (pl.kind == kQ4Coop) {
+        // cooperative 4-bit kernel: blocks of 2 * nts row tiles (nts <= 3),
+        // one workgroup per CU
+        const int RT = (R + 15) / 16;
+        const int nts = RT <= 2 ? 1 : (RT <= 4 ? 2 : 3);
+        pl.nt = nts;
+        pl.pg = 1;
+        pl.rows_per_block = 32 * nts;
+        pl.n_rowblocks = (RT + 2 * nts - 1) / (2 * nts);
+        if (g_attn_rowblocks > 0) {
+            pl.n_rowblocks = std::max(pl.n_rowblocks, std::min(g_attn_rowblocks, (RT + 1) / 2));
+            const int per = (RT + pl.n_rowblocks - 1) / pl.n_rowblocks;     // tiles per block
+            pl.nt = (per + 1) / 2;
+            pl.rows_per_block = 32 * pl.nt;
+            pl.n_rowblocks = (R + pl.rows_per_block - 1) / pl.rows_per_block;
+        }
+        splits_for(B * Hkv * pl.n_rowblocks, pl.split_len, pl.n_splits);
+    } else if (mfma) {
         const int RT = (R + 15) / 16;
         // row tiles per wave: up to 3 on the pipelined kernel, 2 on the
         // register-staged one
@@ -237,7 +258,7 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
         // split lengths: multiples of the kernel's stage (8 positions for the
         // others), at most kMaxSplits splits per sequence, page ids of a split
         // within the pipelined kernel's LDS table
-        const int64_t q = pl.kind == kMfmaDma ? (q4 ? 128 : 32 * pl.pg) : 8;    // a power of two
+        const int64_t q = pl.kind == kQ4Coop ? 128 : (pl.kind == kMfmaDma ? (q4 ? 128 : 32 * pl.pg) : 8);   // a power of two
         const int64_t smax = std::min(round_up(L, q), max_split / q * q);
         const int64_t smin = std::max<int64_t>(q, round_up(ceil_div(L, kMaxSplits), q));
         pl.split_q = (int)q;
@@ -308,6 +329,11 @@ int sv_set_option(int option, int value) {
             if (value < 0 || value > 2) return SV_EINVAL;
             prev = g_attn_occupancy;
             g_attn_occupancy = value;
+            return prev;
+        case SV_OPT_ATTN_Q4_KERNEL:
+            if (value < 0 || value > 1) return SV_EINVAL;
+            prev = g_attn_q4_kernel;
+            g_attn_q4_kernel = value;
             return prev;
         case SV_OPT_ARGMAX_CHUNK:
             if (value <= 0 || value % 8 != 0) return SV_EINVAL;
@@ -389,7 +415,8 @@ int verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads, co
 
     hipStream_t st = (hipStream_t)stream;
     hipError_t e;
-    if (pl.kind == kMfmaDma) e = launch_attn_dma(p, D, pl.nt, pl.pg, kv->dtype == SV_Q4, pl.occ, st);
+    if (pl.kind == kQ4Coop) e = launch_attn_q4c(p, pl.nt, st);
+    else if (pl.kind == kMfmaDma) e = launch_attn_dma(p, D, pl.nt, pl.pg, kv->dtype == SV_Q4, pl.occ, st);
     else if (pl.kind == kMfmaStaged) e = launch_attn_mfma(p, kv->dtype, D, pl.nt, pl.pg, st);
     else e = launch_attn_valu(p, kv->dtype, D, st);
     if (e != hipSuccess) return hip_fail(e);

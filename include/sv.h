@@ -402,6 +402,9 @@ int sv_last_hip_error(void);
  *                           one row tile per wave (1 or 2: half-size LDS
  *                           rings, twice the work units); 0 (default) =
  *                           planner's choice
+ *   SV_OPT_ATTN_Q4_KERNEL   4-bit caches of head dim 256: 0 (default) the
+ *                           cooperative fp16 matrix-core kernel, 1 the
+ *                           pipelined kernel with bf16 staging
  * Returns the previous value, or SV_EINVAL for an unknown option or a value
  * out of range.  A workspace sized under one setting may be too small under
  * another (the call then returns SV_EWORKSPACE).
@@ -412,6 +415,7 @@ int sv_last_hip_error(void);
 #define SV_OPT_ATTN_ROWBLOCKS  3
 #define SV_OPT_ATTN_POSGROUPS  4
 #define SV_OPT_ATTN_OCCUPANCY  5
+#define SV_OPT_ATTN_Q4_KERNEL  6
 int sv_set_option(int option, int value);
 
 #ifdef __cplusplus
