@@ -50,6 +50,8 @@
 // aligned to the end of the keys, xdnf.cn notes section 5.3]: 64-bit ancestor
 // sets in LDS, applied on chunks that reach the draft rows or the split end.
 // Output: unnormalised partials (O, m, l) per row for the split merge.
+#include <type_traits>
+
 #include "attn_sched.h"
 
 namespace sv {
@@ -125,28 +127,19 @@ __device__ __forceinline__ u32x4 dequant_word(uint32_t w, h2 s, uint32_t m_lo, u
     return r;
 }
 
-// Matrix instructions with their operands placed explicitly: the queries (B
-// of S^T) and the O accumulators stay in the accumulation registers for the
-// whole split, which leaves the architectural registers to the prefetched
-// fragments and the vector work.  Every operand here is produced by an LDS
-// read, by another matrix instruction accumulating in place, or long before
-// (the queries, the sequence's last instructions before a barrier), so no
-// extra wait states are needed between them and their producers; the
-// destination never overlaps a source (early clobber), and vector reads of
-// results wait behind mfma_drain().
-__device__ __forceinline__ f32x4 mfma_s0(h8 a, h8 b_acc) {
-    f32x4 d;
-    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b_acc));
-    return d;
+__device__ __forceinline__ f32x4 mfma16(h8 a, h8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ void mfma_s(f32x4 &c, h8 a, h8 b_acc) {
-    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b_acc));
-}
+
+// O^T += V^T P^T with the accumulator tied in place in the accumulation
+// registers (the compiler's own form renames accumulators across the loop
+// back-edge and copies all of them every chunk).  Its operands come from LDS
+// reads (the compiler waits for those) and from the previous instruction of
+// the same accumulator; vector code that reads or rescales the accumulators
+// first waits behind mfma_drain().
 __device__ __forceinline__ void mfma_o(f32x4 &acc, h8 a, h8 b) {
     asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
-// wait states before vector instructions read accumulators that the last
-// matrix instructions wrote
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
 template <int NTS, bool PAGED>
@@ -259,6 +252,21 @@ __global__ __launch_bounds__(256, 1) void attn_q4c_kernel(AttnParams p) {
         }
     };
 
+    // DMA instruction j of this wave for full stage st of a contiguous cache
+    // (the last stage and paged caches: the whole stage at once through issue)
+    auto issue_one = [&](int st, int j) {
+        const int tb = p0 + st * T;
+        if constexpr (!PAGED) {
+            if (tb + T <= p1) {
+                const uint32_t slot = ring_u32 + (uint32_t)((st & 1) * STAGE + wave * LPW * 1024);
+                dma16s(__builtin_amdgcn_readfirstlane(slot + (uint32_t)(j * 1024)),
+                       dma_gb[j] + ((head_row0 + tb) << dma_rsh[j]), dma_off[j]);
+                return;
+            }
+        }
+        if (j == 0) issue(st);
+    };
+
     // ---- prologue: stage 0, the queries, stage 1 --------------------------------
     issue(0);
 
@@ -310,13 +318,12 @@ __global__ __launch_bounds__(256, 1) void attn_q4c_kernel(AttnParams p) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) v[j] = (_Float16)ldexpf((float)raw[k][pi[j]], kq);
             qf[i][k] = v;
-            asm volatile("" : "+a"(qf[i][k]));           // held in the accumulation registers
         }
     }
     if (n_st > 1) issue(1);
 
     f32x4 o[RB][4];
-    float m_ref[RB], l_s[NTS];
+    float m_ref[RB], l_s[NTS], l_p[NTS];
 #pragma unroll
     for (int t = 0; t < RB; ++t) {
         m_ref[t] = -INFINITY;
@@ -430,179 +437,198 @@ __global__ __launch_bounds__(256, 1) void attn_q4c_kernel(AttnParams p) {
         const h8 kf = kread(0, k);
 #pragma unroll
         for (int i = 0; i < NTS; ++i) {
-            if (k == 0) sacc[i] = mfma_s0(kf, qf[i][k]);
-            else mfma_s(sacc[i], kf, qf[i][k]);
+            sacc[i] = mfma16(kf, qf[i][k], k == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[i]);
         }
     }
-    mfma_drain();
     apply_mask(0, sacc);
 #pragma unroll
     for (int i = 0; i < NTS; ++i) row_max(sacc[i], i, mxb);
 
-    constexpr int MC = 8 * NTS;             // matrix instructions per phase
-    constexpr int TCC = NTS + 4;            // vector tasks of phase (c): P tiles, V words
-    constexpr int TCE = NTS + 4;            // of phase (e): row maxima, K words
+    auto vread = [&](int g, int dt) {
+        const uint8_t *vp = vst + (g & 1) * FST;
+        const int dg = 4 * wave + dt;                    // 16-wide head-dim tile
+        const s16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(__attribute__((address_space(3))) uint8_t *)(
+                vp + v_lane0 + 1024 * dg));
+        const s16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(__attribute__((address_space(3))) uint8_t *)(
+                vp + v_lane1 + 1024 * dg));
+        const short __attribute__((ext_vector_type(8))) w8 = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+        return __builtin_bit_cast(h8, w8);
+    };
 
-    h8 kf[8];
-
-    // Chunks past the last one are still dequantised and multiplied (into
-    // buffers nobody reads afterwards; the ring reads stay in bounds), so that
-    // the matrix and vector instruction streams below have no branches.  Each
-    // matrix instruction is followed by its share of vector work, and
-    // scheduling barriers keep that order.  A chunk whose row maximum moves a
-    // reference leaves the inner loop; the outer loop rescales the
-    // accumulators and re-enters at the same chunk, so the matrix
-    // accumulators are only ever written by matrix instructions inside the
-    // inner loop.
-    int g = 0;
-    bool resumed = false;
-#pragma unroll 1
-    while (true) {
-#pragma unroll 1
-        for (; g < NCH; ++g) {
-            if (!resumed) {
-                // ---- barrier 1: maxima of S(g) published; the ring slot of stage
-                // s + 1 is free once every wave has dequantised chunk 4 s + 3 ------
-                __syncthreads();
-                if (((g + 1) & (CPS - 1)) == 0) {
-                    const int st = (g + 1) / CPS + 1;
-                    if (st < n_st) issue(st);
-                }
-            }
-            resumed = false;
-            // K fragments of S(g + 1): dequantised by every thread before this
-            // barrier; their latency hides behind (b)
-            {
-                const int gs = g + 1 < NCH ? g + 1 : g;
+    // References from chunk 0's exact row maxima (every wave reads the same
+    // published values), so that typical splits never move one afterwards.
+    __syncthreads();
+    {
+        const float *mxr = mxb + l16 * RB * 2;
 #pragma unroll
-                for (int k = 0; k < 8; ++k) kf[k] = kread(gs, k);
-            }
+        for (int t = 0; t < RB; ++t) m_ref[t] = fmaxf(mxr[2 * t], mxr[2 * t + 1]);
+    }
 
-            // ---- (b) does a reference maximum move? (the same rule in every wave)
-            const float *mxr = mxb + (g & 1) * ROWS * 2 + l16 * RB * 2;
+    // Vector and matrix instructions of a SIMD do not overlap on this hardware
+    // (measured: a matrix instruction plus n vector instructions cost the sum
+    // of both), so each phase is ordered for latency: its LDS reads go out
+    // first, the vector work that needs only registers follows, and the
+    // matrix instructions (whose operands have landed by then) come last,
+    // with the vector work that needs late operands slotted between them.
+    // Chunks past the last one are still dequantised and multiplied (into
+    // buffers nobody reads afterwards; the ring reads stay in bounds), so the
+    // streams have no branches.
+    //
+    // chunk(SLOW, g, first): one chunk.  The fast form (SLOW false) returns
+    // true, before any matrix work, when a row maximum would move its
+    // reference; the caller then finishes the split with the slow form, which
+    // rescales in place.  Keeping the rescale out of the fast loop leaves its
+    // matrix accumulators written by matrix instructions only, so they stay
+    // in the accumulation registers without copies.  `first` skips barrier 1
+    // (already passed by the chunk the fast loop left).
+    auto chunk = [&](auto slow_c, int g, bool first) -> bool {
+        constexpr bool SLOW = decltype(slow_c)::value;
+        // ---- barrier 1: maxima of S(g) published, K(g + 1) staged; the ring
+        // slot of stage s + 1 is free once every wave has dequantised chunk
+        // 4 s + 3 (its loads go out between the matrix instructions below)
+        if (!first) __syncthreads();
+        const int st_issue = ((g + 1) & (CPS - 1)) == 0 ? (g + 1) / CPS + 1 : n_st;
+
+        // ---- (c) loads: row maxima of S(g), K fragments of S(g + 1), codes of
+        // V(g + 1) ----------------------------------------------------------------
+        const float *mxr = mxb + (g & 1) * ROWS * 2 + l16 * RB * 2;
+        float mxv[2 * RB];
+#pragma unroll
+        for (int t = 0; t < 2 * RB; ++t) mxv[t] = mxr[t];
+        // K fragments of S(g + 1): a ring of 4, the first 4 read now
+        const int gs = g + 1 < NCH ? g + 1 : g;
+        h8 kf[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) kf[k] = kread(gs, k);
+        const Codes cv = dq_load(1, g + 1);
+
+        if constexpr (SLOW) {
+            // ---- (b) the lazy rule, in place: a reference moves when the
+            // chunk's maximum exceeds it by more than 2^8
+            float alpha[RB];
             bool grow = false;
 #pragma unroll
             for (int t = 0; t < RB; ++t) {
-                const float cm = fmaxf(mxr[2 * t], mxr[2 * t + 1]);
-                grow = grow || (cm > m_ref[t] + 8.f);
-            }
-            if (__builtin_expect(__any(grow), 0)) break;
-
-            // ---- (c) S(g + 1) on the matrix cores; P(g) and V(g + 1) on the
-            // vector units --------------------------------------------------------
-            f32x4 sacc_n[NTS];
-            {
-                uint8_t *pw = pbuf + (g & 1) * ROWS * PROW;
-                const Codes cv = dq_load(1, g + 1);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-#pragma unroll
-                    for (int i = 0; i < NTS; ++i) {
-                        const int idx = NTS * k + i;
-                        if (k == 0) sacc_n[i] = mfma_s0(kf[k], qf[i][k]);
-                        else mfma_s(sacc_n[i], kf[k], qf[i][k]);
-#pragma unroll
-                        for (int t = 0; t < TCC; ++t) {
-                            if (idx != (t * MC) / TCC) continue;
-                            if (t < NTS) {
-                                // P of tile t: exponentials, row sums, fp16 to LDS
-                                const float mr = hh ? m_ref[NTS + t] : m_ref[t];
-                                const float mu = mr == -INFINITY ? 0.f : mr;
-                                float pr[4];
-#pragma unroll
-                                for (int j = 0; j < 4; ++j)
-                                    pr[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][j], sl2[t], -mu));
-                                l_s[t] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-                                typedef float f32x2_t __attribute__((ext_vector_type(2)));
-                                u32x2 pk;
-                                pk[0] = __builtin_bit_cast(uint32_t,
-                                                           __builtin_convertvector((f32x2_t){pr[0], pr[1]}, h2));
-                                pk[1] = __builtin_bit_cast(uint32_t,
-                                                           __builtin_convertvector((f32x2_t){pr[2], pr[3]}, h2));
-                                *(u32x2 *)(pw + (16 * (hh * NTS + t) + l16) * PROW + (16 * pt + 4 * qd) * 2) = pk;
-                            } else {
-                                dq_word(1, g + 1, cv, t - NTS);
-                            }
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                }
-            }
-
-            // stage (g + 2) / 4 is needed from here on: this wave's part landed
-            if (((g + 2) & (CPS - 1)) == 0 && g + 2 < NCH) wait_vm<0>();
-
-            // ---- barrier 2: P(g) published; V(g + 1) staged; K(g + 2)'s stage landed
-            __syncthreads();
-
-            // ---- (e) O^T += V^T P(g)^T on the matrix cores; the row maxima of
-            // S(g + 1) and K(g + 2) on the vector units; then the K fragments of
-            // S(g + 2) ------------------------------------------------------------
-            mfma_drain();                                  // S(g + 1) complete before the vector reads
-            apply_mask(g + 1, sacc_n);
-            {
-                float *mxw = mxb + ((g + 1) & 1) * ROWS * 2;
-                const int gk = g + 2 < NCH ? g + 2 : g;
-                const Codes ck = dq_load(0, gk);
-                const uint8_t *vp = vst + (g & 1) * FST;
-                const uint8_t *prd = pbuf + (g & 1) * ROWS * PROW + p_lane;
-                h8 vf[4];
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt) {
-                    const int dg = 4 * wave + dt;            // 16-wide head-dim tile
-                    const s16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4 *)(__attribute__((address_space(3))) uint8_t *)(
-                            vp + v_lane0 + 1024 * dg));
-                    const s16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4 *)(__attribute__((address_space(3))) uint8_t *)(
-                            vp + v_lane1 + 1024 * dg));
-                    const short __attribute__((ext_vector_type(8))) w8 = {h0[0], h0[1], h0[2], h0[3],
-                                                                          h1[0], h1[1], h1[2], h1[3]};
-                    vf[dt] = __builtin_bit_cast(h8, w8);
-                }
-                h8 pf[RB];
-#pragma unroll
-                for (int t = 0; t < RB; ++t) pf[t] = *(const h8 *)(prd + 16 * t * PROW);
-#pragma unroll
-                for (int t = 0; t < RB; ++t) {
-#pragma unroll
-                    for (int dt = 0; dt < 4; ++dt) {
-                        const int idx = 4 * t + dt;
-                        mfma_o(o[t][dt], vf[dt], pf[t]);
-#pragma unroll
-                        for (int u = 0; u < TCE; ++u) {
-                            if (idx != (u * MC) / TCE) continue;
-                            if (u < NTS) row_max(sacc_n[u], u, mxw);
-                            else dq_word(0, gk, ck, u - NTS);
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < NTS; ++i) sacc[i] = sacc_n[i];
-        }
-        if (g >= NCH) break;
-        // ---- a reference maximum moves at chunk g: rescale, re-enter --------
-        {
-            mfma_drain();
-            const float *mxr = mxb + (g & 1) * ROWS * 2 + l16 * RB * 2;
-            float alpha[RB];
-#pragma unroll
-            for (int t = 0; t < RB; ++t) {
-                const float cm = fmaxf(mxr[2 * t], mxr[2 * t + 1]);
+                const float cm = fmaxf(mxv[2 * t], mxv[2 * t + 1]);
                 const bool need = cm > m_ref[t] + 8.f;
                 alpha[t] = need ? __builtin_amdgcn_exp2f(m_ref[t] - cm) : 1.f;
                 m_ref[t] = need ? cm : m_ref[t];
+                grow = grow || need;
             }
+            if (__any(grow)) {
+                mfma_drain();
 #pragma unroll
-            for (int t = 0; t < RB; ++t)
+                for (int t = 0; t < RB; ++t)
 #pragma unroll
-                for (int dt = 0; dt < 4; ++dt) o[t][dt] *= alpha[t];
+                    for (int dt = 0; dt < 4; ++dt) o[t][dt] *= alpha[t];
 #pragma unroll
-            for (int i = 0; i < NTS; ++i) l_s[i] *= hh ? alpha[NTS + i] : alpha[i];
-            resumed = true;
+                for (int i = 0; i < NTS; ++i) l_s[i] *= hh ? alpha[NTS + i] : alpha[i];
+            }
         }
+
+        // P(g) (the fast form checks the references after writing it)
+        uint8_t *pw = pbuf + (g & 1) * ROWS * PROW;
+#pragma unroll
+        for (int t = 0; t < NTS; ++t) {
+            const float mr = hh ? m_ref[NTS + t] : m_ref[t];
+            const float mu = mr == -INFINITY ? 0.f : mr;
+            float pr[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pr[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][j], sl2[t], -mu));
+            l_p[t] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+            typedef float f32x2_t __attribute__((ext_vector_type(2)));
+            u32x2 pk;
+            pk[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){pr[0], pr[1]}, h2));
+            pk[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){pr[2], pr[3]}, h2));
+            *(u32x2 *)(pw + (16 * (hh * NTS + t) + l16) * PROW + (16 * pt + 4 * qd) * 2) = pk;
+        }
+        dq_word(1, g + 1, cv, 0);
+        dq_word(1, g + 1, cv, 1);
+
+        if constexpr (!SLOW) {
+            bool grow = false;
+#pragma unroll
+            for (int t = 0; t < RB; ++t) grow = grow || (fmaxf(mxv[2 * t], mxv[2 * t + 1]) > m_ref[t] + 8.f);
+            if (__builtin_expect(__any(grow), 0)) return true;
+        }
+#pragma unroll
+        for (int t = 0; t < NTS; ++t) l_s[t] += l_p[t];
+
+        // ---- S(g + 1) on the matrix cores; V(g + 1) words 2, 3 and the loads of
+        // a freed ring slot between them ------------------------------------------
+        f32x4 sacc_n[NTS];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const h8 ka = kf[k & 3];
+            if (k + 4 < 8) kf[k & 3] = kread(gs, k + 4);
+#pragma unroll
+            for (int i = 0; i < NTS; ++i) {
+                sacc_n[i] = mfma16(ka, qf[i][k], k == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc_n[i]);
+            }
+            if (k == 2) dq_word(1, g + 1, cv, 2);
+            if (k == 5) dq_word(1, g + 1, cv, 3);
+            if (k < LPW && st_issue < n_st) issue_one(st_issue, k);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (LPW > 8 && st_issue < n_st)
+#pragma unroll
+            for (int j = 8; j < LPW; ++j) issue_one(st_issue, j);
+
+        // stage (g + 2) / 4 is needed from here on: this wave's part landed
+        if (((g + 2) & (CPS - 1)) == 0 && g + 2 < NCH) wait_vm<0>();
+
+        // ---- barrier 2: P(g) published; V(g + 1) staged; K(g + 2)'s stage landed
+        __syncthreads();
+
+        // ---- (e) loads: V^T fragments, codes of K(g + 2), P(g) fragments; then
+        // the row maxima of S(g + 1), K(g + 2), and O^T += V^T P(g)^T -------------
+        {
+            h8 vf[4];
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) vf[dt] = vread(g, dt);
+            const int gk = g + 2 < NCH ? g + 2 : g;
+            const Codes ck = dq_load(0, gk);
+            const uint8_t *prd = pbuf + (g & 1) * ROWS * PROW + p_lane;
+            // P fragments: a ring of 2
+            h8 pf[2];
+            pf[0] = *(const h8 *)prd;
+            pf[1] = *(const h8 *)(prd + 16 * PROW);
+            apply_mask(g + 1, sacc_n);
+            float *mxw = mxb + ((g + 1) & 1) * ROWS * 2;
+#pragma unroll
+            for (int i = 0; i < NTS; ++i) row_max(sacc_n[i], i, mxw);
+            dq_word(0, gk, ck, 0);
+            dq_word(0, gk, ck, 1);
+#pragma unroll
+            for (int t = 0; t < RB; ++t) {
+                const h8 pa = pf[t & 1];
+                if (t + 2 < RB) pf[t & 1] = *(const h8 *)(prd + 16 * (t + 2) * PROW);
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) o[t][dt] = mfma16(vf[dt], pa, o[t][dt]);
+                // K words 2 and 3 between the matrix instructions (both after the
+                // first tile when there are only two)
+                if (t == (RB >= 4 ? 1 : 0)) dq_word(0, gk, ck, 2);
+                if (t == (RB >= 4 ? 3 : 1)) dq_word(0, gk, ck, 3);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NTS; ++i) sacc[i] = sacc_n[i];
+        return false;
+    };
+
+    using FastTag = std::integral_constant<bool, false>;
+    using SlowTag = std::integral_constant<bool, true>;
+    int g = 0;
+#pragma unroll 1
+    for (; g < NCH; ++g)
+        if (chunk(FastTag{}, g, g == 0)) break;
+    if (g < NCH) {
+        chunk(SlowTag{}, g, true);
+#pragma unroll 1
+        for (++g; g < NCH; ++g) chunk(SlowTag{}, g, false);
     }
 
     mfma_drain();
