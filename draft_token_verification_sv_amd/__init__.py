@@ -3,7 +3,9 @@
 Argument marshalling only: every step of the verify path runs in the HIP
 kernels behind the C ABI of ``include/sv.h``.  PyTorch supplies device memory
 and the current stream.  Importing this package loads the library and raises
-if it has not been built; there is no fallback implementation.
+if it has not been built; there is no fallback implementation.  With the
+environment variable ``SV_DEBUG=1`` it loads ``libsv_debug.so`` (kernels that
+record broken device-side inputs; read them with ``check_device_errors``).
 
     kv = KVCache.contiguous(k, v)                 # [B, Hkv, cap, D] bf16/fp32
     out, lse = verify_attn(kv, q, ctx_lens, parent, max_ctx)
@@ -22,21 +24,21 @@ import torch
 __all__ = [
     "SV_F32", "SV_BF16", "SV_Q4", "SVError", "KVCache", "lib", "library_path",
     "verify_attn", "verify_attn_workspace_size", "greedy_accept", "greedy_accept_workspace_size",
-    "kv_compact", "greedy_accept_compact", "kv_append", "sample_accept", "set_option", "SV_OPT_ATTN_TARGET_WGS", "SV_OPT_ARGMAX_CHUNK", "SV_OPT_ATTN_ROWBLOCKS",
-    "SV_OPT_ATTN_POSGROUPS", "SV_OPT_ATTN_OCCUPANCY", "SV_OPT_ATTN_Q4_KERNEL", "SV_F16",
-    "ssm_conv_tree", "gated_delta_net_tree", "recurrent_commit", "tree_schedule",
+    "kv_compact", "greedy_accept_compact", "kv_append", "sample_accept", "SV_F16", "TUNING_FIELDS",
+    "check_device_errors", "SV_DEVERR_PARENT", "SV_DEVERR_PAGE", "SV_DEVERR_CTX", "SV_DEVERR_PATH",
+    "ssm_conv_tree", "gated_delta_net_tree", "recurrent_commit", "tree_schedule", "debug_build",
 ]
 
 SV_F32, SV_BF16, SV_Q4, SV_F16 = 0, 1, 2, 3
-SV_OPT_ATTN_TARGET_WGS, SV_OPT_ARGMAX_CHUNK, SV_OPT_ATTN_ROWBLOCKS, SV_OPT_ATTN_POSGROUPS = 1, 2, 3, 4
-SV_OPT_ATTN_OCCUPANCY = 5
-SV_OPT_ATTN_Q4_KERNEL = 6
+SV_DEVERR_PARENT, SV_DEVERR_PAGE, SV_DEVERR_CTX, SV_DEVERR_PATH = 1, 2, 4, 8
 
-library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsv.so")
+debug_build = os.environ.get("SV_DEBUG", "") not in ("", "0")
+library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                            "libsv_debug.so" if debug_build else "libsv.so")
 if not os.path.exists(library_path):
     raise ImportError(
-        f"{library_path} is missing: build it with `python draft_token_verification_sv_amd/build.py` "
-        "(there is no CPU fallback)")
+        f"{library_path} is missing: build it with `python draft_token_verification_sv_amd/build.py"
+        f"{' --debug' if debug_build else ''}` (there is no CPU fallback)")
 lib = ctypes.CDLL(library_path)
 
 
@@ -57,6 +59,34 @@ class _KvDesc(ctypes.Structure):
         ("layer_stride", ctypes.c_int64),
         ("scale_layer_stride", ctypes.c_int64),
     ]
+
+
+# sv_tuning: per-call launch tuning (0 = the library's choice for every field)
+TUNING_FIELDS = ("attn_target_wgs", "attn_rowblocks", "attn_posgroups", "attn_occupancy", "attn_q4_kernel",
+                 "argmax_chunk")
+
+
+class _Tuning(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in TUNING_FIELDS]
+
+
+def _tuning(tuning) -> Optional[_Tuning]:
+    """A dict of sv_tuning fields (``attn_q4_kernel`` may also be "cooperative"
+    or "pipelined") -> the struct, or None."""
+    if not tuning:
+        return None
+    t = _Tuning()
+    for key, val in tuning.items():
+        if key not in TUNING_FIELDS:
+            raise ValueError(f"unknown tuning field {key!r}")
+        if key == "attn_q4_kernel" and isinstance(val, str):
+            val = {"cooperative": 1, "pipelined": 2}[val]
+        setattr(t, key, int(val))
+    return t
+
+
+def _tref(t: Optional[_Tuning]):
+    return None if t is None else ctypes.byref(t)
 
 
 _P = ctypes.c_void_p
@@ -100,8 +130,17 @@ lib.sv_recurrent_commit.argtypes = [_I, _I, _I, _I, _I, _P, _I, _P, _I, _I, _P, 
 lib.sv_error_string.restype = ctypes.c_char_p
 lib.sv_error_string.argtypes = [_I]
 lib.sv_last_hip_error.restype = _I
-lib.sv_set_option.restype = _I
-lib.sv_set_option.argtypes = [_I, _I]
+lib.sv_verify_attn_tuned_workspace_size.restype = ctypes.c_size_t
+lib.sv_verify_attn_tuned_workspace_size.argtypes = [ctypes.POINTER(_KvDesc), _I, _I, _I, _I, _I,
+                                                    ctypes.POINTER(_Tuning)]
+lib.sv_verify_attn_tuned.restype = _I
+lib.sv_verify_attn_tuned.argtypes = [ctypes.POINTER(_KvDesc), _I, _I, _I, _P, _I, _P, _I, _P,
+                                     ctypes.c_float, _I, ctypes.POINTER(_Tuning), _P, _P, _P, ctypes.c_size_t, _P]
+lib.sv_greedy_accept_tuned.restype = _I
+lib.sv_greedy_accept_tuned.argtypes = [_I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Tuning), _P,
+                                       ctypes.c_size_t, _P]
+lib.sv_check_device_errors.restype = _I
+lib.sv_check_device_errors.argtypes = [_P]
 
 
 class SVError(RuntimeError):
@@ -214,17 +253,36 @@ class KVCache:
         return cls(k=k, v=v, k_scale=k_scale, v_scale=v_scale, page_table=page_table)
 
 
+# Default workspaces, one per (kind, device, stream): a workspace serves one
+# stream at a time, and each is allocated while its stream is current, so the
+# caching allocator orders its reuse on that same stream.
 _ws_cache: dict = {}
 
 
+def _ws_key(kind: str, dev: torch.device) -> tuple:
+    return (kind, torch.device(dev).index, _stream(dev))
+
+
 def _workspace(kind: str, dev: torch.device, nbytes: int, zero: bool) -> torch.Tensor:
-    key = (kind, dev)
+    key = _ws_key(kind, dev)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
         size = max(nbytes, 256)
         buf = (torch.zeros if zero else torch.empty)(size, dtype=torch.uint8, device=dev)
         _ws_cache[key] = buf
     return buf
+
+
+def _drop_workspace(kind: str, dev: torch.device) -> None:
+    """Forget a default workspace after a failed call (an acceptance workspace
+    must be all zeros on entry; a failed call may not have left it so)."""
+    _ws_cache.pop(_ws_key(kind, dev), None)
+
+
+def _check_ws(rc: int, where: str, kind: str, dev: torch.device, default_ws: bool) -> None:
+    if rc != 0 and default_ws:
+        _drop_workspace(kind, dev)
+    _check(rc, where)
 
 
 def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
@@ -234,8 +292,12 @@ def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
 
 
 def verify_attn_workspace_size(kv: KVCache, batch: int, n_nodes: int, n_q_heads: int, max_ctx: int,
-                               window: int = 0) -> int:
+                               window: int = 0, tuning: Optional[dict] = None) -> int:
     d = kv.desc()
+    t = _tuning(tuning)
+    if t is not None:
+        return int(lib.sv_verify_attn_tuned_workspace_size(ctypes.byref(d), batch, n_nodes, n_q_heads, max_ctx,
+                                                           window, _tref(t)))
     if window:
         return int(lib.sv_verify_attn_window_workspace_size(ctypes.byref(d), batch, n_nodes, n_q_heads, max_ctx,
                                                             window))
@@ -245,10 +307,12 @@ def verify_attn_workspace_size(kv: KVCache, batch: int, n_nodes: int, n_q_heads:
 def verify_attn(kv: KVCache, q: torch.Tensor, ctx_lens: torch.Tensor, parent: torch.Tensor,
                 max_ctx: int, sm_scale: float = 0.0, out: Optional[torch.Tensor] = None,
                 lse: Optional[torch.Tensor] = None, want_lse: bool = True,
-                workspace: Optional[torch.Tensor] = None, layer: int = 0, window: int = 0):
+                workspace: Optional[torch.Tensor] = None, layer: int = 0, window: int = 0,
+                tuning: Optional[dict] = None):
     """Masked GQA attention of the verify rows.  ``q`` ``[B, N, Hq, D]``.
 
-    ``window`` > 0: only the last ``window`` key rows of each sequence."""
+    ``window`` > 0: only the last ``window`` key rows of each sequence.
+    ``tuning``: sv_tuning fields for this call (see ``TUNING_FIELDS``)."""
     if q.dim() != 4 or not q.is_contiguous() or not q.is_cuda:
         raise ValueError("q must be a contiguous [B, N, Hq, D] device tensor")
     B, N, Hq, D = q.shape
@@ -259,21 +323,24 @@ def verify_attn(kv: KVCache, q: torch.Tensor, ctx_lens: torch.Tensor, parent: to
     if lse is None and want_lse:
         lse = torch.empty((B, N, Hq), dtype=torch.float32, device=q.device)
     d = kv.desc(layer)
-    if window:
-        need = int(lib.sv_verify_attn_window_workspace_size(ctypes.byref(d), B, N, Hq, int(max_ctx), int(window)))
-    else:
-        need = int(lib.sv_verify_attn_workspace_size(ctypes.byref(d), B, N, Hq, int(max_ctx)))
-    if workspace is None:
+    t = _tuning(tuning)
+    default_ws = workspace is None
+    if default_ws:
+        need = int(lib.sv_verify_attn_tuned_workspace_size(ctypes.byref(d), B, N, Hq, int(max_ctx), int(window),
+                                                           _tref(t)))
         workspace = _workspace("attn", q.device, need, zero=False)
     args = (ctypes.byref(d), B, N, Hq, _ptr(ctx_lens), int(max_ctx), _ptr(q), _dtype_code(q), _ptr(parent),
             float(sm_scale))
     tail = (_ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device))
-    if window:
+    if t is not None:
+        rc = lib.sv_verify_attn_tuned(*args, int(window), _tref(t), *tail)
+        _check_ws(rc, "sv_verify_attn_tuned", "attn", q.device, default_ws)
+    elif window:
         rc = lib.sv_verify_attn_window(*args, int(window), *tail)
-        _check(rc, "sv_verify_attn_window")
+        _check_ws(rc, "sv_verify_attn_window", "attn", q.device, default_ws)
     else:
         rc = lib.sv_verify_attn(*args, *tail)
-        _check(rc, "sv_verify_attn")
+        _check_ws(rc, "sv_verify_attn", "attn", q.device, default_ws)
     return out, lse
 
 
@@ -282,7 +349,8 @@ def greedy_accept_workspace_size(batch: int, n_nodes: int, vocab: int) -> int:
 
 
 def greedy_accept(logits: torch.Tensor, draft_ids: torch.Tensor, parent: torch.Tensor,
-                  want_argmax: bool = True, workspace: Optional[torch.Tensor] = None, outputs=None):
+                  want_argmax: bool = True, workspace: Optional[torch.Tensor] = None, outputs=None,
+                  tuning: Optional[dict] = None):
     """Greedy acceptance.  ``logits`` ``[B, N, V]`` fp32/bf16.
 
     Returns ``(accept_len [B], path [B, N], tokens [B, N], argmax [B, N] or None)``.
@@ -301,12 +369,20 @@ def greedy_accept(logits: torch.Tensor, draft_ids: torch.Tensor, parent: torch.T
     else:
         acc, path, tok, am = outputs
     need = int(lib.sv_greedy_accept_workspace_size(B, N, V))
-    if workspace is None:
+    default_ws = workspace is None
+    if default_ws:
         workspace = _workspace("accept", dev, need, zero=True)
+    t = _tuning(tuning)
+    if t is not None:
+        rc = lib.sv_greedy_accept_tuned(B, N, V, _ptr(logits), _dtype_code(logits), _ptr(draft_ids), _ptr(parent),
+                                        _ptr(acc), _ptr(path), _ptr(tok), _ptr(am), _tref(t), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(dev))
+        _check_ws(rc, "sv_greedy_accept_tuned", "accept", dev, default_ws)
+        return acc, path, tok, am
     rc = lib.sv_greedy_accept(B, N, V, _ptr(logits), _dtype_code(logits), _ptr(draft_ids), _ptr(parent),
                               _ptr(acc), _ptr(path), _ptr(tok), _ptr(am), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _stream(dev))
-    _check(rc, "sv_greedy_accept")
+    _check_ws(rc, "sv_greedy_accept", "accept", dev, default_ws)
     return acc, path, tok, am
 
 
@@ -335,19 +411,20 @@ def sample_accept(logits: torch.Tensor, gumbel: torch.Tensor, temperature: float
     else:
         acc, path, tok, ys = outputs
     need = int(lib.sv_greedy_accept_workspace_size(B, N, V))
-    if workspace is None:
+    default_ws = workspace is None
+    if default_ws:
         workspace = _workspace("accept", dev, need, zero=True)
     if top_k:
         rc = lib.sv_sample_accept_topk(B, N, V, _ptr(logits), _dtype_code(logits), _ptr(gumbel), float(temperature),
                                        int(top_k), _ptr(draft_ids), _ptr(parent), _ptr(acc), _ptr(path), _ptr(tok),
                                        _ptr(ys), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                        _stream(dev))
-        _check(rc, "sv_sample_accept_topk")
+        _check_ws(rc, "sv_sample_accept_topk", "accept", dev, default_ws)
         return acc, path, tok, ys
     rc = lib.sv_sample_accept(B, N, V, _ptr(logits), _dtype_code(logits), _ptr(gumbel), float(temperature),
                               _ptr(draft_ids), _ptr(parent), _ptr(acc), _ptr(path), _ptr(tok), _ptr(ys),
                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
-    _check(rc, "sv_sample_accept")
+    _check_ws(rc, "sv_sample_accept", "accept", dev, default_ws)
     return acc, path, tok, ys
 
 
@@ -394,7 +471,8 @@ def greedy_accept_compact(logits: torch.Tensor, draft_ids: torch.Tensor, parent:
     if new_lens is None:
         new_lens = torch.empty(B, dtype=torch.int32, device=dev)
     need = int(lib.sv_greedy_accept_workspace_size(B, N, V))
-    if workspace is None:
+    default_ws = workspace is None
+    if default_ws:
         workspace = _workspace("accept", dev, need, zero=True)
     d = kv.desc(0)
     L = kv.n_layers if n_layers is None else n_layers
@@ -402,7 +480,7 @@ def greedy_accept_compact(logits: torch.Tensor, draft_ids: torch.Tensor, parent:
                                       _ptr(acc), _ptr(path), _ptr(tok), _ptr(am), ctypes.byref(d), L,
                                       _ptr(ctx_lens), int(max_ctx), _ptr(new_lens), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(), _stream(dev))
-    _check(rc, "sv_greedy_accept_compact")
+    _check_ws(rc, "sv_greedy_accept_compact", "accept", dev, default_ws)
     return acc, path, tok, am, new_lens
 
 
@@ -553,5 +631,13 @@ def recurrent_commit(state_nodes: torch.Tensor, state: torch.Tensor, x: torch.Te
     _check(rc, "sv_recurrent_commit")
 
 
-def set_option(option: int, value: int) -> int:
-    return int(lib.sv_set_option(option, value))
+def check_device_errors(device=None) -> int:
+    """The precondition bits (SV_DEVERR_*) recorded on ``device`` since the
+    previous check, then cleared; waits for the device's current stream.
+    Always 0 with the release library."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    with torch.cuda.device(dev):
+        rc = int(lib.sv_check_device_errors(_stream(dev)))
+    if rc < 0:
+        raise SVError(rc, "sv_check_device_errors")
+    return rc

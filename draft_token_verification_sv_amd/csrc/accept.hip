@@ -65,19 +65,22 @@ __device__ void compact_sequence(const CompactParams &cp, int b, int ctx, const 
                 r >>= 1;
                 const int h = r % cp.Hkv, layer = r / cp.Hkv;
                 const int j = mov_s[m];
-                const int64_t ri = kv_row_index(cp.kv, b, cp.Hkv, h, ctx + (pass == 0 ? path_s[j] : j));
-                if (ri < 0) continue;
+                const int64_t ri = kv_row_index(cp.kv, b, cp.Hkv, h, ctx + (pass == 0 ? path_s[j] : j), cp.err);
+                // a source whose page is outside the pool reads as a zero row; such
+                // a destination is not written
+                if (ri < 0 && pass == 1) continue;
                 uint8_t *lds = stage + ul * unit_bytes;
                 if (pc < vpieces) {
                     uint8_t *g = (uint8_t *)(which ? cp.kv.v : cp.kv.k) + (int64_t)layer * cp.layer_stride +
                                  ri * row_bytes + pc * 16;
-                    if (pass == 0) *(u32x4 *)(lds + pc * 16) = *(const u32x4 *)g;
+                    const u32x4 zero = {0u, 0u, 0u, 0u};
+                    if (pass == 0) *(u32x4 *)(lds + pc * 16) = ri < 0 ? zero : *(const u32x4 *)g;
                     else *(u32x4 *)g = *(const u32x4 *)(lds + pc * 16);
                 } else {
                     const int w = pc - vpieces;
                     uint8_t *g = (uint8_t *)(which ? cp.kv.vs : cp.kv.ks) + (int64_t)layer * cp.scale_layer_stride +
                                  ri * srow_bytes + w * 4;
-                    if (pass == 0) *(uint32_t *)(lds + row_bytes + w * 4) = *(const uint32_t *)g;
+                    if (pass == 0) *(uint32_t *)(lds + row_bytes + w * 4) = ri < 0 ? 0u : *(const uint32_t *)g;
                     else *(uint32_t *)g = *(const uint32_t *)(lds + row_bytes + w * 4);
                 }
             }
@@ -199,7 +202,7 @@ __global__ __launch_bounds__(256) void argmax_accept_kernel(AcceptParams p) {
     }
     if (lane == 0) __hip_atomic_store(&p.seqs_done[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if constexpr (COMPACT) {
-        if (lane == 0) cinfo_s[0] = clamp_ctx(p.cp.ctx_lens[b], p.cp.max_ctx);
+        if (lane == 0) cinfo_s[0] = ctx_of(p.cp.ctx_lens, b, p.cp.max_ctx, p.err);
     }
     const int a = walk_sequence<COMPACT>(p, b, lane, am_s, dr_s, par_s, path_s);
     if (p.argmax != nullptr && lane < N) p.argmax[(int64_t)b * N + lane] = am_s[lane];

@@ -61,7 +61,7 @@ __device__ int walk_sequence(const AcceptParams &p, int b, int lane, int *am_s, 
             __hip_atomic_exchange(&p.keys[(int64_t)b * N + lane], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         am_s[lane] = (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
         dr_s[lane] = p.draft[(int64_t)b * N + lane];
-        par_s[lane] = p.parent[(int64_t)b * N + lane];
+        par_s[lane] = parent_of(p.parent + (int64_t)b * N, lane, p.err);
     }
     __builtin_amdgcn_s_waitcnt(0);           // the LDS writes of all lanes (one wave: no barrier)
     __builtin_amdgcn_wave_barrier();

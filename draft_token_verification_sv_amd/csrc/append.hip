@@ -32,8 +32,8 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
     const int b = (int)(rest / p.n);
     const int D = p.D;
     if (4 * lane >= D) return;
-    const int pos = clamp_ctx(p.ctx_lens[b], p.max_ctx) + i;
-    const int64_t ri = kv_row_index(p.kv, b, p.Hkv, h, pos);
+    const int pos = ctx_of(p.ctx_lens, b, p.max_ctx, p.err) + i;
+    const int64_t ri = kv_row_index(p.kv, b, p.Hkv, h, pos, p.err);
     if (ri < 0) return;
 
     // the lane's 4 source values

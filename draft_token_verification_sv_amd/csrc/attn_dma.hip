@@ -125,6 +125,10 @@ __device__ __forceinline__ void dma16s(uint32_t lds_base, const void *sbase, uin
 
 constexpr int kMaxSplitPages = 512;
 
+// the source of every DMA of a row whose page lies outside the pool: one row
+// of zeros as wide as the widest row (bf16, head dim 256)
+__device__ __attribute__((aligned(16))) uint8_t zero_row[512] = {};
+
 template <int D, int NT, int PG, bool PAGED, bool Q4, int OCC>
 __global__ __launch_bounds__(256, OCC) void attn_dma_kernel(AttnParams p) {
     using C = DCfg<D, NT, PG, Q4, OCC>;
@@ -158,7 +162,7 @@ __global__ __launch_bounds__(256, OCC) void attn_dma_kernel(AttnParams p) {
 
     // ---- tree (only splits that reach the draft rows) and page ids ---------
     const bool has_draft = p1 > ctx;
-    if (has_draft && tid < N) par_s[tid] = p.parent[(int64_t)b * N + tid];
+    if (has_draft && tid < N) par_s[tid] = parent_of(p.parent + (int64_t)b * N, tid, p.err);
     int first_page = 0;
     const int ps_shift = (p.kv.page_size > 0 && (p.kv.page_size & (p.kv.page_size - 1)) == 0)
                              ? __builtin_ctz((unsigned)p.kv.page_size) : -1;
@@ -166,9 +170,10 @@ __global__ __launch_bounds__(256, OCC) void attn_dma_kernel(AttnParams p) {
         first_page = p0 / p.kv.page_size;
         const int last_page = (p1 - 1) / p.kv.page_size;
         for (int e = tid; e <= last_page - first_page; e += 256) {
-            int pgid = p.kv.page_table[(int64_t)b * p.kv.max_pages + first_page + e];
-            pgid = pgid < 0 ? 0 : (pgid >= p.kv.capacity ? (int)p.kv.capacity - 1 : pgid);
-            pages_s[e] = pgid;
+            const int pgid = p.kv.page_table[(int64_t)b * p.kv.max_pages + first_page + e];
+            const bool bad = pgid < 0 || pgid >= p.kv.capacity;
+            SV_DEVCHECK(p.err, bad, SV_DEVERR_PAGE);
+            pages_s[e] = bad ? -1 : pgid;                  // -1: a zero row
         }
     }
     __syncthreads();
@@ -265,8 +270,11 @@ __global__ __launch_bounds__(256, OCC) void attn_dma_kernel(AttnParams p) {
                     pq = pos / ps;
                     pr = pos - pq * ps;
                 }
-                const int64_t ri = ((int64_t)pages_s[pq - first_page] * p.Hkv + kvh) * ps + pr;
-                dma16(__builtin_amdgcn_readfirstlane(slot + (uint32_t)(j * 1024)), dma_gb[jj] + (ri << rsh) + col);
+                const int pg = pages_s[pq - first_page];
+                const int64_t ri = ((int64_t)pg * p.Hkv + kvh) * ps + pr;
+                // a page outside the pool reads the zero row
+                const uint8_t *src = pg < 0 ? zero_row + col : dma_gb[jj] + (ri << rsh) + col;
+                dma16(__builtin_amdgcn_readfirstlane(slot + (uint32_t)(j * 1024)), src);
             }
         }
     };

@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnParams p) {
     const int l16 = lane & 15, qd = lane >> 4;
 
     if (p1 > ctx) {                     // this split reaches the draft rows
-        if (tid < N) par_s[tid] = p.parent[(int64_t)b * N + tid];
+        if (tid < N) par_s[tid] = parent_of(p.parent + (int64_t)b * N, tid, p.err);
         __syncthreads();
         if (tid < N) anc_s[tid] = ancestor_bits(par_s, tid);
         // visible after the first barrier of the tile loop
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnParams p) {
 
     auto row_idx = [&](int pos) -> int64_t {
         if (!PAGED) return ((int64_t)b * p.Hkv + kvh) * p.kv.capacity + pos;
-        return kv_row_index(p.kv, b, p.Hkv, kvh, pos);
+        return kv_row_index(p.kv, b, p.Hkv, kvh, pos, p.err);
     };
 
     auto load_tile = [&](int tp) {

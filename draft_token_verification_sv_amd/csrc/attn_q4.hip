@@ -178,14 +178,16 @@ __global__ __launch_bounds__(256, 1) void attn_q4c_kernel(AttnParams p) {
 
     // ---- tree (splits that reach the draft rows) and page ids --------------
     const bool has_draft = p1 > ctx;
-    if (has_draft && tid < N) par_s[tid] = p.parent[(int64_t)b * N + tid];
+    if (has_draft && tid < N) par_s[tid] = parent_of(p.parent + (int64_t)b * N, tid, p.err);
     int first_page = 0;
     if constexpr (PAGED) {
         first_page = p0 / p.kv.page_size;
         const int last_page = (p1 - 1) / p.kv.page_size;
         for (int e = tid; e <= last_page - first_page; e += 256) {
             const int pgid = p.kv.page_table[(int64_t)b * p.kv.max_pages + first_page + e];
-            pages_s[e] = (pgid < 0 || pgid >= p.kv.capacity) ? -1 : pgid;
+            const bool bad = pgid < 0 || pgid >= p.kv.capacity;
+            SV_DEVCHECK(p.err, bad, SV_DEVERR_PAGE);
+            pages_s[e] = bad ? -1 : pgid;
         }
     }
     __syncthreads();
@@ -497,11 +499,12 @@ __global__ __launch_bounds__(256, 1) void attn_q4c_kernel(AttnParams p) {
         float mxv[2 * RB];
 #pragma unroll
         for (int t = 0; t < 2 * RB; ++t) mxv[t] = mxr[t];
-        // K fragments of S(g + 1): a ring of 4, the first 4 read now
+        // K fragments of S(g + 1): a ring of KR, the first KR read now
+        constexpr int KR = 3;
         const int gs = g + 1 < NCH ? g + 1 : g;
-        h8 kf[4];
+        h8 kf[KR];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) kf[k] = kread(gs, k);
+        for (int k = 0; k < KR; ++k) kf[k] = kread(gs, k);
         const Codes cv = dq_load(1, g + 1);
 
         if constexpr (SLOW) {
@@ -561,8 +564,8 @@ __global__ __launch_bounds__(256, 1) void attn_q4c_kernel(AttnParams p) {
         f32x4 sacc_n[NTS];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const h8 ka = kf[k & 3];
-            if (k + 4 < 8) kf[k & 3] = kread(gs, k + 4);
+            const h8 ka = kf[k % KR];
+            if (k + KR < 8) kf[k % KR] = kread(gs, k + KR);
 #pragma unroll
             for (int i = 0; i < NTS; ++i) {
                 sacc_n[i] = mfma16(ka, qf[i][k], k == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc_n[i]);

@@ -169,7 +169,7 @@ __device__ __forceinline__ bool attn_unit(const AttnParams &p, int u, bool recor
         const int bh = u / p.n_splits;
         w.kvh = bh % p.Hkv;
         w.b = bh / p.Hkv;
-        w.ctx = clamp_ctx(p.ctx_lens[w.b], p.max_ctx);
+        w.ctx = ctx_of(p.ctx_lens, w.b, p.max_ctx, p.err);
         const int L = w.ctx + p.N;
         const int lo = L - (int)key_range(p, w.ctx);    // first key row (0 without a window)
         w.p0 = lo + w.s * p.split_len;
@@ -187,7 +187,7 @@ __device__ __forceinline__ bool attn_unit(const AttnParams &p, int u, bool recor
         // one sequence per lane of wavefront 0: every reduction is a DPP scan,
         // no barrier until the result is published
         if (wave == 0) {
-            const int cb = lane < p.B ? clamp_ctx(p.ctx_lens[lane], p.max_ctx) : 0;
+            const int cb = lane < p.B ? ctx_of(p.ctx_lens, lane, p.max_ctx, p.err) : 0;
             const uint32_t Lb = lane < p.B ? key_range(p, cb) : 0u;
             const double tot = wave_sum_f64((double)Lb);
             int lo, hi;
@@ -209,7 +209,7 @@ __device__ __forceinline__ bool attn_unit(const AttnParams &p, int u, bool recor
 #pragma unroll
         for (int k = 0; k < kSchedRounds; ++k) {
             const int b = 256 * k + tid;
-            const int cb = b < p.B ? clamp_ctx(p.ctx_lens[b], p.max_ctx) : 0;
+            const int cb = b < p.B ? ctx_of(p.ctx_lens, b, p.max_ctx, p.err) : 0;
             Lr[k] = b < p.B ? key_range(p, cb) : 0u;
             Fr[k] = (uint32_t)(cb + p.N);
             tl += (double)Lr[k];

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
     const int rglob = rb * kRowsV + r;
     const bool row_ok = r < p.rows_per_block && rglob < R;
 
-    if (tid < N) par_s[tid] = p.parent[(int64_t)b * N + tid];
+    if (tid < N) par_s[tid] = parent_of(p.parent + (int64_t)b * N, tid, p.err);
     __syncthreads();
     if (tid < N) anc_s[tid] = ancestor_bits(par_s, tid);
 
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
             float kv8[VPC], vv8[VPC];
             bool ok = false;
             if (pos < p1) {
-                const int64_t ri = kv_row_index(p.kv, b, p.Hkv, kvh, pos);
+                const int64_t ri = kv_row_index(p.kv, b, p.Hkv, kvh, pos, p.err);
                 if (ri >= 0) {
                     load_row_chunk_f32<KVT>(kv8, kb, ksb, ri, ch, D);
                     load_row_chunk_f32<KVT>(vv8, vb, vsb, ri, ch, D);
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
     } else {
         base = ((int64_t)b * p.Hkv + kvh) * p.n_splits;
         ns_cap = p.n_splits;
-        const int L = (int)key_range(p, clamp_ctx(p.ctx_lens[b], p.max_ctx));
+        const int L = (int)key_range(p, ctx_of(p.ctx_lens, b, p.max_ctx, p.err));
         ns = min(p.n_splits, (L + p.split_len - 1) / p.split_len);
     }
     const float *op = p.part_o + (base * p.R + r) * D + 4 * c;

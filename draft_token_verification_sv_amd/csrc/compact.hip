@@ -31,13 +31,15 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
     const int N = p.N;
 
     // the length, the accept count and this thread's path entry load together
-    const int ctx = clamp_ctx(p.ctx_lens[b], p.max_ctx);
+    const int ctx = ctx_of(p.ctx_lens, b, p.max_ctx, p.err);
     const int a = p.accept_len[b];
     const int pj = (tid >= 1 && tid < N) ? p.path[(int64_t)b * N + tid] : -1;
     const bool a_ok = a >= 0 && a < N;
     if (p.new_lens != nullptr && which == 0 && h == 0 && layer == 0 && tid == 0)
         p.new_lens[b] = a_ok ? ctx + a + 1 : ctx;
+    SV_DEVCHECK(p.err, tid == 0 && !a_ok, SV_DEVERR_PATH);
     if (!a_ok) return;
+    SV_DEVCHECK(p.err, tid >= 1 && tid <= a && (pj < tid || pj >= N), SV_DEVERR_PATH);
 
     // moving rows: j in [1, a] with j < path[j] < N
     if (tid < 64) src_s[tid] = (tid >= 1 && tid <= a && pj > tid && pj < N) ? pj : -1;
@@ -53,14 +55,15 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
                          ? (uint8_t *)(which ? p.kv.vs : p.kv.ks) + (int64_t)layer * p.scale_layer_stride
                          : nullptr;
 
-    // gather every source row ...
+    // gather every source row (a source whose page is outside the pool reads
+    // as a zero row) ...
     for (int e = tid; e < 64 * chunks; e += 256) {
         const int jj = e / chunks, ch = e % chunks;
         const int src = src_s[jj];
         if (src < 0) continue;
-        const int64_t ri = kv_row_index(p.kv, b, p.Hkv, h, ctx + src);
-        if (ri < 0) continue;
-        *(u32x4 *)(buf + jj * kMaxRowBytes + ch * 16) = *(const u32x4 *)(base + ri * row_bytes + ch * 16);
+        const int64_t ri = kv_row_index(p.kv, b, p.Hkv, h, ctx + src, p.err);
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        *(u32x4 *)(buf + jj * kMaxRowBytes + ch * 16) = ri < 0 ? zero : *(const u32x4 *)(base + ri * row_bytes + ch * 16);
     }
     if (sbase != nullptr) {
         for (int e = tid; e < 64 * schunks; e += 256) {
@@ -68,8 +71,7 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
             const int src = src_s[jj];
             if (src < 0) continue;
             const int64_t ri = kv_row_index(p.kv, b, p.Hkv, h, ctx + src);
-            if (ri < 0) continue;
-            *(uint32_t *)(sbuf + jj * 16 + w * 4) = *(const uint32_t *)(sbase + ri * srow_bytes + w * 4);
+            *(uint32_t *)(sbuf + jj * 16 + w * 4) = ri < 0 ? 0u : *(const uint32_t *)(sbase + ri * srow_bytes + w * 4);
         }
     }
     __syncthreads();
@@ -77,7 +79,7 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
     for (int e = tid; e < 64 * chunks; e += 256) {
         const int jj = e / chunks, ch = e % chunks;
         if (src_s[jj] < 0) continue;
-        const int64_t ri = kv_row_index(p.kv, b, p.Hkv, h, ctx + jj);
+        const int64_t ri = kv_row_index(p.kv, b, p.Hkv, h, ctx + jj, p.err);
         if (ri < 0) continue;
         *(u32x4 *)(base + ri * row_bytes + ch * 16) = *(const u32x4 *)(buf + jj * kMaxRowBytes + ch * 16);
     }

@@ -46,6 +46,20 @@ __device__ __forceinline__ uint32_t pack_hi_halves(uint32_t a, uint32_t b) {
     return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
+// Precondition reports (sv_check_device_errors): in a build with SV_DEBUG a
+// kernel that meets a broken device-side input ORs its bit into the word;
+// release builds compile the checks away.
+#ifdef SV_DEBUG
+#define SV_DEVCHECK(err, cond, bit)                                   \
+    do {                                                              \
+        if ((err) != nullptr && (cond)) atomicOr((err), (unsigned)(bit)); \
+    } while (0)
+#else
+#define SV_DEVCHECK(err, cond, bit) \
+    do {                            \
+    } while (0)
+#endif
+
 // Ancestor-or-self bit set of every node of one tree, built from the parent
 // array in LDS.  `par` holds parent[0..n-1]; a parent that is not an earlier
 // node ends the walk (no out-of-range access, bounded by n steps).
@@ -65,18 +79,37 @@ __device__ __forceinline__ uint64_t ancestor_bits(const int *par, int i) {
 // Row number of KV row (b, h, pos) in the cache arrays (rows of any width); -1
 // when the page id is outside the pool (the row is then read as zeros and
 // never written).
-__device__ __forceinline__ int64_t kv_row_index(const KvView &kv, int b, int Hkv, int h, int pos) {
+__device__ __forceinline__ int64_t kv_row_index(const KvView &kv, int b, int Hkv, int h, int pos,
+                                                unsigned int *err = nullptr) {
     if (kv.page_table == nullptr) {
         return ((int64_t)b * Hkv + h) * kv.capacity + pos;
     }
     const int ps = kv.page_size;
     const int page = kv.page_table[(int64_t)b * kv.max_pages + pos / ps];
-    if (page < 0 || page >= kv.capacity) return -1;
+    if (page < 0 || page >= kv.capacity) {
+        SV_DEVCHECK(err, true, SV_DEVERR_PAGE);
+        return -1;
+    }
     return ((int64_t)page * Hkv + h) * ps + (pos % ps);
 }
 
 __device__ __forceinline__ int clamp_ctx(int c, int max_ctx) {
     return c < 0 ? 0 : (c > max_ctx ? max_ctx : c);
+}
+
+// ctx_lens[b], clamped to [0, max_ctx] (out-of-range values reported)
+__device__ __forceinline__ int ctx_of(const int32_t *ctx_lens, int b, int max_ctx, unsigned int *err) {
+    const int c = ctx_lens[b];
+    SV_DEVCHECK(err, c < 0 || c > max_ctx, SV_DEVERR_CTX);
+    return clamp_ctx(c, max_ctx);
+}
+
+// parent[b][i] (row pointer `par_row`); an entry of node i >= 1 outside
+// [0, i) is reported (the walks treat it as the end of the path)
+__device__ __forceinline__ int parent_of(const int32_t *par_row, int i, unsigned int *err) {
+    const int v = par_row[i];
+    SV_DEVCHECK(err, i >= 1 && (v < 0 || v >= i), SV_DEVERR_PARENT);
+    return v;
 }
 
 // XOR lane exchange within a wavefront of 64

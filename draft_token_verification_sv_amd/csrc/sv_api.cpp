@@ -13,17 +13,36 @@ namespace sv {
 namespace {
 
 thread_local int g_last_hip_error = 0;
-int g_attn_target_wgs = 0;     // 0: choose by batch (see plan_attn)
-int g_argmax_chunk = 16384;
-int g_attn_rowblocks = 0;      // 0: planner's choice
-int g_attn_posgroups = 0;      // 0: planner's choice
-int g_attn_occupancy = 0;      // 0: planner's choice
-int g_attn_q4_kernel = 0;      // 0: cooperative 4-bit kernel (head dim 256), 1: pipelined bf16-staging kernel
 
-int hip_fail(hipError_t e) {
-    g_last_hip_error = (int)e;
-    return SV_EHIP;
+// One call's tuning (sv_tuning), validated, zeros meaning the library's choice.
+struct Tuning {
+    int attn_target_wgs = 0;   // 0: choose by kernel (see plan_attn)
+    int attn_rowblocks = 0;    // 0: planner's choice
+    int attn_posgroups = 0;    // 0: planner's choice
+    int attn_occupancy = 0;    // 0: planner's choice
+    int attn_q4_pipelined = 0; // 1: 4-bit head-dim-256 caches on the pipelined bf16-staging kernel
+    int argmax_chunk = 16384;
+};
+
+// sv_tuning -> Tuning; false for a value out of range
+bool read_tuning(const sv_tuning *t, Tuning &out) {
+    out = Tuning{};
+    if (t == nullptr) return true;
+    if (t->attn_target_wgs < 0 || t->attn_rowblocks < 0) return false;
+    if (t->attn_posgroups != 0 && t->attn_posgroups != 1 && t->attn_posgroups != 2 && t->attn_posgroups != 4)
+        return false;
+    if (t->attn_occupancy < 0 || t->attn_occupancy > 2) return false;
+    if (t->attn_q4_kernel < 0 || t->attn_q4_kernel > 2) return false;
+    if (t->argmax_chunk < 0 || t->argmax_chunk % 8 != 0) return false;
+    out.attn_target_wgs = t->attn_target_wgs;
+    out.attn_rowblocks = t->attn_rowblocks;
+    out.attn_posgroups = t->attn_posgroups;
+    out.attn_occupancy = t->attn_occupancy;
+    out.attn_q4_pipelined = t->attn_q4_kernel == 2;
+    if (t->argmax_chunk > 0) out.argmax_chunk = t->argmax_chunk;
+    return true;
 }
+
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t m) { return ceil_div(a, m) * m; }
@@ -96,7 +115,7 @@ struct AttnPlan {
 //                                     other 4-bit KV -> register-staged kernel
 //   otherwise                         vector-ALU kernel
 AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int Hkv, int max_ctx,
-                   int page_size, int window) {
+                   int page_size, int window, const Tuning &tu) {
     AttnPlan pl{};
     const int G = Hq / Hkv;
     const int R = G * N;
@@ -107,8 +126,8 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
     // head dim 256; other 4-bit caches go to the register-staged kernel
     const bool q4 = kv_dtype == SV_Q4;
     pl.kind = !mfma ? kValu : ((kv_dtype == SV_BF16 || (q4 && D == 256)) ? kMfmaDma : kMfmaStaged);
-    if (pl.kind == kMfmaDma && q4 && g_attn_q4_kernel == 0) pl.kind = kQ4Coop;
-    int target = g_attn_target_wgs > 0 ? g_attn_target_wgs : ((pl.kind == kMfmaDma || pl.kind == kQ4Coop) ? 256 : 512);
+    if (pl.kind == kMfmaDma && q4 && !tu.attn_q4_pipelined) pl.kind = kQ4Coop;
+    int target = tu.attn_target_wgs > 0 ? tu.attn_target_wgs : ((pl.kind == kMfmaDma || pl.kind == kQ4Coop) ? 256 : 512);
     pl.occ = 1;
     const double pos_bytes = kv_dtype == SV_F32 ? D * 8.0 : (kv_dtype == SV_BF16 ? D * 4.0 : D * 1.125);
     // the pipelined kernel keeps a split's page ids in LDS
@@ -140,14 +159,14 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
     // 24/4 heads, dim 256, 8-row chain at 1K-4K keys -2 to -4 %; at 8K-32K
     // within the spread, at 128K +3.5 %).
     auto occupancy2 = [&](bool single_pair, bool single_short) {
-        const bool planned = g_attn_occupancy == 0 && (B > 1 || single_pair || single_short);
-        if (!(planned || g_attn_occupancy == 2) || pl.kind != kMfmaDma || q4 || pl.nt != 1) return;
+        const bool planned = tu.attn_occupancy == 0 && (B > 1 || single_pair || single_short);
+        if (!(planned || tu.attn_occupancy == 2) || pl.kind != kMfmaDma || q4 || pl.nt != 1) return;
         pl.occ = 2;
         pl.pg = std::min(pl.pg, std::max(1, std::min(2, 32768 / (128 * D))));
         // a batch and the regrouped blocks fill two workgroups per CU; a short
         // single sequence keeps the one-per-CU grid
         const bool keep_grid = planned && B == 1 && !single_pair;
-        if (g_attn_target_wgs == 0 && !keep_grid) target = 512;
+        if (tu.attn_target_wgs == 0 && !keep_grid) target = 512;
     };
 
     // Pipelined bf16 kernel, one sequence (static splits): a split of 4.25
@@ -174,8 +193,8 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
         pl.pg = 1;
         pl.rows_per_block = 32 * nts;
         pl.n_rowblocks = (RT + 2 * nts - 1) / (2 * nts);
-        if (g_attn_rowblocks > 0) {
-            pl.n_rowblocks = std::max(pl.n_rowblocks, std::min(g_attn_rowblocks, (RT + 1) / 2));
+        if (tu.attn_rowblocks > 0) {
+            pl.n_rowblocks = std::max(pl.n_rowblocks, std::min(tu.attn_rowblocks, (RT + 1) / 2));
             const int per = (RT + pl.n_rowblocks - 1) / pl.n_rowblocks;     // tiles per block
             pl.nt = (per + 1) / 2;
             pl.rows_per_block = 32 * pl.nt;
@@ -190,8 +209,8 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
         if (RT == 1) {
             pl.pg = pl.kind == kMfmaDma ? (q4 ? 1 : std::min(4, 65536 / (128 * D)))
                                         : std::min(4, (kMfmaTileElems / D) / 32);
-            if (g_attn_posgroups > 0 && pl.kind == kMfmaDma && !q4)
-                pl.pg = std::min(g_attn_posgroups, std::min(4, 65536 / (128 * D)));
+            if (tu.attn_posgroups > 0 && pl.kind == kMfmaDma && !q4)
+                pl.pg = std::min(tu.attn_posgroups, std::min(4, 65536 / (128 * D)));
             pl.nt = 1;
             pl.rows_per_block = 16;
             pl.n_rowblocks = 1;
@@ -201,7 +220,7 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
         } else {
             pl.pg = 1;
             int nrb = (RT + max_tiles - 1) / max_tiles;
-            if (g_attn_rowblocks > 0) nrb = std::max(nrb, std::min(g_attn_rowblocks, RT));
+            if (tu.attn_rowblocks > 0) nrb = std::max(nrb, std::min(tu.attn_rowblocks, RT));
             // One sequence with more row tiles than wavefronts, 4K-64K keys:
             // blocks of <= 4 tiles (one per wavefront) at two workgroups
             // per CU, so each SIMD runs two wavefronts whose matrix and vector
@@ -213,7 +232,7 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
             // and below 4K too (2K: 18.6 -> 22.7 us), where the splits are few
             // positions long and the extra row blocks only add prologues.
             const bool single_pair = pl.kind == kMfmaDma && !q4 && B == 1 && RT > 4 && L > 4096 && L <= 65536 &&
-                                     g_attn_rowblocks == 0 && g_attn_occupancy != 1;
+                                     tu.attn_rowblocks == 0 && tu.attn_occupancy != 1;
             if (single_pair) nrb = (RT + 3) / 4;
             // More row blocks (each reads the same KV tiles, from L2 after the
             // first) shorten the per-split work but multiply the splits, whose
@@ -222,7 +241,7 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
             // (whose per-stage cost grows with the tiles per wave), 15% on the
             // register-staged one (measured on the workloads of the bench).
             const double max_part = pl.kind == kMfmaDma ? 0.35 : 0.15;
-            for (; g_attn_rowblocks == 0 && !single_pair;) {
+            for (; tu.attn_rowblocks == 0 && !single_pair;) {
                 const int tpb = (RT + nrb - 1) / nrb;
                 splits_for(B * Hkv * nrb, pl.split_len, pl.n_splits);
                 const double part = (double)pl.n_splits * R * (D + 2) * 4.0;
@@ -236,9 +255,9 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
             pl.nt = (tpb + 3) / 4;
             // a block of one or two row tiles leaves wavefronts without rows:
             // they take other positions of a longer stage instead (bf16 cache)
-            if (pl.kind == kMfmaDma && !q4 && pl.nt == 1 && g_attn_posgroups > 0) {
+            if (pl.kind == kMfmaDma && !q4 && pl.nt == 1 && tu.attn_posgroups > 0) {
                 const int pg_rows = tpb == 1 ? 4 : (tpb == 2 ? 2 : 1);
-                pl.pg = std::min(std::min(g_attn_posgroups, pg_rows), std::min(4, 65536 / (128 * D)));
+                pl.pg = std::min(std::min(tu.attn_posgroups, pg_rows), std::min(4, 65536 / (128 * D)));
             }
             occupancy2(single_pair, B == 1 && L <= 6144);
             splits_for(B * Hkv * pl.n_rowblocks, pl.split_len, pl.n_splits);
@@ -290,6 +309,11 @@ int check_attn_shape(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_head
 }  // namespace
 }  // namespace sv
 
+int sv::hip_fail(hipError_t e) {
+    g_last_hip_error = (int)e;
+    return SV_EHIP;
+}
+
 using namespace sv;
 
 extern "C" {
@@ -307,60 +331,29 @@ const char *sv_error_string(int code) {
 
 int sv_last_hip_error(void) { return g_last_hip_error; }
 
-int sv_set_option(int option, int value) {
-    int prev;
-    switch (option) {
-        case SV_OPT_ATTN_TARGET_WGS:
-            if (value < 0) return SV_EINVAL;
-            prev = g_attn_target_wgs;
-            g_attn_target_wgs = value;
-            return prev;
-        case SV_OPT_ATTN_ROWBLOCKS:
-            if (value < 0) return SV_EINVAL;
-            prev = g_attn_rowblocks;
-            g_attn_rowblocks = value;
-            return prev;
-        case SV_OPT_ATTN_POSGROUPS:
-            if (value != 0 && value != 1 && value != 2 && value != 4) return SV_EINVAL;
-            prev = g_attn_posgroups;
-            g_attn_posgroups = value;
-            return prev;
-        case SV_OPT_ATTN_OCCUPANCY:
-            if (value < 0 || value > 2) return SV_EINVAL;
-            prev = g_attn_occupancy;
-            g_attn_occupancy = value;
-            return prev;
-        case SV_OPT_ATTN_Q4_KERNEL:
-            if (value < 0 || value > 1) return SV_EINVAL;
-            prev = g_attn_q4_kernel;
-            g_attn_q4_kernel = value;
-            return prev;
-        case SV_OPT_ARGMAX_CHUNK:
-            if (value <= 0 || value % 8 != 0) return SV_EINVAL;
-            prev = g_argmax_chunk;
-            g_argmax_chunk = value;
-            return prev;
-    }
-    return SV_EINVAL;
-}
-
 }  // extern "C"
 
 namespace {
 
-size_t attn_workspace_size(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads, int max_ctx, int window) {
+size_t attn_workspace_size(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads, int max_ctx, int window,
+                           const sv_tuning *tuning) {
+    Tuning tu;
+    if (!read_tuning(tuning, tu)) return 0;
     if (check_attn_shape(kv, batch, n_nodes, n_q_heads, max_ctx) != SV_OK) return 0;
     if (window < 0 || (window > 0 && window < n_nodes)) return 0;
     const AttnPlan pl = plan_attn(kv->dtype, SV_BF16, kv->head_dim, batch, n_nodes, n_q_heads,
-                                  kv->n_kv_heads, max_ctx, kv->page_size, window);
+                                  kv->n_kv_heads, max_ctx, kv->page_size, window, tu);
     const AttnPlan pf = plan_attn(kv->dtype, SV_F32, kv->head_dim, batch, n_nodes, n_q_heads,
-                                  kv->n_kv_heads, max_ctx, kv->page_size, window);
+                                  kv->n_kv_heads, max_ctx, kv->page_size, window, tu);
     return std::max(pl.ws_bytes, pf.ws_bytes);
 }
 
 int verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads, const int32_t *ctx_lens, int max_ctx,
-                const void *q, int q_dtype, const int32_t *parent, float sm_scale, int window, void *out, float *lse,
-                void *workspace, size_t workspace_bytes, void *stream) {
+                const void *q, int q_dtype, const int32_t *parent, float sm_scale, int window,
+                const sv_tuning *tuning, void *out, float *lse, void *workspace, size_t workspace_bytes,
+                void *stream) {
+    Tuning tu;
+    if (!read_tuning(tuning, tu)) return SV_EINVAL;
     int rc = check_attn_shape(kv, batch, n_nodes, n_q_heads, max_ctx);
     if (rc != SV_OK) return rc;
     if (window < 0 || (window > 0 && window < n_nodes)) return SV_EINVAL;
@@ -371,7 +364,7 @@ int verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads, co
     if (q_dtype == SV_BF16 && kv->dtype == SV_F32) return SV_EUNSUPPORTED;
     const int D = kv->head_dim;
     const AttnPlan pl = plan_attn(kv->dtype, q_dtype, D, batch, n_nodes, n_q_heads, kv->n_kv_heads, max_ctx,
-                                  kv->page_size, window);
+                                  kv->page_size, window, tu);
     if (pl.dyn ? (batch > kSchedMaxBatch || pl.split_max < 0) : pl.n_splits > kMaxSplits)
         return SV_EUNSUPPORTED;
     if (workspace == nullptr || workspace_bytes < pl.ws_bytes) return SV_EWORKSPACE;
@@ -412,6 +405,7 @@ int verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads, co
     // write back from L2 when the split kernel ends, which the merge waits for.
     // Large ones stay cached for the merge (measured: 6 MB -1 us, 34 MB +3 us).
     p.part_nt = pl.ml_off <= ((size_t)8 << 20);
+    p.err = device_error_word();
 
     hipStream_t st = (hipStream_t)stream;
     hipError_t e;
@@ -431,7 +425,7 @@ extern "C" {
 
 size_t sv_verify_attn_workspace_size(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
                                      int max_ctx) {
-    return attn_workspace_size(kv, batch, n_nodes, n_q_heads, max_ctx, 0);
+    return attn_workspace_size(kv, batch, n_nodes, n_q_heads, max_ctx, 0, nullptr);
 }
 
 int sv_verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
@@ -439,13 +433,13 @@ int sv_verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
                    const void *q, int q_dtype, const int32_t *parent, float sm_scale,
                    void *out, float *lse,
                    void *workspace, size_t workspace_bytes, void *stream) {
-    return verify_attn(kv, batch, n_nodes, n_q_heads, ctx_lens, max_ctx, q, q_dtype, parent, sm_scale, 0, out, lse,
-                       workspace, workspace_bytes, stream);
+    return verify_attn(kv, batch, n_nodes, n_q_heads, ctx_lens, max_ctx, q, q_dtype, parent, sm_scale, 0, nullptr,
+                       out, lse, workspace, workspace_bytes, stream);
 }
 
 size_t sv_verify_attn_window_workspace_size(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
                                             int max_ctx, int window) {
-    return attn_workspace_size(kv, batch, n_nodes, n_q_heads, max_ctx, window);
+    return attn_workspace_size(kv, batch, n_nodes, n_q_heads, max_ctx, window, nullptr);
 }
 
 int sv_verify_attn_window(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
@@ -453,8 +447,22 @@ int sv_verify_attn_window(const sv_kv_cache *kv, int batch, int n_nodes, int n_q
                           const void *q, int q_dtype, const int32_t *parent, float sm_scale, int window,
                           void *out, float *lse,
                           void *workspace, size_t workspace_bytes, void *stream) {
-    return verify_attn(kv, batch, n_nodes, n_q_heads, ctx_lens, max_ctx, q, q_dtype, parent, sm_scale, window, out,
-                       lse, workspace, workspace_bytes, stream);
+    return verify_attn(kv, batch, n_nodes, n_q_heads, ctx_lens, max_ctx, q, q_dtype, parent, sm_scale, window,
+                       nullptr, out, lse, workspace, workspace_bytes, stream);
+}
+
+size_t sv_verify_attn_tuned_workspace_size(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
+                                           int max_ctx, int window, const sv_tuning *tuning) {
+    return attn_workspace_size(kv, batch, n_nodes, n_q_heads, max_ctx, window, tuning);
+}
+
+int sv_verify_attn_tuned(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
+                         const int32_t *ctx_lens, int max_ctx,
+                         const void *q, int q_dtype, const int32_t *parent, float sm_scale, int window,
+                         const sv_tuning *tuning, void *out, float *lse,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+    return verify_attn(kv, batch, n_nodes, n_q_heads, ctx_lens, max_ctx, q, q_dtype, parent, sm_scale, window,
+                       tuning, out, lse, workspace, workspace_bytes, stream);
 }
 
 size_t sv_greedy_accept_workspace_size(int batch, int n_nodes, int vocab) {
@@ -470,13 +478,16 @@ namespace {
 // argument checks and parameters of an acceptance launch
 int accept_params(int batch, int n_nodes, int vocab, const void *logits, int logits_dtype,
                   const int32_t *draft_ids, const int32_t *parent, int32_t *accept_len, int32_t *path,
-                  int32_t *tokens, int32_t *argmax, void *workspace, size_t workspace_bytes, AcceptParams &p) {
+                  int32_t *tokens, int32_t *argmax, void *workspace, size_t workspace_bytes, AcceptParams &p,
+                  const sv_tuning *tuning = nullptr) {
+    Tuning tu;
+    if (!read_tuning(tuning, tu)) return SV_EINVAL;
     if (batch < 1 || n_nodes < 1 || n_nodes > 64 || vocab < 1) return SV_EINVAL;
     if (logits == nullptr || draft_ids == nullptr || parent == nullptr || accept_len == nullptr ||
         path == nullptr || tokens == nullptr)
         return SV_EINVAL;
     if (logits_dtype != SV_F32 && logits_dtype != SV_BF16) return SV_EINVAL;
-    const int64_t chunks = ceil_div(vocab, g_argmax_chunk);
+    const int64_t chunks = ceil_div(vocab, tu.argmax_chunk);
     if ((int64_t)batch * n_nodes * chunks > (int64_t)INT32_MAX) return SV_EUNSUPPORTED;
     const size_t need = sv_greedy_accept_workspace_size(batch, n_nodes, vocab);
     if (workspace == nullptr || workspace_bytes < need) return SV_EWORKSPACE;
@@ -495,7 +506,8 @@ int accept_params(int batch, int n_nodes, int vocab, const void *logits, int log
     p.B = batch;
     p.N = n_nodes;
     p.V = vocab;
-    p.chunk = g_argmax_chunk;
+    p.chunk = tu.argmax_chunk;
+    p.err = device_error_word();
     p.n_chunks = (int)chunks;
     p.logits_f32 = logits_dtype == SV_F32;
     return SV_OK;
@@ -531,6 +543,7 @@ int compact_params(const sv_kv_cache *kv, int n_layers, int batch, int n_nodes, 
     p.n_layers = n_layers;
     p.max_ctx = max_ctx;
     p.dtype = kv->dtype;
+    p.err = device_error_word();
     return SV_OK;
 }
 
@@ -546,6 +559,20 @@ int sv_greedy_accept(int batch, int n_nodes, int vocab,
     AcceptParams p;
     const int rc = accept_params(batch, n_nodes, vocab, logits, logits_dtype, draft_ids, parent, accept_len, path,
                                  tokens, argmax, workspace, workspace_bytes, p);
+    if (rc != SV_OK) return rc;
+    const hipError_t e = launch_accept(p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return SV_OK;
+}
+
+int sv_greedy_accept_tuned(int batch, int n_nodes, int vocab,
+                           const void *logits, int logits_dtype,
+                           const int32_t *draft_ids, const int32_t *parent,
+                           int32_t *accept_len, int32_t *path, int32_t *tokens, int32_t *argmax,
+                           const sv_tuning *tuning, void *workspace, size_t workspace_bytes, void *stream) {
+    AcceptParams p;
+    const int rc = accept_params(batch, n_nodes, vocab, logits, logits_dtype, draft_ids, parent, accept_len, path,
+                                 tokens, argmax, workspace, workspace_bytes, p, tuning);
     if (rc != SV_OK) return rc;
     const hipError_t e = launch_accept(p, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);
@@ -584,6 +611,7 @@ int sv_kv_append(const sv_kv_cache *kv, int batch, int n_rows, const int32_t *ct
     p.Hkv = kv->n_kv_heads;
     p.D = kv->head_dim;
     p.max_ctx = max_ctx;
+    p.err = device_error_word();
     const hipError_t e = launch_append(p, src_dtype, kv->dtype, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);
     return SV_OK;

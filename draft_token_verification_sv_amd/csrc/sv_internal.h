@@ -43,6 +43,7 @@ struct AttnParams {
     int q_f32;                    // 1: q/out are fp32, 0: bf16
     int part_nt;                  // 1: streaming (non-temporal) stores for the partial O
     int window;                   // > 0: only the last `window` key rows of each sequence
+    unsigned int *err;            // precondition word (SV_DEBUG builds), else nullptr
 };
 
 struct CompactParams {
@@ -51,6 +52,7 @@ struct CompactParams {
     const int32_t *ctx_lens, *path, *accept_len;
     int32_t *new_lens;
     int B, N, Hkv, D, n_layers, max_ctx, dtype;
+    unsigned int *err;            // precondition word (SV_DEBUG builds), else nullptr
 };
 
 struct AcceptParams {
@@ -67,6 +69,7 @@ struct AcceptParams {
     const float *gumbel;          // [B][N][V] noise: sample at `temperature` instead of the argmax (or null)
     float temperature;
     int top_k;                    // > 0: sample among each row's top_k logits (launch_topk_accept)
+    unsigned int *err;            // precondition word (SV_DEBUG builds), else nullptr
 };
 
 struct AppendParams {
@@ -74,6 +77,7 @@ struct AppendParams {
     const int32_t *ctx_lens;      // [B]
     const void *k_new, *v_new;    // [B][n][Hkv][D], fp32 or bf16
     int B, n, Hkv, D, max_ctx;
+    unsigned int *err;            // precondition word (SV_DEBUG builds), else nullptr
 };
 
 struct ConvTreeParams {
@@ -114,6 +118,13 @@ struct CommitParams {
 constexpr int kMfmaTileElems = 16384;          // T * D bf16 elements per K (or V) tile
 constexpr int kValuTileElems = 8192;           // T * D fp32 elements per K (or V) tile
 constexpr int kMaxSplits = 1024;               // splits per (sequence, KV head, row block)
+
+// Records e as the calling thread's last HIP error; returns SV_EHIP.
+int hip_fail(hipError_t e);
+
+// The current device's precondition word (sv_check_device_errors): its
+// device address in a build with SV_DEBUG, nullptr otherwise.
+unsigned int *device_error_word();
 
 // launchers (return the hipError_t of the launch) -------------------------
 hipError_t launch_attn_mfma(const AttnParams &p, int dtype, int D, int nt, int pg, hipStream_t s);

@@ -387,36 +387,79 @@ const char *sv_error_string(int code);
 int sv_last_hip_error(void);
 
 /*
- * Launch tuning (for benchmarks and sweeps; the defaults need no setting).
- *   SV_OPT_ATTN_TARGET_WGS  workgroups the attention launch aims for; 0 (the
- *                           default) = 256 on the pipelined bf16 path, 512 on
- *                           the others
- *   SV_OPT_ARGMAX_CHUNK     logits elements per argmax workgroup, a positive
- *                           multiple of 8 (default 16384)
- *   SV_OPT_ATTN_ROWBLOCKS   packed-row blocks per (sequence, KV head) on the
- *                           matrix-core paths; 0 (default) = planner's choice
- *   SV_OPT_ATTN_POSGROUPS   waves sharing one 16-row tile on the pipelined bf16
- *                           path (1, 2 or 4; each takes 32 positions of a
- *                           stage); 0 (default) = planner's choice
- *   SV_OPT_ATTN_OCCUPANCY   workgroups per CU on the pipelined bf16 path for
- *                           one row tile per wave (1 or 2: half-size LDS
- *                           rings, twice the work units); 0 (default) =
- *                           planner's choice
- *   SV_OPT_ATTN_Q4_KERNEL   4-bit caches of head dim 256: 0 (default) the
- *                           cooperative fp16 matrix-core kernel, 1 the
- *                           pipelined kernel with bf16 staging
- * Returns the previous value, or SV_EINVAL for an unknown option or a value
- * out of range.  A workspace sized under one setting may be too small under
- * another (the call then returns SV_EWORKSPACE).
- * Process-wide; not synchronised with calls in flight on other threads.
+ * Per-call launch tuning (benchmarks and sweeps; the defaults need none).
+ * Passed by pointer to the *_tuned calls below; NULL, or a zero field, keeps
+ * the library's choice.  The library keeps no tuning state between calls.
+ *   attn_target_wgs  workgroups the attention launch aims for (>= 0); default
+ *                    256 on the pipelined and cooperative kernels, 512 on the
+ *                    others
+ *   attn_rowblocks   packed-row blocks per (sequence, KV head) on the
+ *                    matrix-core kernels (>= 0)
+ *   attn_posgroups   waves sharing one 16-row tile on the pipelined bf16
+ *                    kernel: 1, 2 or 4 (each takes 32 positions of a stage)
+ *   attn_occupancy   workgroups per CU on the pipelined bf16 kernel for one
+ *                    row tile per wave: 1 or 2 (half-size LDS rings, twice the
+ *                    work units)
+ *   attn_q4_kernel   4-bit caches of head dim 256 with >= 16 packed rows:
+ *                    1 the cooperative fp16 matrix-core kernel (the default),
+ *                    2 the pipelined kernel with bf16 staging
+ *   argmax_chunk     logits per argmax workgroup, a positive multiple of 8
+ *                    (default 16384)
+ * A value out of range makes the call return SV_EINVAL (the workspace-size
+ * query returns 0).  A workspace sized under one tuning may be too small
+ * under another (the call then returns SV_EWORKSPACE).
  */
-#define SV_OPT_ATTN_TARGET_WGS 1
-#define SV_OPT_ARGMAX_CHUNK    2
-#define SV_OPT_ATTN_ROWBLOCKS  3
-#define SV_OPT_ATTN_POSGROUPS  4
-#define SV_OPT_ATTN_OCCUPANCY  5
-#define SV_OPT_ATTN_Q4_KERNEL  6
-int sv_set_option(int option, int value);
+typedef struct sv_tuning {
+    int32_t attn_target_wgs;
+    int32_t attn_rowblocks;
+    int32_t attn_posgroups;
+    int32_t attn_occupancy;
+    int32_t attn_q4_kernel;
+    int32_t argmax_chunk;
+} sv_tuning;
+
+/* sv_verify_attn_window with a tuning (window 0 = the whole key range). */
+size_t sv_verify_attn_tuned_workspace_size(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
+                                           int max_ctx, int window, const sv_tuning *tuning);
+int sv_verify_attn_tuned(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
+                         const int32_t *ctx_lens, int max_ctx,
+                         const void *q, int q_dtype, const int32_t *parent, float sm_scale, int window,
+                         const sv_tuning *tuning, void *out, float *lse,
+                         void *workspace, size_t workspace_bytes, void *stream);
+/* sv_greedy_accept with a tuning (argmax_chunk). */
+int sv_greedy_accept_tuned(int batch, int n_nodes, int vocab,
+                           const void *logits, int logits_dtype,
+                           const int32_t *draft_ids, const int32_t *parent,
+                           int32_t *accept_len, int32_t *path, int32_t *tokens, int32_t *argmax,
+                           const sv_tuning *tuning, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sv_check_device_errors -- the device-side precondition word.
+ *
+ * The calls above treat broken device-side inputs as documented (a parent
+ * that is not an earlier node ends the node's path; a page id outside the
+ * pool reads as zero rows; ctx_lens are clamped to [0, max_ctx]; out-of-range
+ * path / accept_len entries skip rows) and say nothing.  A library built with
+ * SV_DEBUG (libsv_debug.so) also records each such input when a kernel meets
+ * it, with an atomic OR into a word in device memory (one word per GPU):
+ *   SV_DEVERR_PARENT  parent[b][i] outside [0, i) for some i >= 1
+ *                     (attention, acceptance);
+ *   SV_DEVERR_PAGE    a page id outside [0, capacity) for a position the call
+ *                     reads or writes (attention, compaction, append);
+ *   SV_DEVERR_CTX     ctx_lens[b] < 0 or > max_ctx (attention, compaction,
+ *                     append);
+ *   SV_DEVERR_PATH    accept_len[b] outside [0, N-1] or path[b][j] outside
+ *                     [j, N-1] for j <= accept_len[b] (compaction).
+ * This call waits for `stream` (the one exception to "never synchronises"),
+ * returns the bits recorded on the current device since the previous call,
+ * and clears them.  A release build records nothing and returns 0 without
+ * touching the device.  Negative return: SV_EHIP.
+ */
+#define SV_DEVERR_PARENT 1
+#define SV_DEVERR_PAGE   2
+#define SV_DEVERR_CTX    4
+#define SV_DEVERR_PATH   8
+int sv_check_device_errors(void *stream);
 
 #ifdef __cplusplus
 }

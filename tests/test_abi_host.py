@@ -225,14 +225,75 @@ def test_recurrent_checks(lib):
     assert commit(path=0) == -1 and commit(Dk=32) == -1
 
 
-def test_options(lib):
-    prev = lib.sv_set_option(1, 300)
-    assert prev == 0
-    assert lib.sv_set_option(1, 0) == 300
-    assert lib.sv_set_option(2, 12) == -1                   # not a multiple of 8
-    assert lib.sv_set_option(2, 4096) == 16384
-    assert lib.sv_set_option(2, 16384) == 4096
-    assert lib.sv_set_option(4, 3) == -1                   # position groups: 1, 2 or 4
-    assert lib.sv_set_option(4, 2) == 0
-    assert lib.sv_set_option(4, 0) == 2
-    assert lib.sv_set_option(9, 1) == -1
+class Tuning(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("attn_target_wgs", "attn_rowblocks", "attn_posgroups",
+                                              "attn_occupancy", "attn_q4_kernel", "argmax_chunk")]
+
+
+def test_tuning_per_call(lib):
+    """Tuning travels with the call: out-of-range fields are rejected before
+    anything is launched, a null or all-zero tuning is the default plan, and
+    nothing persists from one call to the next."""
+    lib.sv_verify_attn_tuned_workspace_size.restype = ctypes.c_size_t
+    d = kv()
+    base = lib.sv_verify_attn_workspace_size(ctypes.byref(d), 1, 8, 24, 4096)
+    assert base > 0
+
+    def ws(**f):
+        t = Tuning(**f)
+        return lib.sv_verify_attn_tuned_workspace_size(ctypes.byref(d), 1, 8, 24, 4096, 0, ctypes.byref(t))
+    assert lib.sv_verify_attn_tuned_workspace_size(ctypes.byref(d), 1, 8, 24, 4096, 0, None) == base
+    assert ws() == base
+    assert ws(attn_posgroups=3) == 0 and ws(attn_occupancy=3) == 0 and ws(attn_q4_kernel=3) == 0
+    assert ws(attn_target_wgs=-1) == 0 and ws(attn_rowblocks=-2) == 0 and ws(argmax_chunk=12) == 0
+    more = ws(attn_target_wgs=4096)                 # more splits, more partials
+    assert more > base
+    assert lib.sv_verify_attn_workspace_size(ctypes.byref(d), 1, 8, 24, 4096) == base   # no state kept
+
+    P = ctypes.c_void_p(FAKE)
+    bad = Tuning(attn_posgroups=3)
+    rc = lib.sv_verify_attn_tuned(ctypes.byref(d), 1, 8, 24, P, 4096, P, 1, P, ctypes.c_float(0.0), 0,
+                                  ctypes.byref(bad), P, None, P, ctypes.c_size_t(1 << 30), None)
+    assert rc == -1
+    small = Tuning(attn_target_wgs=4096)          # needs more than the default workspace
+    rc = lib.sv_verify_attn_tuned(ctypes.byref(d), 1, 8, 24, P, 4096, P, 1, P, ctypes.c_float(0.0), 0,
+                                  ctypes.byref(small), P, None, P, ctypes.c_size_t(base), None)
+    assert rc == -3
+    chunk = Tuning(argmax_chunk=12)
+    rc = lib.sv_greedy_accept_tuned(1, 8, 151936, P, 1, P, P, P, P, P, None, ctypes.byref(chunk), P,
+                                    ctypes.c_size_t(1 << 20), None)
+    assert rc == -1
+    rc = lib.sv_greedy_accept_tuned(0, 8, 151936, P, 1, P, P, P, P, P, None, None, P, ctypes.c_size_t(1 << 20),
+                                    None)
+    assert rc == -1
+
+
+def _debug_lib():
+    path = os.path.join(ROOT, "draft_token_verification_sv_amd", "libsv_debug.so")
+    if not os.path.exists(path):
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "sv_build", os.path.join(ROOT, "draft_token_verification_sv_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build(debug=True)
+    return ctypes.CDLL(path)
+
+
+def test_check_device_errors_host_side(lib):
+    """sv_check_device_errors: the release library records nothing and returns
+    0 without touching a device; the SV_DEBUG library exports the same entry
+    points and, with no GPU to read the word from, reports SV_EHIP (the HIP
+    error kept for sv_last_hip_error)."""
+    assert lib.sv_check_device_errors(None) == 0
+    dbg = _debug_lib()
+    with open(HEADER) as f:
+        names = set(re.findall(r"\b(sv_[a-z_]+)\s*\(", f.read()))
+    for n in sorted(names):
+        assert hasattr(dbg, n), n
+    import torch
+    if torch.cuda.is_available():
+        assert dbg.sv_check_device_errors(None) >= 0
+    else:
+        assert dbg.sv_check_device_errors(None) == -4
+        assert dbg.sv_last_hip_error() != 0

@@ -65,3 +65,20 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
     assert r.stdout == ""
+
+
+def test_attention_flops_and_binding_roof():
+    # Q K^T and P V: 2 + 2 flops per (row, key, head-dim) element, rows =
+    # 6 query heads x 16 nodes per KV head, 4 KV heads, 131088 keys
+    cfg = workloads.CONFIGS["C4"]
+    flops = bench.attn_algorithmic_flops(cfg, np.array([131072]))
+    assert flops == 4 * (6 * 16) * 4 * 131088 * 256 == 51_545_899_008
+    # at peak the matrix cores need longer than HBM needs for the bytes:
+    # the 4-bit block is matrix-bound, the 4K bf16 chain HBM-bound
+    t_mfma = flops / (bench.MFMA_PEAK_TFLOPS * 1e12)
+    t_hbm = bench.attn_algorithmic_bytes(cfg, np.array([131072])) / (bench.HBM_PEAK_GBPS * 1e9)
+    assert t_mfma > t_hbm and bench.uses_matrix_cores(cfg)
+    c2 = workloads.CONFIGS["C2"]
+    assert (bench.attn_algorithmic_flops(c2, np.array([4096])) / (bench.MFMA_PEAK_TFLOPS * 1e12)
+            < bench.attn_algorithmic_bytes(c2, np.array([4096])) / (bench.HBM_PEAK_GBPS * 1e9))
+    assert not bench.uses_matrix_cores(workloads.CONFIGS["C1"])          # fp32, 2 rows: vector ALU

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import workloads
-from sv_harness import DeviceCase, check_attention, oracle_accept, say
+from sv_harness import DeviceCase, check_attention, oracle_accept, q4_key_rounding, say
 
 pytestmark = pytest.mark.gpu
 
@@ -96,12 +96,8 @@ def test_attention_split_count_independent(sv, target):
     cfg = _small("C3", ctx=900)
     case = workloads.make_case(cfg, seed=3, variant="peaked")
     dc = DeviceCase(case)
-    prev = sv.set_option(sv.SV_OPT_ATTN_TARGET_WGS, target)
-    try:
-        out, lse = dc.attn()
-        torch.cuda.synchronize()
-    finally:
-        sv.set_option(sv.SV_OPT_ATTN_TARGET_WGS, prev)
+    out, lse = dc.attn(tuning={"attn_target_wgs": target})
+    torch.cuda.synchronize()
     check_attention(case, out, lse)
 
 
@@ -134,12 +130,8 @@ def test_attention_batch_schedule(sv, path, target):
     say(f"[attn-batch] {path[0]} target_wgs={target}")
     case = _skewed_case(path)
     dc = DeviceCase(case)
-    prev = sv.set_option(sv.SV_OPT_ATTN_TARGET_WGS, target)
-    try:
-        out, lse = dc.attn()
-        torch.cuda.synchronize()
-    finally:
-        sv.set_option(sv.SV_OPT_ATTN_TARGET_WGS, prev)
+    out, lse = dc.attn(tuning={"attn_target_wgs": target})
+    torch.cuda.synchronize()
     ma, rel, le = check_attention(case, out, lse)
     say(f"    max_abs={ma:.3g} rel={rel:.3g} lse={le:.3g}")
 
@@ -149,12 +141,8 @@ def test_attention_position_groups(sv, pg):
     say(f"[attn-pg] posgroups={pg}")
     case = _skewed_case(BATCH_PATHS[0], seed=12)
     dc = DeviceCase(case)
-    prev = sv.set_option(sv.SV_OPT_ATTN_POSGROUPS, pg)
-    try:
-        out, lse = dc.attn()
-        torch.cuda.synchronize()
-    finally:
-        sv.set_option(sv.SV_OPT_ATTN_POSGROUPS, prev)
+    out, lse = dc.attn(tuning={"attn_posgroups": pg})
+    torch.cuda.synchronize()
     check_attention(case, out, lse)
 
 
@@ -187,14 +175,8 @@ def test_attention_two_per_cu(sv, label, target):
     cfg, kw = [(c, k) for (l, c, k) in ATTN_CASES if l == label][0]
     say(f"[attn occ2] {label} target={target}")
     case = workloads.make_case(cfg, seed=5, **kw)
-    prev = sv.set_option(sv.SV_OPT_ATTN_OCCUPANCY, 2)
-    prev_t = sv.set_option(sv.SV_OPT_ATTN_TARGET_WGS, target)
-    try:
-        out, lse = DeviceCase(case).attn()
-        torch.cuda.synchronize()
-    finally:
-        sv.set_option(sv.SV_OPT_ATTN_OCCUPANCY, prev)
-        sv.set_option(sv.SV_OPT_ATTN_TARGET_WGS, prev_t)
+    out, lse = DeviceCase(case).attn(tuning={"attn_occupancy": 2, "attn_target_wgs": target})
+    torch.cuda.synchronize()
     check_attention(case, out, lse)
 
 
@@ -238,6 +220,32 @@ def test_attention_q4_single_sequence(sv, case_):
     out, lse = DeviceCase(case).attn(window=window)
     torch.cuda.synchronize()
     check_attention(case, out, lse, ref=oracle.verify_attention(case, window=window))
+
+
+Q4_KERNEL_CASES = [
+    # (label, config, make_case kwargs, window): 4-bit caches of head dim 256
+    ("C4 q4 ctx700", _small("C4", ctx=700), {}, 0),
+    ("C4 q4 ctx130 peaked", _small("C4", ctx=130), {"variant": "peaked"}, 0),
+    ("C4 q4 ctx2100 peaked windowed", _small("C4", ctx=2100), {"variant": "peaked"}, 900),
+    ("R=16 q4 chain", workloads.Config("r16", 2, 8, 2, 256, 4, "bf16", "q4", "f32", 50, 129, ctx_hi=166,
+                                       q_std=0.5, kv_std=0.5), {"variant": "peaked"}, 0),
+    ("q4 paged tree 9 tiles", workloads.Config("pt9", 1, 24, 4, 256, 22, "bf16", "q4", "f32", 50, 900,
+                                               tree="ddtree", paged=True, q_std=0.5, kv_std=0.5,
+                                               draft_rule="tree"), {}, 0),
+]
+
+
+@pytest.mark.parametrize("kernel", ["cooperative", "pipelined"])
+@pytest.mark.parametrize("label,cfg,kw,window", Q4_KERNEL_CASES, ids=[c[0] for c in Q4_KERNEL_CASES])
+def test_attention_q4_kernels(sv, label, cfg, kw, window, kernel):
+    """Both kernels for 4-bit caches of head dim 256 (the cooperative fp16 one,
+    the default, and the pipelined bf16-staging one, chosen per call)."""
+    say(f"[attn q4 kernel] {label} {kernel}")
+    case = workloads.make_case(cfg, seed=77, capacity_pad=2, **kw)
+    out, lse = DeviceCase(case).attn(window=window, tuning={"attn_q4_kernel": kernel})
+    torch.cuda.synchronize()
+    ref = oracle.verify_attention(case, window=window)
+    check_attention(case, out, lse, ref=ref, key_rounding=q4_key_rounding(case, kernel))
 
 
 @pytest.mark.parametrize("edge", PLAN_EDGES, ids=[e[0] for e in PLAN_EDGES])
@@ -370,19 +378,15 @@ def test_accept_repeated_calls_and_chunk_sizes(sv):
                                       (8, _small("C2", ctx=8, vocab=1000)),
                                       (1024, _small("C5", ctx=8, ctx_hi=9, vocab=151936)),
                                       (65536, _small("C3", ctx=8, vocab=70000))]):
-        prev = sv.set_option(sv.SV_OPT_ARGMAX_CHUNK, chunk)
-        try:
-            for rep in range(3):
-                case = workloads.make_case(cfg, seed=300 + 10 * k + rep)
-                dc = DeviceCase(case)
-                acc, path, tok, am = dc.accept(workspace=None)
-                torch.cuda.synchronize()
-                r_am, r_acc, r_path, r_tok = oracle_accept(case)
-                np.testing.assert_array_equal(am.cpu().numpy(), r_am)
-                np.testing.assert_array_equal(path.cpu().numpy(), r_path)
-                np.testing.assert_array_equal(tok.cpu().numpy(), r_tok)
-        finally:
-            sv.set_option(sv.SV_OPT_ARGMAX_CHUNK, prev)
+        for rep in range(3):
+            case = workloads.make_case(cfg, seed=300 + 10 * k + rep)
+            dc = DeviceCase(case)
+            acc, path, tok, am = dc.accept(workspace=None, tuning={"argmax_chunk": chunk})
+            torch.cuda.synchronize()
+            r_am, r_acc, r_path, r_tok = oracle_accept(case)
+            np.testing.assert_array_equal(am.cpu().numpy(), r_am)
+            np.testing.assert_array_equal(path.cpu().numpy(), r_path)
+            np.testing.assert_array_equal(tok.cpu().numpy(), r_tok)
 
 
 SAMPLE_CASES = [
