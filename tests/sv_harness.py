@@ -27,6 +27,49 @@ def dev_tensor(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
     raise ValueError(dtype)
 
 
+CANARY_BYTES = 4096
+CANARY_BYTE = 0xA5
+
+
+class Guarded:
+    """A device buffer of `shape` and `dtype` followed by a band of
+    CANARY_BYTES bytes set to CANARY_BYTE; `t` is the buffer (a contiguous
+    view), `check` asserts the band is intact."""
+
+    def __init__(self, shape, dtype, device, zero=False):
+        n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        self.n = n
+        self.raw = torch.empty(n + CANARY_BYTES, dtype=torch.uint8, device=device)
+        if zero:
+            self.raw[:n].zero_()
+        else:
+            self.raw[:n].fill_(0x7F)
+        self.raw[n:].fill_(CANARY_BYTE)
+        self.t = self.raw[:n].view(dtype).view(shape)
+
+    def check(self, name, where=""):
+        torch.cuda.synchronize()
+        band = self.raw[self.n:]
+        bad = int((band != CANARY_BYTE).sum())
+        assert bad == 0, f"{where}: {bad} canary bytes after {name} were overwritten"
+
+
+def sample_accept_guarded(logits, gumbel, T, drafts, parent, **kw):
+    """sample_accept with every output and the zero-filled workspace followed
+    by a canary band; checks the bands and that the workspace is all zeros
+    again, then returns (accept_len, path, tokens, samples)."""
+    import draft_token_verification_sv_amd as sv
+    B, N, V = logits.shape
+    dev = logits.device
+    ws = Guarded((sv.greedy_accept_workspace_size(B, N, V),), torch.uint8, dev, zero=True)
+    outs = [Guarded((B,), torch.int32, dev)] + [Guarded((B, N), torch.int32, dev) for _ in range(3)]
+    res = sv.sample_accept(logits, gumbel, T, drafts, parent, workspace=ws.t, outputs=tuple(o.t for o in outs), **kw)
+    for g, name in zip([ws] + outs, ("workspace", "accept_len", "path", "tokens", "samples")):
+        g.check(name, "sample_accept")
+    assert not bool(ws.t.any()), "acceptance workspace not returned to zero"
+    return res
+
+
 class DeviceCase:
     """Device copies of a case's arrays plus the binding's KVCache view."""
 
@@ -53,12 +96,40 @@ class DeviceCase:
         self.max_ctx = int(case.ctx_lens.max())
 
     def attn(self, **kw):
+        """verify_attn with out, lse and the workspace allocated here, each
+        followed by a canary band that is checked after the call (unless the
+        caller passes its own buffers)."""
         import draft_token_verification_sv_amd as sv
-        return sv.verify_attn(self.kv, self.q, self.ctx, self.parent, self.max_ctx, **kw)
+        if any(k in kw for k in ("out", "lse", "workspace")):
+            return sv.verify_attn(self.kv, self.q, self.ctx, self.parent, self.max_ctx, **kw)
+        cfg = self.case.cfg
+        B, N, Hq = self.q.shape[:3]
+        need = sv.verify_attn_workspace_size(self.kv, B, N, Hq, self.max_ctx, window=kw.get("window", 0),
+                                             tuning=kw.get("tuning"))
+        assert need > 0
+        out = Guarded(tuple(self.q.shape), self.q.dtype, self.q.device)
+        lse = Guarded((B, N, Hq), torch.float32, self.q.device)
+        ws = Guarded((need,), torch.uint8, self.q.device)
+        o, l = sv.verify_attn(self.kv, self.q, self.ctx, self.parent, self.max_ctx, out=out.t, lse=lse.t,
+                              workspace=ws.t, **kw)
+        for g, name in ((out, "out"), (lse, "lse"), (ws, "attention workspace")):
+            g.check(name, cfg.name)
+        return o, l
 
     def accept(self, **kw):
+        """greedy_accept with a zero-filled workspace followed by a canary band
+        (unless the caller passes one): the band must stay intact and the
+        workspace must be all zeros again after the call."""
         import draft_token_verification_sv_amd as sv
-        return sv.greedy_accept(self.logits, self.drafts, self.parent, **kw)
+        if "workspace" in kw:
+            return sv.greedy_accept(self.logits, self.drafts, self.parent, **kw)
+        B, N, V = self.logits.shape
+        ws = Guarded((sv.greedy_accept_workspace_size(B, N, V),), torch.uint8, self.logits.device, zero=True)
+        res = sv.greedy_accept(self.logits, self.drafts, self.parent, workspace=ws.t, **kw)
+        ws.check("acceptance workspace", self.case.cfg.name)
+        torch.cuda.synchronize()
+        assert not bool(ws.t.any()), "acceptance workspace not returned to zero"
+        return res
 
     def cache_arrays_host(self):
         """Host copies of the cache arrays in the storage form of the case."""

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import workloads
-from sv_harness import DeviceCase, check_attention, oracle_accept, q4_key_rounding, say
+from sv_harness import DeviceCase, check_attention, oracle_accept, q4_key_rounding, sample_accept_guarded, say
 
 pytestmark = pytest.mark.gpu
 
@@ -275,17 +275,28 @@ def test_attention_large_batch(sv, B):
     check_attention(case, out, lse, batch=sorted({0, 1, B // 4, B // 2, B - 2, B - 1}))
 
 
-FULL = [("C2", None, None), ("C3", None, None), ("C4", [0, 7, 23], None), ("C5", None, [0, 3, 7])]
+FULL = [
+    # (config, query heads checked (None: all), sequences checked (None: all), variant)
+    ("C2", None, None, ""),
+    ("C3", None, None, ""),
+    ("C3", None, None, "peaked"),
+    ("C4", [0, 6, 12, 18, 23], None, ""),          # one query head of every KV head, and the last
+    ("C4", [0, 6, 12, 18], None, "peaked"),
+    ("C5", None, None, ""),
+]
 
 
-@pytest.mark.parametrize("name,heads,batch", FULL, ids=[f[0] for f in FULL])
-def test_attention_full_size_sampled(sv, name, heads, batch):
+@pytest.mark.parametrize("name,heads,batch,variant", FULL,
+                         ids=[f[0] + ("-" + f[3] if f[3] else "") for f in FULL])
+def test_attention_full_size_sampled(sv, name, heads, batch, variant):
     """The configurations at their full sizes, in the launch configuration the
     benchmark times (library defaults), against the oracle on all rows (C2,
-    C3) or sampled heads / sequences (C4: 131072 cached tokens, C5: batch of 8)."""
+    C3, C5) or one query head of every KV head (C4: 131072 cached tokens).
+    The peaked variants give each draft row's own key a score far above the
+    cache's, so the tree mask decides an O(1) part of every output."""
     cfg = C[name]
-    say(f"[attn-full] {cfg.name} heads={heads} batch={batch}")
-    case = workloads.make_case(cfg, seed=1)
+    say(f"[attn-full] {cfg.name} heads={heads} batch={batch} variant={variant or 'plain'}")
+    case = workloads.make_case(cfg, seed=1, variant=variant)
     dc = DeviceCase(case)
     out, lse = dc.attn()
     torch.cuda.synchronize()
@@ -416,8 +427,8 @@ def test_sample_accept(sv, label, cfg, T):
     par = np.maximum(case.parent, 0)
     drafts = np.where(rng.random((B, N)) < 0.8, ys[np.arange(B)[:, None], par], case.draft_ids).astype(np.int32)
     from sv_harness import dev_tensor
-    acc, path, tok, y = sv.sample_accept(dev_tensor(case.logits, cfg.logits_dtype), dev_tensor(g, "f32"), T,
-                                         dev_tensor(drafts, "i32"), dev_tensor(case.parent, "i32"))
+    acc, path, tok, y = sample_accept_guarded(dev_tensor(case.logits, cfg.logits_dtype), dev_tensor(g, "f32"), T,
+                                              dev_tensor(drafts, "i32"), dev_tensor(case.parent, "i32"))
     torch.cuda.synchronize()
     r_y, r_acc, r_path, r_tok = oracle.sample_accept(lg32, g, T, drafts, case.parent)
     np.testing.assert_array_equal(y.cpu().numpy(), r_y)
@@ -465,8 +476,8 @@ def test_sample_accept_topk(sv, label, cfg, T, k, special):
     par = np.maximum(case.parent, 0)
     drafts = np.where(rng.random((B, N)) < 0.8, ys[np.arange(B)[:, None], par], case.draft_ids).astype(np.int32)
     from sv_harness import dev_tensor
-    acc, path, tok, y = sv.sample_accept(dev_tensor(logits, cfg.logits_dtype), dev_tensor(g, "f32"), T,
-                                         dev_tensor(drafts, "i32"), dev_tensor(case.parent, "i32"), top_k=k)
+    acc, path, tok, y = sample_accept_guarded(dev_tensor(logits, cfg.logits_dtype), dev_tensor(g, "f32"), T,
+                                              dev_tensor(drafts, "i32"), dev_tensor(case.parent, "i32"), top_k=k)
     torch.cuda.synchronize()
     r_y, r_acc, r_path, r_tok = oracle.sample_accept(lg32, g, T, drafts, case.parent, top_k=k)
     np.testing.assert_array_equal(y.cpu().numpy(), r_y)
