@@ -27,6 +27,7 @@ __all__ = [
     "kv_compact", "greedy_accept_compact", "kv_append", "sample_accept", "SV_F16", "TUNING_FIELDS",
     "check_device_errors", "SV_DEVERR_PARENT", "SV_DEVERR_PAGE", "SV_DEVERR_CTX", "SV_DEVERR_PATH",
     "ssm_conv_tree", "gated_delta_net_tree", "recurrent_commit", "tree_schedule", "debug_build",
+    "verify_attn_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 SV_F32, SV_BF16, SV_Q4, SV_F16 = 0, 1, 2, 3
@@ -139,6 +140,10 @@ lib.sv_verify_attn_tuned.argtypes = [ctypes.POINTER(_KvDesc), _I, _I, _I, _P, _I
 lib.sv_greedy_accept_tuned.restype = _I
 lib.sv_greedy_accept_tuned.argtypes = [_I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P, ctypes.POINTER(_Tuning), _P,
                                        ctypes.c_size_t, _P]
+lib.sv_verify_attn_noalloc.restype = _I
+lib.sv_verify_attn_noalloc.argtypes = [ctypes.POINTER(_KvDesc), _I, _I, _I, _P, _I, _P, _I, _P, ctypes.c_float, _I,
+                                       _P, _P, _P]
+NOALLOC_SCRATCH_BYTES = 32 << 20
 lib.sv_check_device_errors.restype = _I
 lib.sv_check_device_errors.argtypes = [_P]
 
@@ -341,6 +346,28 @@ def verify_attn(kv: KVCache, q: torch.Tensor, ctx_lens: torch.Tensor, parent: to
     else:
         rc = lib.sv_verify_attn(*args, *tail)
         _check_ws(rc, "sv_verify_attn", "attn", q.device, default_ws)
+    return out, lse
+
+
+def verify_attn_noalloc(kv: KVCache, q: torch.Tensor, ctx_lens: torch.Tensor, parent: torch.Tensor,
+                        max_ctx: int, out: torch.Tensor, lse: Optional[torch.Tensor] = None, sm_scale: float = 0.0,
+                        layer: int = 0, window: int = 0):
+    """verify_attn through sv_verify_attn_noalloc: no workspace (the library's
+    static per-GPU buffer of NOALLOC_SCRATCH_BYTES holds the split partials;
+    calls that overlap on one GPU race), and the caller passes the outputs, so
+    nothing is allocated."""
+    if q.dim() != 4 or not q.is_contiguous() or not q.is_cuda:
+        raise ValueError("q must be a contiguous [B, N, Hq, D] device tensor")
+    B, N, Hq, D = q.shape
+    _i32(ctx_lens, "ctx_lens")
+    _i32(parent, "parent")
+    if out is None or out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped like q")
+    d = kv.desc(layer)
+    rc = lib.sv_verify_attn_noalloc(ctypes.byref(d), B, N, Hq, _ptr(ctx_lens), int(max_ctx), _ptr(q),
+                                    _dtype_code(q), _ptr(parent), float(sm_scale), int(window), _ptr(out), _ptr(lse),
+                                    _stream(q.device))
+    _check(rc, "sv_verify_attn_noalloc")
     return out, lse
 
 

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "attn_sched.h"
 
@@ -421,7 +422,66 @@ int verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads, co
 
 }  // namespace
 
+namespace {
+
+// Split partials of sv_verify_attn_noalloc: a static buffer in device memory,
+// one copy per GPU (each device that loads the library holds it until the
+// process ends).  In host code `scratch` is only a stand-in for the symbol;
+// its device address on each GPU comes from hipGetSymbolAddress, looked up
+// once per device with that device current and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = (size_t)SV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The current device's copy of `scratch`, or nullptr (HIP error recorded).
+void *device_scratch() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        hip_fail(e);
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxScratchDevices) {
+        hip_fail(hipErrorInvalidDevice);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr) {
+            hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol);
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
 extern "C" {
+
+int sv_verify_attn_noalloc(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
+                           const int32_t *ctx_lens, int max_ctx,
+                           const void *q, int q_dtype, const int32_t *parent, float sm_scale, int window,
+                           void *out, float *lse, void *stream) {
+    // argument and size checks first: a call that cannot run touches no device
+    int rc = check_attn_shape(kv, batch, n_nodes, n_q_heads, max_ctx);
+    if (rc != SV_OK) return rc;
+    if (window < 0 || (window > 0 && window < n_nodes)) return SV_EINVAL;
+    if (q_dtype != SV_F32 && q_dtype != SV_BF16) return SV_EINVAL;
+    const AttnPlan pl = plan_attn(kv->dtype, q_dtype, kv->head_dim, batch, n_nodes, n_q_heads, kv->n_kv_heads,
+                                  max_ctx, kv->page_size, window, Tuning{});
+    if (pl.ws_bytes > kScratchBytes) return SV_EWORKSPACE;
+    void *ws = device_scratch();
+    if (ws == nullptr) return SV_EHIP;
+    return verify_attn(kv, batch, n_nodes, n_q_heads, ctx_lens, max_ctx, q, q_dtype, parent, sm_scale, window,
+                       nullptr, out, lse, ws, kScratchBytes, stream);
+}
 
 size_t sv_verify_attn_workspace_size(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
                                      int max_ctx) {

@@ -169,6 +169,27 @@ int sv_verify_attn_window(const sv_kv_cache *kv, int batch, int n_nodes, int n_q
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * sv_verify_attn_noalloc -- sv_verify_attn_window (window 0 = the whole key
+ * range) with no workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, serving loops and harnesses that
+ * forbid allocation.  The split partials go to a static buffer of
+ * SV_NOALLOC_SCRATCH_BYTES (32 MiB) in device memory, one per GPU, that the
+ * library holds from its first use on that GPU until the process ends; the
+ * call allocates and frees nothing.  A call whose launch plan needs more than
+ * that (sv_verify_attn_window_workspace_size tells in advance) returns
+ * SV_EWORKSPACE before touching the device.  The buffer needs no clearing
+ * (the partials are written before they are read within each call), but
+ * every call on one GPU shares it: calls that may overlap on one GPU (other
+ * streams, other host threads) race and must be serialised by the caller.
+ * Arguments, results and errors otherwise as sv_verify_attn_window.
+ */
+#define SV_NOALLOC_SCRATCH_BYTES (32u << 20)
+int sv_verify_attn_noalloc(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads,
+                           const int32_t *ctx_lens, int max_ctx,
+                           const void *q, int q_dtype, const int32_t *parent, float sm_scale, int window,
+                           void *out, float *lse, void *stream);
+
+/*
  * sv_greedy_accept -- greedy acceptance [DFN "Architecture": greedy verify;
  * "From autoregressive to DDTree": longest accepted root path].
  *

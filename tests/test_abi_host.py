@@ -297,3 +297,20 @@ def test_check_device_errors_host_side(lib):
     else:
         assert dbg.sv_check_device_errors(None) == -4
         assert dbg.sv_last_hip_error() != 0
+
+
+def test_noalloc_rejects_large_plans_on_the_host(lib):
+    """sv_verify_attn_noalloc: a plan whose split partials exceed the static
+    32 MiB buffer (64 paged sequences of 30K keys, 32/8 heads, dim 128) returns
+    SV_EWORKSPACE before any device call; bad arguments return SV_EINVAL."""
+    lib.sv_verify_attn_workspace_size.restype = ctypes.c_size_t
+    d = kv(dtype=1, n_kv_heads=8, head_dim=128, page_size=16, capacity=200000, n_seqs=0,
+           max_pages_per_seq=(30000 + 16 + 15) // 16, page_table=FAKE + 0x200000)
+    assert lib.sv_verify_attn_workspace_size(ctypes.byref(d), 64, 16, 32, 30000) > 32 << 20
+    P = ctypes.c_void_p(FAKE)
+    assert lib.sv_verify_attn_noalloc(ctypes.byref(d), 64, 16, 32, P, 30000, P, 1, P, ctypes.c_float(0.0), 0, P,
+                                      None, None) == -3
+    assert lib.sv_verify_attn_noalloc(ctypes.byref(d), 64, 0, 32, P, 30000, P, 1, P, ctypes.c_float(0.0), 0, P,
+                                      None, None) == -1
+    assert lib.sv_verify_attn_noalloc(ctypes.byref(d), 64, 16, 32, P, 30000, P, 1, P, ctypes.c_float(0.0), 8, P,
+                                      None, None) == -1              # window below N
