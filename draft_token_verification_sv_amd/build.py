@@ -32,11 +32,9 @@ FLAGS = [
 # extra flags per source: the cooperative 4-bit kernel keeps no NaN semantics
 # in its maxima (inputs are finite; masked scores are -inf, which stays exact)
 EXTRA = {"attn_q4.hip": ["-fno-honor-nans"]}
-# sources left to the compiler's own choice of accumulation registers: the
-# cooperative 4-bit kernel needs all 512 registers of a wave, and with its
-# rescale kept out of the fast loop the accumulation-register form measured
-# 144 us against 156 us for the forced VGPR form (131K-key 4-bit block of 16)
-NO_VGPR_FORM = {"attn_q4.hip"}
+# sources left to the compiler's own choice of accumulation registers (none:
+# the cooperative 4-bit kernel places its O accumulators itself)
+NO_VGPR_FORM: set = set()
 
 
 def _compile(src: str, obj_dir: str, debug: bool) -> str:

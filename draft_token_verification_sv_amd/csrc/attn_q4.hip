@@ -127,19 +127,95 @@ __device__ __forceinline__ u32x4 dequant_word(uint32_t w, h2 s, uint32_t m_lo, u
     return r;
 }
 
-__device__ __forceinline__ f32x4 mfma16(h8 a, h8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+// ---- matrix instructions ------------------------------------------------------
+// S^T = K Q^T runs with its accumulators in architectural VGPRs.  The O^T
+// accumulators (up to 24 tiles of 16 x 16 fp32) live in the accumulation
+// registers a0..a95 for the whole kernel: tile I in a[4I .. 4I+3], written
+// and read only by the inline assembly below (the kernel is compiled in the
+// VGPR matrix form and never spills, so the compiler itself uses no
+// accumulation register; the clobbers make it count them in the kernel's
+// register total).  With the compiler's own allocation the O tiles moved to
+// other registers inside the loop and were copied back on every chunk.
+// Hazards the compiler cannot see are covered here: s_nop 1 before an S
+// instruction (its operands may have just been written by vector code),
+// mfma_drain() before vector code reads a matrix result.
+__device__ __forceinline__ f32x4 mfma_s_first(h8 a, h8 b) {
+    f32x4 d;
+    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+    return d;
+}
+__device__ __forceinline__ void mfma_s_acc(f32x4 &c, h8 a, h8 b) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
 
-// O^T += V^T P^T with the accumulator tied in place in the accumulation
-// registers (the compiler's own form renames accumulators across the loop
-// back-edge and copies all of them every chunk).  Its operands come from LDS
-// reads (the compiler waits for those) and from the previous instruction of
-// the same accumulator; vector code that reads or rescales the accumulators
-// first waits behind mfma_drain().
-__device__ __forceinline__ void mfma_o(f32x4 &acc, h8 a, h8 b) {
-    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+template <int I> struct OTile;
+#define SV_OTILE(I, R0, R1, R2, R3)                                                                        \
+    template <> struct OTile<I> {                                                                          \
+        static __device__ __forceinline__ void zero() {                                                    \
+            asm volatile("v_accvgpr_write_b32 a" #R0 ", 0\n\tv_accvgpr_write_b32 a" #R1                     \
+                         ", 0\n\tv_accvgpr_write_b32 a" #R2 ", 0\n\tv_accvgpr_write_b32 a" #R3 ", 0" ::       \
+                             : "a" #R0, "a" #R1, "a" #R2, "a" #R3);                                         \
+        }                                                                                                  \
+        static __device__ __forceinline__ void mac(h8 a, h8 b) {                                           \
+            asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_f16 a[" #R0 ":" #R3 "], %0, %1, a[" #R0 ":" #R3 "]"  \
+                         ::"v"(a), "v"(b)                                                                  \
+                         : "a" #R0, "a" #R1, "a" #R2, "a" #R3);                                             \
+        }                                                                                                  \
+        static __device__ __forceinline__ f32x4 read() {                                                   \
+            f32x4 r;                                                                                       \
+            asm volatile("v_accvgpr_read_b32 %0, a" #R0 "\n\tv_accvgpr_read_b32 %1, a" #R1                  \
+                         "\n\tv_accvgpr_read_b32 %2, a" #R2 "\n\tv_accvgpr_read_b32 %3, a" #R3                \
+                         : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]));                                 \
+            return r;                                                                                      \
+        }                                                                                                  \
+        static __device__ __forceinline__ void scale(float f) {                                            \
+            float t0, t1, t2, t3;                                                                          \
+            asm volatile("v_accvgpr_read_b32 %0, a" #R0 "\n\tv_accvgpr_read_b32 %1, a" #R1                  \
+                         "\n\tv_accvgpr_read_b32 %2, a" #R2 "\n\tv_accvgpr_read_b32 %3, a" #R3                \
+                         "\n\tv_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\tv_mul_f32 %2, %2, %4"            \
+                         "\n\tv_mul_f32 %3, %3, %4"                                                        \
+                         "\n\tv_accvgpr_write_b32 a" #R0 ", %0\n\tv_accvgpr_write_b32 a" #R1 ", %1"           \
+                         "\n\tv_accvgpr_write_b32 a" #R2 ", %2\n\tv_accvgpr_write_b32 a" #R3 ", %3"           \
+                         : "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)                                       \
+                         : "v"(f)                                                                          \
+                         : "a" #R0, "a" #R1, "a" #R2, "a" #R3);                                             \
+        }                                                                                                  \
+    };
+SV_OTILE(0, 0, 1, 2, 3)
+SV_OTILE(1, 4, 5, 6, 7)
+SV_OTILE(2, 8, 9, 10, 11)
+SV_OTILE(3, 12, 13, 14, 15)
+SV_OTILE(4, 16, 17, 18, 19)
+SV_OTILE(5, 20, 21, 22, 23)
+SV_OTILE(6, 24, 25, 26, 27)
+SV_OTILE(7, 28, 29, 30, 31)
+SV_OTILE(8, 32, 33, 34, 35)
+SV_OTILE(9, 36, 37, 38, 39)
+SV_OTILE(10, 40, 41, 42, 43)
+SV_OTILE(11, 44, 45, 46, 47)
+SV_OTILE(12, 48, 49, 50, 51)
+SV_OTILE(13, 52, 53, 54, 55)
+SV_OTILE(14, 56, 57, 58, 59)
+SV_OTILE(15, 60, 61, 62, 63)
+SV_OTILE(16, 64, 65, 66, 67)
+SV_OTILE(17, 68, 69, 70, 71)
+SV_OTILE(18, 72, 73, 74, 75)
+SV_OTILE(19, 76, 77, 78, 79)
+SV_OTILE(20, 80, 81, 82, 83)
+SV_OTILE(21, 84, 85, 86, 87)
+SV_OTILE(22, 88, 89, 90, 91)
+SV_OTILE(23, 92, 93, 94, 95)
+#undef SV_OTILE
+
+// f(std::integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
 }
+
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
 template <int NTS, bool PAGED>
@@ -324,14 +400,11 @@ __global__ __launch_bounds__(256, 1) void attn_q4c_kernel(AttnParams p) {
     }
     if (n_st > 1) issue(1);
 
-    f32x4 o[RB][4];
+    // O^T tile (row tile t, head-dim tile dt of this wave) = OTile<4 t + dt>
+    static_for<0, 4 * RB>([&](auto ic) { OTile<decltype(ic)::value>::zero(); });
     float m_ref[RB], l_s[NTS], l_p[NTS];
 #pragma unroll
-    for (int t = 0; t < RB; ++t) {
-        m_ref[t] = -INFINITY;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int t = 0; t < RB; ++t) m_ref[t] = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NTS; ++i) l_s[i] = 0.f;
 
@@ -406,12 +479,14 @@ __global__ __launch_bounds__(256, 1) void attn_q4c_kernel(AttnParams p) {
             const int pos0 = cb + 16 * pt + 4 * qd;
 #pragma unroll
             for (int i = 0; i < NTS; ++i) {
-                const uint64_t anc = node_of[i] >= 0 ? anc_s[node_of[i]] : 0ull;
+                const uint64_t anc_r = anc_s[node_of[i] > 0 ? node_of[i] : 0];     // in bounds for every lane
+                const uint64_t anc = node_of[i] >= 0 ? anc_r : 0ull;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int pos = pos0 + j;
                     bool vis = pos < p1;
-                    if (pos >= ctx) vis = vis && (((anc >> ((pos - ctx) & 63)) & 1ull) != 0ull);
+                    // bitwise, not short-circuit: no branch per lane
+                    vis &= (pos < ctx) | (((anc >> ((pos - ctx) & 63)) & 1ull) != 0ull);
                     sc[i][j] = vis ? sc[i][j] : -INFINITY;
                 }
             }
@@ -439,9 +514,11 @@ __global__ __launch_bounds__(256, 1) void attn_q4c_kernel(AttnParams p) {
         const h8 kf = kread(0, k);
 #pragma unroll
         for (int i = 0; i < NTS; ++i) {
-            sacc[i] = mfma16(kf, qf[i][k], k == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc[i]);
+            if (k == 0) sacc[i] = mfma_s_first(kf, qf[i][k]);
+            else mfma_s_acc(sacc[i], kf, qf[i][k]);
         }
     }
+    mfma_drain();
     apply_mask(0, sacc);
 #pragma unroll
     for (int i = 0; i < NTS; ++i) row_max(sacc[i], i, mxb);
@@ -518,14 +595,15 @@ __global__ __launch_bounds__(256, 1) void attn_q4c_kernel(AttnParams p) {
                 const bool need = cm > m_ref[t] + 8.f;
                 alpha[t] = need ? __builtin_amdgcn_exp2f(m_ref[t] - cm) : 1.f;
                 m_ref[t] = need ? cm : m_ref[t];
-                grow = grow || need;
+                grow |= need;
             }
             if (__any(grow)) {
                 mfma_drain();
-#pragma unroll
-                for (int t = 0; t < RB; ++t)
-#pragma unroll
-                    for (int dt = 0; dt < 4; ++dt) o[t][dt] *= alpha[t];
+                static_for<0, 4 * RB>([&](auto ic) {
+                    constexpr int I = decltype(ic)::value;
+                    OTile<I>::scale(alpha[I / 4]);
+                });
+                asm volatile("s_nop 3");
 #pragma unroll
                 for (int i = 0; i < NTS; ++i) l_s[i] *= hh ? alpha[NTS + i] : alpha[i];
             }
@@ -553,7 +631,7 @@ __global__ __launch_bounds__(256, 1) void attn_q4c_kernel(AttnParams p) {
         if constexpr (!SLOW) {
             bool grow = false;
 #pragma unroll
-            for (int t = 0; t < RB; ++t) grow = grow || (fmaxf(mxv[2 * t], mxv[2 * t + 1]) > m_ref[t] + 8.f);
+            for (int t = 0; t < RB; ++t) grow |= fmaxf(mxv[2 * t], mxv[2 * t + 1]) > m_ref[t] + 8.f;
             if (__builtin_expect(__any(grow), 0)) return true;
         }
 #pragma unroll
@@ -568,7 +646,8 @@ __global__ __launch_bounds__(256, 1) void attn_q4c_kernel(AttnParams p) {
             if (k + KR < 8) kf[k % KR] = kread(gs, k + KR);
 #pragma unroll
             for (int i = 0; i < NTS; ++i) {
-                sacc_n[i] = mfma16(ka, qf[i][k], k == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sacc_n[i]);
+                if (k == 0) sacc_n[i] = mfma_s_first(ka, qf[i][k]);
+                else mfma_s_acc(sacc_n[i], ka, qf[i][k]);
             }
             if (k == 2) dq_word(1, g + 1, cv, 2);
             if (k == 5) dq_word(1, g + 1, cv, 3);
@@ -578,6 +657,7 @@ __global__ __launch_bounds__(256, 1) void attn_q4c_kernel(AttnParams p) {
         if (LPW > 8 && st_issue < n_st)
 #pragma unroll
             for (int j = 8; j < LPW; ++j) issue_one(st_issue, j);
+        mfma_drain();                                       // S(g + 1) complete before vector reads
 
         // stage (g + 2) / 4 is needed from here on: this wave's part landed
         if (((g + 2) & (CPS - 1)) == 0 && g + 2 < NCH) wait_vm<0>();
@@ -604,18 +684,20 @@ __global__ __launch_bounds__(256, 1) void attn_q4c_kernel(AttnParams p) {
             for (int i = 0; i < NTS; ++i) row_max(sacc_n[i], i, mxw);
             dq_word(0, gk, ck, 0);
             dq_word(0, gk, ck, 1);
-#pragma unroll
-            for (int t = 0; t < RB; ++t) {
+            static_for<0, RB>([&](auto tc) {
+                constexpr int t = decltype(tc)::value;
                 const h8 pa = pf[t & 1];
-                if (t + 2 < RB) pf[t & 1] = *(const h8 *)(prd + 16 * (t + 2) * PROW);
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt) o[t][dt] = mfma16(vf[dt], pa, o[t][dt]);
+                if constexpr (t + 2 < RB) pf[t & 1] = *(const h8 *)(prd + 16 * (t + 2) * PROW);
+                static_for<0, 4>([&](auto dc) {
+                    constexpr int dt = decltype(dc)::value;
+                    OTile<4 * t + dt>::mac(vf[dt], pa);
+                });
                 // K words 2 and 3 between the matrix instructions (both after the
                 // first tile when there are only two)
-                if (t == (RB >= 4 ? 1 : 0)) dq_word(0, gk, ck, 2);
-                if (t == (RB >= 4 ? 3 : 1)) dq_word(0, gk, ck, 3);
+                if constexpr (t == (RB >= 4 ? 1 : 0)) dq_word(0, gk, ck, 2);
+                if constexpr (t == (RB >= 4 ? 3 : 1)) dq_word(0, gk, ck, 3);
                 __builtin_amdgcn_sched_barrier(0);
-            }
+            });
         }
 #pragma unroll
         for (int i = 0; i < NTS; ++i) sacc[i] = sacc_n[i];
@@ -646,24 +728,25 @@ __global__ __launch_bounds__(256, 1) void attn_q4c_kernel(AttnParams p) {
 
     // ---- partials of this split --------------------------------------------------
     const int64_t part = wu.part;
-#pragma unroll
-    for (int t = 0; t < RB; ++t) {
+    static_for<0, RB>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
         const int rl = 16 * t + l16;
-        if (rl >= rows_here) continue;
         float *op = p.part_o + (part * R + row0 + rl) * D;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
+        static_for<0, 4>([&](auto dc) {
+            constexpr int dt = decltype(dc)::value;
+            const f32x4 o = OTile<4 * t + dt>::read();
+            if (rl >= rows_here) return;
             // slot s = 64 wave + 16 dt + 4 qd + j holds head-dim 8 (s / 8) + pi(s % 8)
             const int s0 = 64 * wave + 16 * dt + 4 * qd;
             const int base = s0 & ~7;
             const int odd = (s0 >> 2) & 1;               // slots 4..7 of the group of 8
             // pi(0..3) = 0, 4, 2, 6;  pi(4..7) = 1, 5, 3, 7
-            op[base + (odd ? 1 : 0)] = o[t][dt][0];
-            op[base + (odd ? 5 : 4)] = o[t][dt][1];
-            op[base + (odd ? 3 : 2)] = o[t][dt][2];
-            op[base + (odd ? 7 : 6)] = o[t][dt][3];
-        }
-    }
+            op[base + (odd ? 1 : 0)] = o[0];
+            op[base + (odd ? 5 : 4)] = o[1];
+            op[base + (odd ? 3 : 2)] = o[2];
+            op[base + (odd ? 7 : 6)] = o[3];
+        });
+    });
     if (pt == 0 && qd == 0) {
 #pragma unroll
         for (int i = 0; i < NTS; ++i) {
