@@ -51,3 +51,50 @@ def test_kernels_use_no_scratch(tmp_path):
     assert all("private_segment_fixed_size" in v for v in kernels.values())
     bad = {k: v for k, v in kernels.items() if v["private_segment_fixed_size"] != 0}
     assert not bad, bad
+
+
+def test_cooperative_kernel_owns_its_accumulation_registers(tmp_path):
+    """The cooperative 4-bit attention kernel keeps its O accumulators in
+    a0..a95 through inline assembly alone; the compiler must not place any
+    value of its own there (a spill or copy into them would corrupt O without
+    an error).  Compiled to assembly with the library's flags, every reference
+    to a0..a95 in those kernels must sit inside an inline-assembly block."""
+    import importlib.util
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("sv_build", os.path.join(root, "draft_token_verification_sv_amd",
+                                                                           "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    if not os.path.exists(mod.HIPCC):
+        pytest.skip("hipcc not found")
+    src = os.path.join(mod.CSRC, "attn_q4.hip")
+    out = tmp_path / "attn_q4.s"
+    flags = [f for f in mod.FLAGS if f not in ("-Wall",)] + mod.EXTRA.get("attn_q4.hip", [])
+    subprocess.run([mod.HIPCC, *flags, "--cuda-device-only", "-S", src, "-o", str(out)], check=True,
+                   capture_output=True)
+    lines = out.read_text().split("\n")
+    starts = [i for i, l in enumerate(lines) if re.match(r"^_Z\S*attn_q4c_kernel\S*:", l)]
+    assert len(starts) == 6, len(starts)                 # 3 tile counts x (contiguous, paged)
+    pinned = re.compile(r"\ba(\d+)\b|\ba\[(\d+):(\d+)\]")
+    for s0 in starts:
+        in_asm, bad, n_asm = False, [], 0
+        for l in lines[s0:]:
+            t = l.strip()
+            if t.startswith(".Lfunc_end"):
+                break
+            if t.startswith(";;#ASMSTART"):
+                in_asm = True
+                continue
+            if t.startswith(";;#ASMEND"):
+                in_asm = False
+                continue
+            code = t.split(";")[0]
+            for m in pinned.finditer(code):
+                lo = int(m.group(1) if m.group(1) is not None else m.group(2))
+                if lo < 96:
+                    if in_asm:
+                        n_asm += 1
+                    else:
+                        bad.append(t)
+        assert n_asm > 0
+        assert not bad, (lines[s0], bad[:5])
