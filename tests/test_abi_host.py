@@ -9,7 +9,9 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-LIB = os.path.join(ROOT, "draft_token_verification_sv_amd", "libsv.so")
+# SV_ABI_LIB: another build of the same entry points (the host-sanitized one of
+# test_abi_host_sanitized.py); by default the library the package loads
+LIB = os.environ.get("SV_ABI_LIB") or os.path.join(ROOT, "draft_token_verification_sv_amd", "libsv.so")
 HEADER = os.path.join(ROOT, "include", "sv.h")
 
 
