@@ -188,30 +188,24 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
     }
 }
 
-// Split merge: one block of 256 threads per (output row, 64-column slice), so
-// that even a short batch (8 rows x 24 heads) gives the grid several blocks
-// per CU.  Thread t covers the 4 columns 4 (t % 16) .. +3 of the slice for
-// the splits s = t / 16 (mod 16), with 16-byte loads; the first OB partial
-// rows of each thread go out together with the (m, l) loads.  The block then
-// finds M = max_s m_s and the weights 2^(m_s - M) (kept in LDS), every thread
-// accumulates its weighted partials, and the 16 split groups add up through
-// LDS.  Slots past the sequence's splits (not written by this call) are never
-// read.  The slice-0 block writes the log-sum-exp.
-constexpr int kMergeCols = 64;
-
+// Split merge: one block of 256 threads per output row.  Thread t covers the 4
+// columns 4 (t % (D/4)) .. +3 of the splits s = t / (D/4) (mod NSG), NSG =
+// 1024 / D split groups, with 16-byte loads.  The first OB partial rows of each
+// thread go out together with the (m, l) loads; the block then finds
+// M = max_s m_s and the weights 2^(m_s - M) (kept in LDS), every thread
+// accumulates its weighted partials, and the split groups add up through LDS.
+// Slots past the sequence's splits (not written by this call) are never read.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
-    constexpr int CG = kMergeCols / 4;      // column groups of one slice
+    constexpr int CG = D / 4;               // column groups of one row
     constexpr int NSG = 256 / CG;           // split groups
-    constexpr int OB = 4;                   // partial rows in flight per thread
-    constexpr int NSL = D / kMergeCols;     // slices per row
+    constexpr int OB = 16;                  // partial rows in flight per thread
     __shared__ float w_s[kMaxSplits];
     __shared__ float red[8];
     __shared__ f32x4 acc_s[NSG - 1][CG];
     const int tid = threadIdx.x;
     const int c = tid % CG, sg = tid / CG;
-    const int slice = blockIdx.x % NSL;
-    const int row = blockIdx.x / NSL;
+    const int row = blockIdx.x;
     const int h = row % p.Hq;
     const int n = (row / p.Hq) % p.N;
     const int b = row / (p.Hq * p.N);
@@ -247,7 +241,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
         const int L = (int)key_range(p, ctx_of(p.ctx_lens, b, p.max_ctx, p.err));
         ns = min(p.n_splits, (L + p.split_len - 1) / p.split_len);
     }
-    const float *op = p.part_o + (base * p.R + r) * D + slice * kMergeCols + 4 * c;
+    const float *op = p.part_o + (base * p.R + r) * D + 4 * c;
     const int64_t sstride = (int64_t)p.R * D;
     f32x4 ov[OB];
 #pragma unroll
@@ -305,7 +299,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
 #pragma unroll
     for (int k = 0; k < NSG - 1; ++k) acc += acc_s[k][c];
     const float inv = 1.f / lsum;
-    const int64_t oi = (((int64_t)b * p.N + n) * p.Hq + h) * D + slice * kMergeCols + 4 * c;
+    const int64_t oi = (((int64_t)b * p.N + n) * p.Hq + h) * D + 4 * c;
     if (p.q_f32) {
         *(f32x4 *)((float *)p.out + oi) = acc * inv;
     } else {
@@ -314,7 +308,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
         pk.y = (uint32_t)f32_to_bf16_bits(acc[2] * inv) | ((uint32_t)f32_to_bf16_bits(acc[3] * inv) << 16);
         *(uint2 *)((uint16_t *)p.out + oi) = pk;
     }
-    if (slice == 0 && tid == 0 && p.lse != nullptr)
+    if (tid == 0 && p.lse != nullptr)
         p.lse[((int64_t)b * p.N + n) * p.Hq + h] = (M + log2f(lsum)) * 0.69314718055994530942f;
 }
 
@@ -354,10 +348,10 @@ hipError_t launch_attn_merge(const AttnParams &p, int D, hipStream_t st) {
             hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(rows), dim3(256), 0, st, p);
             break;
         case 128:
-            hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(rows * 2), dim3(256), 0, st, p);
+            hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(rows), dim3(256), 0, st, p);
             break;
         case 256:
-            hipLaunchKernelGGL(attn_merge_kernel<256>, dim3(rows * 4), dim3(256), 0, st, p);
+            hipLaunchKernelGGL(attn_merge_kernel<256>, dim3(rows), dim3(256), 0, st, p);
             break;
         default: return hipErrorInvalidValue;
     }
