@@ -285,7 +285,12 @@ def run_workload(sv, dev, key, args, steps, full):
     import workloads
     cfg = workloads.CONFIGS[key]
     case = workloads.make_case(cfg, seed=1)
-    tuning = {"attn_target_wgs": args.target_wgs} if args.target_wgs else None
+    tuning = {}
+    if args.target_wgs:
+        tuning["attn_target_wgs"] = args.target_wgs
+    if args.attn_q4_kernel != "default":
+        tuning["attn_q4_kernel"] = args.attn_q4_kernel
+    tuning = tuning or None
     window = args.window
 
     def up(x, kind):
@@ -484,6 +489,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate-bytes", type=float, default=1.1 * 2 ** 30)
     ap.add_argument("--target-wgs", type=int, default=0, help="attention grid target (0: library default)")
+    ap.add_argument("--attn-q4-kernel", default="default", choices=["default", "cooperative", "pipelined", "wide"],
+                    help="kernel for 4-bit caches of head dim 256 (default: the library's choice)")
     ap.add_argument("--spin-cycles", type=float, default=1e8,
                     help="spin kernel ahead of the per-call event timing (clock cycles)")
     ap.add_argument("--window", type=int, default=0,
@@ -552,6 +559,8 @@ def main():
         "events_queued_ahead": head["events_queued_ahead"],
         "per_config": per_config,
     }
+    if args.target_wgs or args.attn_q4_kernel != "default":
+        rec["tuning"] = {"attn_target_wgs": args.target_wgs, "attn_q4_kernel": args.attn_q4_kernel}
     if args.recurrent != "none":
         def capture_timed(steps):
             def capture(fn):

@@ -72,8 +72,10 @@ class _Tuning(ctypes.Structure):
 
 
 def _tuning(tuning) -> Optional[_Tuning]:
-    """A dict of sv_tuning fields (``attn_q4_kernel`` may also be "cooperative"
-    or "pipelined") -> the struct, or None."""
+    """A dict of sv_tuning fields (``attn_q4_kernel`` may also be
+    "cooperative" (the four-wave cooperative kernel), "pipelined" or "wide"
+    (the eight-wave cooperative kernel, also the default)) -> the struct, or
+    None."""
     if not tuning:
         return None
     t = _Tuning()
@@ -81,7 +83,7 @@ def _tuning(tuning) -> Optional[_Tuning]:
         if key not in TUNING_FIELDS:
             raise ValueError(f"unknown tuning field {key!r}")
         if key == "attn_q4_kernel" and isinstance(val, str):
-            val = {"cooperative": 1, "pipelined": 2}[val]
+            val = {"cooperative": 1, "pipelined": 2, "wide": 3}[val]
         setattr(t, key, int(val))
     return t
 

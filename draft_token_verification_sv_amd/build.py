@@ -18,7 +18,7 @@ OUT = os.path.join(PKG, "libsv.so")
 OUT_DEBUG = os.path.join(PKG, "libsv_debug.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["sv_api.cpp", "attn_dma.hip", "attn_mfma.hip", "attn_valu.hip", "attn_q4.hip", "accept.hip",
+SOURCES = ["sv_api.cpp", "attn_dma.hip", "attn_mfma.hip", "attn_valu.hip", "attn_q4.hip", "attn_q4w.hip", "accept.hip",
            "compact.hip", "append.hip", "recurrent.hip", "topk.hip", "debug.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -31,7 +31,7 @@ FLAGS = [
 ]
 # extra flags per source: the cooperative 4-bit kernel keeps no NaN semantics
 # in its maxima (inputs are finite; masked scores are -inf, which stays exact)
-EXTRA = {"attn_q4.hip": ["-fno-honor-nans"]}
+EXTRA = {"attn_q4.hip": ["-fno-honor-nans"], "attn_q4w.hip": ["-fno-honor-nans"]}
 # sources left to the compiler's own choice of accumulation registers (none:
 # the cooperative 4-bit kernel places its O accumulators itself)
 NO_VGPR_FORM: set = set()

@@ -84,7 +84,7 @@ __device__ __forceinline__ double wave_sum_f64(double x) {
 // so that one barrier per call suffices.
 __device__ __forceinline__ uint32_t sched_block_sum(uint32_t v, SchedLds &sm, int &par) {
     v = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_u32(v), 63);
-    if ((threadIdx.x & 63) == 0) sm.red[par][threadIdx.x >> 6] = v;
+    if ((threadIdx.x & 63) == 0 && threadIdx.x < 256) sm.red[par][threadIdx.x >> 6] = v;
     __syncthreads();
     const uint32_t r = sm.red[par][0] + sm.red[par][1] + sm.red[par][2] + sm.red[par][3];
     par ^= 1;
@@ -158,7 +158,7 @@ __device__ __forceinline__ uint32_t key_range(const AttnParams &p, int ctx) {
     return (uint32_t)(p.window > 0 && L > p.window ? p.window : L);
 }
 
-// Decodes unit u.  Must be called by all 256 threads of the block (the dynamic
+// Decodes unit u.  Must be called by all threads of the block (the dynamic
 // schedule synchronises); returns false, uniformly, when u holds no work.
 // `record` marks the row block that writes the per-sequence table.
 __device__ __forceinline__ bool attn_unit(const AttnParams &p, int u, bool record, SchedLds &sm,
@@ -196,26 +196,57 @@ __device__ __forceinline__ bool attn_unit(const AttnParams &p, int u, bool recor
                 const uint32_t c = wave_scan_u32((Lb + x - 1u) / x);
                 return (long long)H * (uint32_t)__builtin_amdgcn_readlane((int)c, 63);
             });
-            const uint32_t ns = (Lb + sl - 1u) / sl;
+            uint32_t ns = (Lb + sl - 1u) / sl;
+            // Fill the grid: while unit slots remain, give the sequence whose
+            // units are the longest one more split (its units shrink toward
+            // the average), so that the last workgroups to finish do not carry
+            // units up to twice the average.  A split is taken only if it
+            // shortens the units (after rounding to the quantum) and leaves no
+            // unit empty; ties go to the lowest sequence.
+            {
+                const uint32_t budget = (uint32_t)(umax / H);
+                uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_u32(ns), 63);
+#pragma unroll 1
+                for (int it = 0; it < 64 && total < budget; ++it) {
+                    const uint32_t cur = ns ? (((Lb + ns - 1u) / ns + (uint32_t)qm) & ~(uint32_t)qm) : 0u;
+                    const uint32_t n1 = ns + 1u;
+                    const uint32_t nxt = ((Lb + n1 - 1u) / n1 + (uint32_t)qm) & ~(uint32_t)qm;
+                    const bool can = ns > 0u && n1 <= (uint32_t)kMaxSplits && nxt < cur &&
+                                     (uint64_t)ns * nxt < (uint64_t)Lb;
+                    unsigned long long key = can ? (((unsigned long long)cur << 8) | (unsigned)(63 - lane)) : 0ull;
+#pragma unroll
+                    for (int m = 1; m < 64; m <<= 1) {
+                        const unsigned long long o = __shfl_xor(key, m, 64);
+                        key = o > key ? o : key;
+                    }
+                    if (key == 0ull) break;
+                    if ((unsigned)(63 - lane) == (unsigned)(key & 255ull)) ns = n1;
+                    ++total;
+                }
+            }
             const uint32_t before = wave_scan_u32(ns) - ns;
             if (lane == 0) sm.pick[0] = -1;           // same wavefront: ordered before the pick
             sched_pick(sm, u, lane, Lb, (uint32_t)(cb + p.N), ns, (long long)H * before, H, qm);
         }
         __syncthreads();
     } else {
+        // the first 256 threads hold the sequences; threads beyond them (a
+        // workgroup of 512) take part in the barriers with no sequence
+        const bool act = tid < 256;
         const int rounds = (p.B + 255) >> 8;         // uniform, <= kSchedRounds
         uint32_t Lr[kSchedRounds], Fr[kSchedRounds];
         double tl = 0.0;
 #pragma unroll
         for (int k = 0; k < kSchedRounds; ++k) {
             const int b = 256 * k + tid;
-            const int cb = b < p.B ? ctx_of(p.ctx_lens, b, p.max_ctx, p.err) : 0;
-            Lr[k] = b < p.B ? key_range(p, cb) : 0u;
+            const bool has = act && b < p.B;
+            const int cb = has ? ctx_of(p.ctx_lens, b, p.max_ctx, p.err) : 0;
+            Lr[k] = has ? key_range(p, cb) : 0u;
             Fr[k] = (uint32_t)(cb + p.N);
             tl += (double)Lr[k];
         }
         tl = wave_sum_f64(tl);
-        if (lane == 0) sm.tot[wave] = tl;
+        if (lane == 0 && act) sm.tot[wave] = tl;
         if (tid == 0) sm.pick[0] = -1;
         __syncthreads();
         const double tot = (sm.tot[0] + sm.tot[1]) + (sm.tot[2] + sm.tot[3]);
@@ -237,7 +268,7 @@ __device__ __forceinline__ bool attn_unit(const AttnParams &p, int u, bool recor
             if (k >= rounds) break;
             const uint32_t ns = (Lr[k] + sl - 1u) / sl;
             const uint32_t incl = wave_scan_u32(ns);
-            if (lane == 63) sm.red[par][wave] = incl;
+            if (lane == 63 && act) sm.red[par][wave] = incl;
             __syncthreads();
             uint32_t before = first + incl - ns;
             uint32_t all = 0;

@@ -131,6 +131,8 @@ hipError_t launch_attn_mfma(const AttnParams &p, int dtype, int D, int nt, int p
 hipError_t launch_attn_dma(const AttnParams &p, int D, int nt, int pg, bool q4, int occ, hipStream_t s);
 int attn_dma_max_split_pages();
 hipError_t launch_attn_q4c(const AttnParams &p, int nts, hipStream_t s);
+hipError_t launch_attn_q4w(const AttnParams &p, int nts, hipStream_t s);
+bool attn_q4w_supports(bool paged, int nts);
 int attn_q4c_max_split_pages();
 hipError_t launch_attn_valu(const AttnParams &p, int dtype, int D, hipStream_t s);
 hipError_t launch_attn_merge(const AttnParams &p, int D, hipStream_t s);

@@ -422,8 +422,13 @@ int sv_last_hip_error(void);
  *                    row tile per wave: 1 or 2 (half-size LDS rings, twice the
  *                    work units)
  *   attn_q4_kernel   4-bit caches of head dim 256 with >= 16 packed rows:
- *                    1 the cooperative fp16 matrix-core kernel (the default),
- *                    2 the pipelined kernel with bf16 staging
+ *                    1 the cooperative fp16 matrix-core kernel with four
+ *                    waves per workgroup, 2 the pipelined kernel with bf16
+ *                    staging, 3 the cooperative fp16 kernel with eight waves
+ *                    per workgroup (two per SIMD); 0 (default) and 3 take the
+ *                    eight-wave kernel where it applies (contiguous caches,
+ *                    and paged caches with up to 64 packed rows per block)
+ *                    and the four-wave one otherwise
  *   argmax_chunk     logits per argmax workgroup, a positive multiple of 8
  *                    (default 16384)
  * A value out of range makes the call return SV_EINVAL (the workspace-size

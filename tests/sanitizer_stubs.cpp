@@ -16,6 +16,8 @@ hipError_t launch_attn_dma(const AttnParams &, int, int, int, bool, int, hipStre
 int attn_dma_max_split_pages() { return 512; }
 hipError_t launch_attn_q4c(const AttnParams &, int, hipStream_t) { return ++g_stub_launches, hipSuccess; }
 int attn_q4c_max_split_pages() { return 512; }
+hipError_t launch_attn_q4w(const AttnParams &, int, hipStream_t) { return ++g_stub_launches, hipSuccess; }
+bool attn_q4w_supports(bool paged, int nts) { return nts >= 1 && nts <= (paged ? 2 : 3); }
 hipError_t launch_attn_valu(const AttnParams &, int, int, hipStream_t) { return ++g_stub_launches, hipSuccess; }
 hipError_t launch_attn_merge(const AttnParams &, int, hipStream_t) { return ++g_stub_launches, hipSuccess; }
 hipError_t launch_accept(const AcceptParams &, hipStream_t) { return ++g_stub_launches, hipSuccess; }

@@ -150,14 +150,15 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
 
 def q4_key_rounding(case, q4_kernel="cooperative"):
     """Relative rounding of a dequantised 4-bit key on the path the library
-    plans for the case: fp16 (2^-11) on the cooperative kernel (bf16 queries,
-    head dim 256, >= 16 packed rows), bf16 (2^-8) on the other matrix-core
-    kernels, none (fp32) on the vector-ALU kernel (< 16 rows)."""
+    plans for the case: fp16 (2^-11) on the cooperative kernels, four- or
+    eight-wave (bf16 queries, head dim 256, >= 16 packed rows), bf16 (2^-8) on
+    the other matrix-core kernels, none (fp32) on the vector-ALU kernel (< 16
+    rows)."""
     cfg = case.cfg
     rows = (cfg.n_q_heads // cfg.n_kv_heads) * cfg.n_nodes
     if rows < 16:
         return 0.0
-    if cfg.head_dim == 256 and q4_kernel == "cooperative":
+    if cfg.head_dim == 256 and q4_kernel in ("cooperative", "wide"):
         return 2.0 ** -11
     return 2.0 ** -8
 

@@ -246,7 +246,7 @@ def test_tuning_per_call(lib):
         return lib.sv_verify_attn_tuned_workspace_size(ctypes.byref(d), 1, 8, 24, 4096, 0, ctypes.byref(t))
     assert lib.sv_verify_attn_tuned_workspace_size(ctypes.byref(d), 1, 8, 24, 4096, 0, None) == base
     assert ws() == base
-    assert ws(attn_posgroups=3) == 0 and ws(attn_occupancy=3) == 0 and ws(attn_q4_kernel=3) == 0
+    assert ws(attn_posgroups=3) == 0 and ws(attn_occupancy=3) == 0 and ws(attn_q4_kernel=4) == 0
     assert ws(attn_target_wgs=-1) == 0 and ws(attn_rowblocks=-2) == 0 and ws(argmax_chunk=12) == 0
     more = ws(attn_target_wgs=4096)                 # more splits, more partials
     assert more > base

@@ -53,10 +53,16 @@ def test_kernels_use_no_scratch(tmp_path):
     assert not bad, bad
 
 
-def test_cooperative_kernel_owns_its_accumulation_registers(tmp_path):
-    """The cooperative 4-bit attention kernel keeps its O accumulators in
-    a0..a95 through inline assembly alone; the compiler must not place any
-    value of its own there (a spill or copy into them would corrupt O without
+@pytest.mark.parametrize("debug", [False, True], ids=["release", "debug"])
+@pytest.mark.parametrize("source,kernel,variants",
+                         [("attn_q4.hip", "attn_q4c_kernel", 6),      # 3 tile counts x (contiguous, paged)
+                          ("attn_q4w.hip", "attn_q4w_kernel", 5)])    # 3 contiguous, 2 paged
+def test_cooperative_kernel_owns_its_accumulation_registers(tmp_path, source, kernel, variants, debug):
+    """The cooperative 4-bit attention kernels keep values of their own in
+    a0..a95 through inline assembly alone (the four-wave kernel its O
+    accumulators; the eight-wave kernel its O accumulators in a0..a47 and its
+    query fragments in a48..a95); the compiler must not place any value of its
+    own there (a spill or copy into them would corrupt O or the scores without
     an error).  Compiled to assembly with the library's flags, every reference
     to a0..a95 in those kernels must sit inside an inline-assembly block."""
     import importlib.util
@@ -67,14 +73,14 @@ def test_cooperative_kernel_owns_its_accumulation_registers(tmp_path):
     spec.loader.exec_module(mod)
     if not os.path.exists(mod.HIPCC):
         pytest.skip("hipcc not found")
-    src = os.path.join(mod.CSRC, "attn_q4.hip")
-    out = tmp_path / "attn_q4.s"
-    flags = [f for f in mod.FLAGS if f not in ("-Wall",)] + mod.EXTRA.get("attn_q4.hip", [])
+    src = os.path.join(mod.CSRC, source)
+    out = tmp_path / (source + ".s")
+    flags = [f for f in mod.FLAGS if f not in ("-Wall",)] + mod.EXTRA.get(source, []) + (["-DSV_DEBUG"] if debug else [])
     subprocess.run([mod.HIPCC, *flags, "--cuda-device-only", "-S", src, "-o", str(out)], check=True,
                    capture_output=True)
     lines = out.read_text().split("\n")
-    starts = [i for i, l in enumerate(lines) if re.match(r"^_Z\S*attn_q4c_kernel\S*:", l)]
-    assert len(starts) == 6, len(starts)                 # 3 tile counts x (contiguous, paged)
+    starts = [i for i, l in enumerate(lines) if re.match(r"^_Z\S*" + kernel + r"\S*:", l)]
+    assert len(starts) == variants, len(starts)
     pinned = re.compile(r"\ba(\d+)\b|\ba\[(\d+):(\d+)\]")
     for s0 in starts:
         in_asm, bad, n_asm = False, [], 0

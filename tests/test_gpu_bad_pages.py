@@ -53,6 +53,7 @@ ATTN = [
     ("pipelined bf16 D128", 16, 4, 128, 4, "bf16", "bf16", "chain", 300, None),
     ("cooperative q4 D256", 24, 4, 256, 16, "bf16", "q4", "chain", 700, None),
     ("pipelined q4 D256", 24, 4, 256, 16, "bf16", "q4", "chain", 700, {"attn_q4_kernel": "pipelined"}),
+    ("eight-wave q4 D256", 24, 4, 256, 8, "bf16", "q4", "chain", 700, {"attn_q4_kernel": "wide"}),
     ("staged q4 D128", 16, 4, 128, 4, "bf16", "q4", "ddtree", 300, None),
     ("vector fp32 D64", 4, 2, 64, 3, "f32", "f32", "chain", 200, None),
 ]

@@ -232,14 +232,24 @@ Q4_KERNEL_CASES = [
     ("q4 paged tree 9 tiles", workloads.Config("pt9", 1, 24, 4, 256, 22, "bf16", "q4", "f32", 50, 900,
                                                tree="ddtree", paged=True, q_std=0.5, kv_std=0.5,
                                                draft_rule="tree"), {}, 0),
+    ("q4 paged chain 3 tiles", workloads.Config("pc3", 2, 24, 4, 256, 8, "bf16", "q4", "f32", 50, 1100,
+                                                ctx_hi=1500, paged=True, q_std=0.5, kv_std=0.5),
+     {"variant": "peaked"}, 0),
+    ("q4 contiguous 5 tiles ragged", workloads.Config("c5t", 1, 20, 4, 256, 15, "bf16", "q4", "f32", 50, 1333,
+                                                      tree="ddtree", q_std=0.5, kv_std=0.5,
+                                                      draft_rule="tree"), {}, 0),
+    ("q4 batch 70", workloads.Config("b70", 70, 8, 2, 256, 4, "bf16", "q4", "f32", 50, 60, ctx_hi=400,
+                                     q_std=0.5, kv_std=0.5), {"variant": "peaked"}, 0),
 ]
 
 
-@pytest.mark.parametrize("kernel", ["cooperative", "pipelined"])
+@pytest.mark.parametrize("kernel", ["cooperative", "pipelined", "wide"])
 @pytest.mark.parametrize("label,cfg,kw,window", Q4_KERNEL_CASES, ids=[c[0] for c in Q4_KERNEL_CASES])
 def test_attention_q4_kernels(sv, label, cfg, kw, window, kernel):
-    """Both kernels for 4-bit caches of head dim 256 (the cooperative fp16 one,
-    the default, and the pipelined bf16-staging one, chosen per call)."""
+    """The kernels for 4-bit caches of head dim 256, chosen per call: the
+    four-wave cooperative fp16 one, the pipelined bf16-staging one and the
+    eight-wave cooperative one (the default; it hands paged blocks of three row
+    tiles per wave pair to the four-wave one)."""
     say(f"[attn q4 kernel] {label} {kernel}")
     case = workloads.make_case(cfg, seed=77, capacity_pad=2, **kw)
     out, lse = DeviceCase(case).attn(window=window, tuning={"attn_q4_kernel": kernel})
@@ -282,6 +292,7 @@ FULL = [
     ("C3", None, None, "peaked"),
     ("C4", [0, 6, 12, 18, 23], None, ""),          # one query head of every KV head, and the last
     ("C4", [0, 6, 12, 18], None, "peaked"),
+    ("C4", [1, 7, 13, 23], None, "wide"),            # the eight-wave 4-bit kernel
     ("C5", None, None, ""),
 ]
 
@@ -296,13 +307,14 @@ def test_attention_full_size_sampled(sv, name, heads, batch, variant):
     cache's, so the tree mask decides an O(1) part of every output."""
     cfg = C[name]
     say(f"[attn-full] {cfg.name} heads={heads} batch={batch} variant={variant or 'plain'}")
-    case = workloads.make_case(cfg, seed=1, variant=variant)
+    tuning = {"attn_q4_kernel": "wide"} if variant == "wide" else None
+    case = workloads.make_case(cfg, seed=1, variant="" if variant == "wide" else variant)
     dc = DeviceCase(case)
-    out, lse = dc.attn()
+    out, lse = dc.attn(tuning=tuning)
     torch.cuda.synchronize()
     ma, rel, le = check_attention(case, out, lse, heads=heads, batch=batch)
     say(f"    max_abs={ma:.3g} rel={rel:.3g} lse={le:.3g}")
-    out2, lse2 = dc.attn()
+    out2, lse2 = dc.attn(tuning=tuning)
     torch.cuda.synchronize()
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
@@ -664,3 +676,30 @@ def test_verify_step_end_to_end(sv):
         for e, g in zip(exp, dc.cache_arrays_host()):
             np.testing.assert_array_equal(g[None], e)
         np.testing.assert_array_equal(new_lens.cpu().numpy(), r_new)
+
+
+def test_default_workspaces_are_per_stream(sv):
+    """The binding's default workspaces are keyed by (kind, device, stream):
+    calls on two streams never share one (a workspace serves one stream at a
+    time), and each stream's results match the oracle."""
+    case = workloads.make_case(_small("C3", ctx=300, vocab=3001), seed=31)
+    dc = DeviceCase(case)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    for s in (s1, s2):
+        with torch.cuda.stream(s):
+            o, l = sv.verify_attn(dc.kv, dc.q, dc.ctx, dc.parent, dc.max_ctx)
+            acc, path, tok, am = sv.greedy_accept(dc.logits, dc.drafts, dc.parent)
+            outs.append((o, l, acc, path))
+    torch.cuda.synchronize()
+    keys = [k for k in sv._ws_cache if k[2] in (s1.cuda_stream, s2.cuda_stream)]
+    assert {k[0] for k in keys} == {"attn", "accept"} and len(keys) == 4
+    by = {(k[0], k[2]): sv._ws_cache[k] for k in keys}
+    for kind in ("attn", "accept"):
+        assert by[(kind, s1.cuda_stream)].data_ptr() != by[(kind, s2.cuda_stream)].data_ptr()
+    r_am, r_acc, r_path, r_tok = oracle_accept(case)
+    for o, l, acc, path in outs:
+        check_attention(case, o, l)
+        np.testing.assert_array_equal(acc.cpu().numpy(), r_acc)
+        np.testing.assert_array_equal(path.cpu().numpy(), r_path)
