@@ -392,13 +392,16 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_q4w_kernel(AttnParams p) {
         for (int i = 0; i < NTS; ++i) sx_w[i * 64] = make_float2(sc[i][2], sc[i][3]);
     };
     // ... and adds the partner's share to its own values 0, 1
-    auto sx_take = [&](const f32x4 (&sc)[NTS], float (&s)[NTS][2]) {
+    auto sx_take = [&](const f32x4 (&sc)[NTS], const float2 (&o)[NTS], float (&s)[NTS][2]) {
 #pragma unroll
         for (int i = 0; i < NTS; ++i) {
-            const float2 o = sx_r[i * 64];
-            s[i][0] = sc[i][0] + o.x;
-            s[i][1] = sc[i][1] + o.y;
+            s[i][0] = sc[i][0] + o[i].x;
+            s[i][1] = sc[i][1] + o[i].y;
         }
+    };
+    auto sx_load = [&](float2 (&o)[NTS]) {
+#pragma unroll
+        for (int i = 0; i < NTS; ++i) o[i] = sx_r[i * 64];
     };
     // the halves of S over this wave's four k-steps; kf holds the fragments
     // of k-steps 0 and 1 on entry (a ring of two: each read goes out after the
@@ -441,7 +444,11 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_q4w_kernel(AttnParams p) {
         sx_put(sacc);
     }
     __syncthreads();
-    sx_take(sacc, s2);
+    {
+        float2 o[NTS];
+        sx_load(o);
+        sx_take(sacc, o, s2);
+    }
     apply_mask(0, s2);
 #pragma unroll
     for (int i = 0; i < NTS; ++i) row_max(s2[i][0], s2[i][1], i);
@@ -578,6 +585,11 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_q4w_kernel(AttnParams p) {
         __syncthreads();
 
         {
+            // the score halves first (the row maxima wait on them), then the
+            // operands of the P.V instructions and the codes of K(g + 2)
+            float2 sxo[NTS];
+            sx_load(sxo);
+            __builtin_amdgcn_sched_barrier(0);
             h8 vf[2];
             vf[0] = vread(0);
             vf[1] = vread(1);
@@ -588,7 +600,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_q4w_kernel(AttnParams p) {
             pf[0] = *(const h8 *)prd;
             pf[1] = *(const h8 *)(prd + 16 * PROW);
             float s2n[NTS][2];
-            sx_take(sacc_n, s2n);
+            sx_take(sacc_n, sxo, s2n);
             apply_mask(g + 1, s2n);
             bool grow = false;
 #pragma unroll
