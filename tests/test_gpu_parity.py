@@ -258,6 +258,47 @@ def test_attention_q4_kernels(sv, label, cfg, kw, window, kernel):
     check_attention(case, out, lse, ref=ref, key_rounding=q4_key_rounding(case, kernel))
 
 
+def _random_q4_cases(n, seed):
+    """Seeded random shapes for the 4-bit head-dim-256 kernels: 16-160 packed
+    rows (GQA groups 2-8, chains and trees), 1-5 sequences of 1-3000 cached
+    tokens, contiguous or paged (pages of 16 or 24), with or without a
+    window."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        hkv = int(rng.choice([1, 2, 4]))
+        g = int(rng.choice([2, 3, 4, 6, 8]))
+        n_nodes = int(rng.integers(max(1, -(-16 // g)), max(2, 160 // g) + 1))
+        n_nodes = min(n_nodes, 64)
+        tree = "ddtree" if rng.random() < 0.5 else "chain"
+        b = int(rng.integers(1, 6))
+        lo = int(rng.integers(1, 3000))
+        hi = int(min(3000, lo + rng.integers(0, 1500)))
+        paged = bool(rng.random() < 0.5)
+        window = int(rng.integers(64, 2500)) if rng.random() < 0.3 else 0
+        cfg = workloads.Config(f"rq{i}", b, hkv * g, hkv, 256, n_nodes, "bf16", "q4", "f32", 50, lo, ctx_hi=hi,
+                               tree=tree, paged=paged, page_size=int(rng.choice([16, 24])), q_std=0.5,
+                               kv_std=0.5, draft_rule="tree" if tree == "ddtree" else "geometric")
+        variant = "peaked" if rng.random() < 0.5 else ""
+        out.append((f"rq{i} B{b} {hkv * g}/{hkv} N{n_nodes} {tree} {lo}-{hi} {'paged' if paged else 'contig'}"
+                    f" W{window} {variant or 'plain'}", cfg, variant, window))
+    return out
+
+
+RANDOM_Q4 = _random_q4_cases(16, 2024)
+
+
+@pytest.mark.parametrize("label,cfg,variant,window", RANDOM_Q4, ids=[c[0] for c in RANDOM_Q4])
+def test_attention_q4_random_shapes(sv, label, cfg, variant, window):
+    """The default 4-bit plan (eight-wave kernel, or the four-wave one for
+    paged three-tile blocks) on seeded random shapes against the oracle."""
+    say(f"[attn q4 random] {label}")
+    case = workloads.make_case(cfg, seed=5, capacity_pad=2, variant=variant)
+    out, lse = DeviceCase(case).attn(window=window)
+    torch.cuda.synchronize()
+    check_attention(case, out, lse, ref=oracle.verify_attention(case, window=window))
+
+
 @pytest.mark.parametrize("edge", PLAN_EDGES, ids=[e[0] for e in PLAN_EDGES])
 def test_attention_plan_edges(sv, edge):
     """Launch plans on both sides of each planner threshold against the oracle."""
