@@ -21,7 +21,9 @@
 //                tile meet in LDS: each wave writes the two values of each
 //                of its lanes' four that its partner finishes and reads the
 //                partner's share of its own two, so that both waves of the
-//                pair take half of the softmax.
+//                pair take half of the softmax (the second half reads each
+//                group of four K rows in the order 2, 3, 0, 1, so that in both
+//                waves a lane's values 0, 1 are its own).
 //   O^T += V^T P^T  wave w owns head-dim slice [32 w, 32 w + 32) of every row
 //                tile.
 // The queries and O each take 48 registers at 96 rows (half of the
@@ -36,6 +38,12 @@
 // the next).  A stage's ring slot is refilled from the first chunk of the
 // stage after it, once the last codes read from it (V of its last chunk) are
 // behind a barrier.
+//
+// Online softmax: the references follow the four-wave kernel's lazy rule
+// (a reference moves only when a chunk's row maximum exceeds it by more than
+// 2^8).  A wave that finds one of its rows past that bound raises a flag in
+// LDS; the fast loop reads only the flag, the slow loop (which rescales O in
+// place) the published maxima.
 #include "attn_q4_common.h"
 
 namespace sv {

@@ -69,6 +69,19 @@ pdc.pt.copy_(torch.from_numpy(pt))
 out, lse = pdc.attn()
 report("bad_page_attn", bits=sv.check_device_errors(), finite=bool(torch.isfinite(out.float()).all()))
 report("after_clear", bits=sv.check_device_errors())
+
+# 4-bit head-dim-256 cache, paged, 48 packed rows: the eight-wave kernel
+qcfg = workloads.Config("q4 paged", 2, 24, 4, 256, 8, "bf16", "q4", "f32", 500, 300, ctx_hi=340, paged=True,
+                        q_std=0.5, kv_std=0.5)
+qcase = workloads.make_case(qcfg, seed=7, capacity_pad=2)
+qdc = DeviceCase(qcase)
+out, lse = qdc.attn()
+report("clean_q4", bits=sv.check_device_errors(), finite=bool(torch.isfinite(out.float()).all()))
+qpt = qcase.page_table.copy()
+qpt[1, 2] = qcase.k.shape[0] + 5                # outside the pool
+qdc.pt.copy_(torch.from_numpy(qpt))
+out, lse = qdc.attn()
+report("bad_page_attn_q4", bits=sv.check_device_errors(), finite=bool(torch.isfinite(out.float()).all()))
 '''
 
 
@@ -91,3 +104,5 @@ def test_debug_library_records_preconditions():
     assert steps["bad_accept_len"]["bits"] == PATH
     assert steps["bad_page_attn"]["bits"] == PAGE and steps["bad_page_attn"]["finite"]
     assert steps["after_clear"]["bits"] == 0
+    assert steps["clean_q4"]["bits"] == 0 and steps["clean_q4"]["finite"]
+    assert steps["bad_page_attn_q4"]["bits"] == PAGE and steps["bad_page_attn_q4"]["finite"]
