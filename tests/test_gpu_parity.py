@@ -285,7 +285,7 @@ def _random_q4_cases(n, seed):
     return out
 
 
-RANDOM_Q4 = _random_q4_cases(16, 2024)
+RANDOM_Q4 = _random_q4_cases(32, 2024)
 
 
 @pytest.mark.parametrize("label,cfg,variant,window", RANDOM_Q4, ids=[c[0] for c in RANDOM_Q4])
