@@ -138,9 +138,12 @@ typedef struct sv_kv_cache {
  * batch     at most 1024 (SV_EUNSUPPORTED beyond).  For batch > 1 the kernels
  *           choose the key-split length on the device from ctx_lens, so the
  *           work per workgroup follows the actual lengths rather than max_ctx.
- * Supported: q SV_BF16 with KV SV_BF16 or SV_Q4 (bf16 matrix cores when
- * (n_q_heads/n_kv_heads) * N >= 16 rows, vector ALU otherwise); q SV_F32 with
- * KV SV_F32, SV_BF16 or SV_Q4 (vector ALU, fp32 arithmetic).
+ * Supported: q SV_BF16 with KV SV_BF16 or SV_Q4 (matrix cores when
+ * (n_q_heads/n_kv_heads) * N >= 16 rows -- bf16, or fp16 for a 4-bit cache of
+ * head dim 256, whose values d * (n - 8) are then rounded to fp16 and whose
+ * query rows are scaled by a power of two into fp16's range; vector ALU
+ * otherwise); q SV_F32 with KV SV_F32, SV_BF16 or SV_Q4 (vector ALU, fp32
+ * arithmetic).
  */
 size_t sv_verify_attn_workspace_size(const sv_kv_cache *kv, int batch, int n_nodes,
                                      int n_q_heads, int max_ctx);
