@@ -174,7 +174,9 @@ __device__ __forceinline__ bool attn_unit(const AttnParams &p, int u, bool recor
         const int lo = L - (int)key_range(p, w.ctx);    // first key row (0 without a window)
         w.p0 = lo + w.s * p.split_len;
         if (w.p0 >= L) return false;
-        w.p1 = min(w.p0 + p.split_len, L);
+        // the last split also takes the keys past n_splits * split_len (a plan
+        // may leave a short remainder on it instead of a unit of its own)
+        w.p1 = w.s == p.n_splits - 1 ? L : min(w.p0 + p.split_len, L);
         w.part = u;
         return true;
     }

@@ -279,6 +279,39 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
         splits_for(B * Hkv * pl.n_rowblocks, pl.split_len, pl.n_splits);
     }
 
+    // One sequence: a key range a little over a multiple of the split length
+    // (ctx + N = 64 * 2048 + 16 for 16 draft rows after a 128K context) is
+    // rounded up to longer splits, or leaves a nearly empty last one.  For n
+    // splits from the planned count up to what the grid holds, splits of
+    // floor(L / n) (in whole quanta) whose last one also takes the remainder
+    // are used instead when that last split runs fewer chunks than the planned
+    // splits (the last split of a plan ends at the key range's end,
+    // attn_sched.h).  4-bit 16-row block at 131072 keys: 61 splits of 2176 ->
+    // 64 of 2048, the last 2064.
+    if (B == 1) {
+        const int64_t groups = (int64_t)Hkv * pl.n_rowblocks;
+        const int64_t n_cap = std::min<int64_t>(std::max<int64_t>(groups * pl.n_splits, target) / groups, kMaxSplits);
+        const int64_t chunk = (pl.kind == kMfmaDma && !q4) ? 32 * pl.pg : 32;
+        auto chunks = [&](int64_t len) { return ceil_div(len, chunk); };
+        // at least two stages per split: the per-split costs (prologue,
+        // partials, merge) outweigh one stage (4-bit, 8 rows at 8K: 36 -> 39 us)
+        const int64_t min_sl = 2 * std::max(squant, chunk);
+        int64_t best = chunks(pl.split_len), best_sl = 0, best_n = 0;
+        for (int64_t n = pl.n_splits; n <= n_cap; ++n) {
+            const int64_t sl = L / n / squant * squant;
+            if (sl < min_sl) break;
+            const int64_t last = L - (n - 1) * sl;           // >= sl
+            if (last > max_split || chunks(last) >= best) continue;
+            best = chunks(last);
+            best_sl = sl;
+            best_n = n;
+        }
+        if (best_n > 0) {
+            pl.split_len = (int)best_sl;
+            pl.n_splits = (int)best_n;
+        }
+    }
+
     int64_t units = (int64_t)B * Hkv * pl.n_splits;
     pl.dyn = B > 1;
     if (pl.dyn) {

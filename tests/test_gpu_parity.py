@@ -206,6 +206,12 @@ Q4_SINGLE = [
     ("q4 paged tree 9 tiles", 24, 4, 22, "ddtree", 900, True, 0),
     ("q4 paged one tile windowed", 8, 2, 4, "chain", 3000, True, 700),
     ("q4 contiguous 6 tiles windowed", 24, 4, 16, "chain", 2500, False, 1000),
+    # L a little over a multiple of the split: 64 splits of 256 keys, the last
+    # one also takes the remaining 16 (and, windowed, of the window's keys)
+    ("q4 last split takes the remainder", 24, 4, 16, "chain", 16384, False, 0),
+    ("q4 paged last split takes the remainder", 24, 4, 16, "chain", 16384, True, 0),
+    ("q4 tree last split takes the remainder", 24, 4, 22, "ddtree", 8192, False, 0),
+    ("q4 windowed last split takes the remainder", 24, 4, 16, "chain", 20000, False, 16400),
 ]
 
 
