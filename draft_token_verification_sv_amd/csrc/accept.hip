@@ -146,6 +146,49 @@ __global__ __launch_bounds__(256) void argmax_accept_kernel(AcceptParams p) {
             }
         };
         int64_t e = lo + (int64_t)tid * EPL;
+        if constexpr (!F32 && !SAMPLE) {
+            // bf16 greedy rows: each value becomes a 16-bit code with the
+            // order of its 64-bit key (negatives 0x8000 - |x|, -0 and +0 both
+            // 0x8000, positives 0x8000 + |x|), two per dword with packed 16-bit
+            // ops; a code and 127 - slot (slot = 8 k + t over the group's 16
+            // loads, in index order within the thread) make a 32-bit key whose
+            // maximum is the group's largest value at its lowest index, which
+            // then enters the 64-bit key: 3 to 4 vector ops per value instead of
+            // ~10.  All 16 loads of a group go out together (the default chunk,
+            // 32768 values, is one group); loads past the chunk's end reread its
+            // last 8 values and are left out of the maximum (the vector path
+            // has chunks and rows of whole 16-byte loads).
+            typedef short s16x2 __attribute__((ext_vector_type(2)));
+            typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+            constexpr int GL = 16;
+            for (; e < hi; e += (int64_t)GL * 256 * EPL) {
+                u32x4 v[GL];
+#pragma unroll
+                for (int k = 0; k < GL; ++k)
+                    v[k] = *(const u32x4 *)((const uint8_t *)base + min(e + (int64_t)k * 256 * EPL, hi - EPL) * 2);
+                uint32_t kb = 0u;
+#pragma unroll
+                for (int k = 0; k < GL; ++k) {
+                    uint32_t kk = 0u;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const uint32_t w = v[k][t];
+                        const uint32_t sg = __builtin_bit_cast(uint32_t, __builtin_bit_cast(s16x2, w) >> (short)15);
+                        const uint32_t o = __builtin_bit_cast(
+                            uint32_t, __builtin_bit_cast(u16x2, w ^ (sg | 0x80008000u)) - __builtin_bit_cast(u16x2, sg));
+                        const uint32_t k0 = (o << 16) | (uint32_t)(8 * GL - 1 - (8 * k + 2 * t));
+                        const uint32_t k1 = (o & 0xFFFF0000u) | (uint32_t)(8 * GL - 1 - (8 * k + 2 * t + 1));
+                        kk = max(kk, max(k0, k1));
+                    }
+                    kb = e + (int64_t)k * 256 * EPL < hi ? max(kb, kk) : kb;
+                }
+                const uint32_t slot = (uint32_t)(8 * GL - 1) - (kb & 0xFFFFu);
+                const uint32_t code = kb >> 16;
+                const uint32_t bits = code >= 0x8000u ? code - 0x8000u : (0x8000u | (0x8000u - code));
+                const uint32_t idx = (uint32_t)e + (slot >> 3) * (256u * EPL) + (slot & 7u);
+                best = umax64(best, make_key(bf16_bits_to_f32(bits), idx));
+            }
+        }
         for (; e + (int64_t)(UNR - 1) * 256 * EPL < hi; e += (int64_t)UNR * 256 * EPL) {
             u32x4 v[UNR];
             f32x4 gv[UNR][2];

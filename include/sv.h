@@ -433,7 +433,8 @@ int sv_last_hip_error(void);
  *                    and paged caches with up to 64 packed rows per block)
  *                    and the four-wave one otherwise
  *   argmax_chunk     logits per argmax workgroup, a positive multiple of 8
- *                    (default 16384)
+ *                    (0, the default: 32768 for greedy acceptance of bf16
+ *                    logits, 16384 otherwise)
  * A value out of range makes the call return SV_EINVAL (the workspace-size
  * query returns 0).  A workspace sized under one tuning may be too small
  * under another (the call then returns SV_EWORKSPACE).

@@ -441,6 +441,46 @@ def test_argmax_natural_and_planted_ties(sv):
     np.testing.assert_array_equal(tok.cpu().numpy(), r_tok)
 
 
+def test_argmax_signed_zero_and_negative_rows(sv):
+    """Rows whose maximum is a zero (-0 and +0 are equal: the lower index
+    wins), a negative value or the smallest negative subnormal, with the
+    deciding entries in full 16384-logit chunks and in the ragged last one."""
+    rng = np.random.default_rng(9)
+    B, N, V = 1, 12, 151936
+    bits = workloads.bf16_bits(-np.abs(rng.standard_normal((B, N, V)).astype(np.float32)) - np.float32(0.5))
+    P0, M0, MT = 0x0000, 0x8000, 0x8001            # +0, -0, -2^-133
+    plants = {0: [(5000, M0), (100, P0)],           # +0 first -> 100
+              1: [(3000, P0), (200, M0)],           # -0 first -> 200
+              2: [(70000, M0)],                     # a lone -0
+              3: [(V - 1, M0), (V - 7, P0)],        # zeros in the ragged chunk -> V - 7
+              4: [(40000, MT)],                     # the largest negative
+              5: [(10, MT), (20, M0)],              # -0 above -2^-133 -> 20
+              6: [(16383, P0), (16384, M0)],        # across a chunk boundary -> 16383
+              7: [(147455, MT), (147456, MT)]}      # last full chunk / ragged chunk tie -> 147455
+    for i, pl in plants.items():
+        for idx, b16 in pl:
+            bits[0, i, idx] = b16
+    bits[0, 8] = bits[0, 8, 0]                       # a flat row -> 0
+    bits[0, 9, [9000, 9001, 150000]] = workloads.bf16_bits(np.array([-0.25], np.float32))[0]
+    parent = workloads.ddtree_parent(rng, N)[None]
+    lg = oracle.widen_bf16(bits)
+    r_am = np.array([[oracle.argmax_first(lg[0, i]) for i in range(N)]])
+    assert list(r_am[0, :10]) == [100, 200, 70000, V - 7, 40000, 20, 16383, 147455, 0, 9000], r_am
+    drafts = workloads.drafts_from_targets(rng, parent[0], r_am[0], V, rng.random(N) < 0.8)[None]
+    import draft_token_verification_sv_amd as m
+    from sv_harness import dev_tensor
+    _, r_acc, r_path, r_tok = oracle.greedy_accept(lg, drafts, parent)
+    for chunk in (0, 8192, 2048 * 8 * 3):
+        acc, path, tok, am = m.greedy_accept(dev_tensor(bits, "bf16"), dev_tensor(drafts, "i32"),
+                                             dev_tensor(parent, "i32"),
+                                             tuning={"argmax_chunk": chunk} if chunk else None)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(am.cpu().numpy(), r_am)
+        np.testing.assert_array_equal(acc.cpu().numpy(), r_acc)
+        np.testing.assert_array_equal(path.cpu().numpy(), r_path)
+        np.testing.assert_array_equal(tok.cpu().numpy(), r_tok)
+
+
 def test_accept_repeated_calls_and_chunk_sizes(sv):
     """The workspace counters return to zero: many calls in a row, different
     shapes and chunk sizes, stay exact."""
