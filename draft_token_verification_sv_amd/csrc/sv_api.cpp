@@ -583,7 +583,7 @@ int accept_params(int batch, int n_nodes, int vocab, const void *logits, int log
     Tuning tu;
     if (!read_tuning(tuning, tu)) return SV_EINVAL;
     // logits per workgroup: greedy bf16 rows 32768 (one group of 16 loads per
-    // thread; C4's 16 rows of 151936: 9.0 -> 7.5 us with the 16-bit codes),
+    // thread; 16 rows of 151936: 9.0 -> 7.5 us with the 16-bit codes),
     // otherwise 16384
     if (tu.argmax_chunk == 0) tu.argmax_chunk = (!sampled && logits_dtype == SV_BF16) ? 32768 : 16384;
     if (batch < 1 || n_nodes < 1 || n_nodes > 64 || vocab < 1) return SV_EINVAL;
