@@ -212,6 +212,7 @@ Q4_SINGLE = [
     ("q4 paged last split takes the remainder", 24, 4, 16, "chain", 16384, True, 0),
     ("q4 tree last split takes the remainder", 24, 4, 22, "ddtree", 8192, False, 0),
     ("q4 windowed last split takes the remainder", 24, 4, 16, "chain", 20000, False, 16400),
+    ("q4 two row blocks, last split takes the remainder", 2, 1, 64, "ddtree", 65536, False, 0),
 ]
 
 
