@@ -109,6 +109,20 @@ def test_attention_workspace_size(lib):
     assert nb >= 2 * 64 * 4 * 48 * (256 + 2) * 4 + 64 * 16 and nb % 256 == 0
 
 
+def test_split_plan_keeps_the_grid_for_a_short_remainder(lib):
+    """One sequence over a 4-bit cache (24/4 heads, 16 rows, head dim 256):
+    a key range 16 keys over 64 * 2048 keeps 64 splits per KV head (the last
+    split takes the 16), so its partial slots equal those of exactly 64 * 2048
+    keys; the plan that rounds every split up to the 128-key stage would have
+    61 splits (fewer slots)."""
+    d = kv(dtype=2, k_scale=FAKE + 0x200000, v_scale=FAKE + 0x300000, capacity=140000)
+    exact = lib.sv_verify_attn_workspace_size(ctypes.byref(d), 1, 16, 24, 131072 - 16)
+    over = lib.sv_verify_attn_workspace_size(ctypes.byref(d), 1, 16, 24, 131072)
+    assert exact > 0 and over == exact
+    per_split = 4 * 96 * (256 + 2) * 4          # O and (m, l) of 96 rows, four KV heads
+    assert over >= 64 * per_split and over < 65 * per_split
+
+
 def test_accept_checks_and_workspace(lib):
     n = lib.sv_greedy_accept_workspace_size(1, 8, 151936)
     # one 64-bit key per row, one counter per sequence
