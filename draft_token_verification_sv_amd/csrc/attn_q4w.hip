@@ -242,46 +242,66 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_q4w_kernel(AttnParams p) {
         if (j == 0) issue(st);
     };
 
-    // ---- prologue: stage 0, the queries, stage 1 --------------------------------
-    issue(0);
-
+    // ---- prologue: the queries, then stages 0 and 1 ---------------------------------
+    // The query loads go out first (behind every workgroup's stage 0 they
+    // landed ~6 us after issue on the 131072-key block).  A wave loads only
+    // its head-dim half of its rows; the row's scale comes from both halves'
+    // maxima, exchanged with the partner wave (w ^ 4) through the score-half
+    // buffer, which is free until the first chunk.
     const int row0 = rb * p.rows_per_block;
     const int rows_here = min(p.rows_per_block, R - row0);
     // S rows of this lane: tile hh * NTS + i, row l16; query fragments of the
     // head-dim half dh go to QTile<4 i + k>
     float sl2[NTS];
     int node_of[NTS];
+    bf16x8 raw[NTS][4];
+    float amax[NTS];
 #pragma unroll
     for (int i = 0; i < NTS; ++i) {
         const int rl = 16 * (hh * NTS + i) + l16;
         const bool ok = rl < rows_here;
         const int r = row0 + rl;
         node_of[i] = ok ? r / G : -1;
-        bf16x8 raw[8];
         if (ok) {
             const int n = r / G, g = r % G;
-            const __bf16 *qp = (const __bf16 *)p.q + (((int64_t)b * N + n) * p.Hq + (int64_t)kvh * G + g) * D + qd * 8;
+            const __bf16 *qp = (const __bf16 *)p.q + (((int64_t)b * N + n) * p.Hq + (int64_t)kvh * G + g) * D +
+                               128 * dh + qd * 8;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) raw[k] = *(const bf16x8 *)(qp + 32 * k);
+            for (int k = 0; k < 4; ++k) raw[i][k] = *(const bf16x8 *)(qp + 32 * k);
         } else {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
+            for (int k = 0; k < 4; ++k) {
                 const bf16x8 z = {};
-                raw[k] = z;
+                raw[i][k] = z;
             }
         }
-        // row maximum magnitude over all 256 values (the lanes l16 + 16 qd)
-        float amax = 0.f;
+    }
+    // row maximum magnitude over this half (the lanes l16 + 16 qd), then over
+    // both halves
+    float *qx = sxb;                                   // [wave][tile][row l16]
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
+    for (int i = 0; i < NTS; ++i) {
+        float a = 0.f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf((float)raw[k][j]));
-        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf((float)raw[i][k][j]));
+        a = fmaxf(a, __shfl_xor(a, 16, 64));
+        a = fmaxf(a, __shfl_xor(a, 32, 64));
+        amax[i] = a;
+        if (qd == 0) qx[(wave * NTS + i) * 16 + l16] = a;
+    }
+    // stages 0 and 1 go out while the other waves' queries land
+    issue(0);
+    if (n_st > 1) issue(1);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NTS; ++i) {
+        const float a = fmaxf(amax[i], qx[((wave ^ 4) * NTS + i) * 16 + l16]);
         // 2^kq * amax in [2^14, 2^15): frexp gives amax = m 2^e, m in [0.5, 1)
         int kq = 0;
-        if (amax > 0.f) {
-            kq = 15 - __builtin_amdgcn_frexp_expf(amax);
+        if (a > 0.f) {
+            kq = 15 - __builtin_amdgcn_frexp_expf(a);
             kq = kq > 100 ? 100 : (kq < -110 ? -110 : kq);
         }
         sl2[i] = ldexpf(p.scale_log2, -kq);
@@ -290,7 +310,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_q4w_kernel(AttnParams p) {
         for (int k = 0; k < 4; ++k) {
             // slot j holds value pi(j), pi = (0, 4, 2, 6, 1, 5, 3, 7)
             const int pi[8] = {0, 4, 2, 6, 1, 5, 3, 7};
-            const bf16x8 src = dh ? raw[4 + k] : raw[k];
+            const bf16x8 src = raw[i][k];
 #pragma unroll
             for (int j = 0; j < 8; ++j) qv[k][j] = (_Float16)ldexpf((float)src[pi[j]], kq);
         }
@@ -299,7 +319,6 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_q4w_kernel(AttnParams p) {
             if (J / 4 == i) QTile<J>::load(qv[J % 4]);
         });
     }
-    if (n_st > 1) issue(1);
 
     // O^T tile (row tile t, head-dim tile dt of this wave) = OTile<2 t + dt>
     static_for<0, 2 * RB>([&](auto ic) { OTile<decltype(ic)::value>::zero(); });
