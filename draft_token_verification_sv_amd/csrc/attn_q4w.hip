@@ -692,15 +692,13 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_q4w_kernel(AttnParams p) {
             constexpr int dt = decltype(dc)::value;
             const f32x4 o = OTile<2 * t + dt>::read();
             if (rl >= rows_here) return;
-            // slot s = 32 wave + 16 dt + 4 qd + j holds head-dim 8 (s / 8) + pi(s % 8)
+            // the four values of slots s0 .. s0 + 3 in one 16-byte store, the row
+            // left in slot order (slot s holds head dim 8 (s / 8) + pi(s % 8),
+            // pi = 0, 4, 2, 6, 1, 5, 3, 7; the merge restores the order): four
+            // scattered 4-byte stores per value group kept every workgroup's
+            // last ~5 us on issuing them
             const int s0 = 32 * wave + 16 * dt + 4 * qd;
-            const int base = s0 & ~7;
-            const int odd = (s0 >> 2) & 1;               // slots 4..7 of the group of 8
-            // pi(0..3) = 0, 4, 2, 6;  pi(4..7) = 1, 5, 3, 7
-            op[base + (odd ? 1 : 0)] = o[0];
-            op[base + (odd ? 5 : 4)] = o[1];
-            op[base + (odd ? 3 : 2)] = o[2];
-            op[base + (odd ? 7 : 6)] = o[3];
+            *(f32x4 *)(op + s0) = o;
         });
     });
     if (pt == 0 && dh == 0 && qd == 0) {

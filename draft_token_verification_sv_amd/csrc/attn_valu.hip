@@ -298,6 +298,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
     if (sg > 0) return;
 #pragma unroll
     for (int k = 0; k < NSG - 1; ++k) acc += acc_s[k][c];
+    if (p.part_perm) {
+        // slots 4c .. 4c + 3 hold head dims 8 (c / 2) + (0, 4, 2, 6) for even c,
+        // (1, 5, 3, 7) for odd c: with the neighbour's four each lane has its
+        // four consecutive dims 4c .. 4c + 3
+        const f32x4 o = {__shfl_xor(acc[0], 1, 64), __shfl_xor(acc[1], 1, 64), __shfl_xor(acc[2], 1, 64),
+                         __shfl_xor(acc[3], 1, 64)};
+        acc = (c & 1) == 0 ? f32x4{acc[0], o[0], acc[2], o[2]} : f32x4{o[1], acc[1], o[3], acc[3]};
+    }
     const float inv = 1.f / lsum;
     const int64_t oi = (((int64_t)b * p.N + n) * p.Hq + h) * D + 4 * c;
     if (p.q_f32) {

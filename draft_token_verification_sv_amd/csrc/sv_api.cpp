@@ -446,6 +446,7 @@ int verify_attn(const sv_kv_cache *kv, int batch, int n_nodes, int n_q_heads, co
     // write back from L2 when the split kernel ends, which the merge waits for.
     // Large ones stay cached for the merge (measured: 6 MB -1 us, 34 MB +3 us).
     p.part_nt = pl.ml_off <= ((size_t)8 << 20);
+    p.part_perm = pl.kind == kQ4Coop;
     p.err = device_error_word();
 
     hipStream_t st = (hipStream_t)stream;

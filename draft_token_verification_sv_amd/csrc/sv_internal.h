@@ -42,6 +42,8 @@ struct AttnParams {
     float scale_log2;             // sm_scale * log2(e)
     int q_f32;                    // 1: q/out are fp32, 0: bf16
     int part_nt;                  // 1: streaming (non-temporal) stores for the partial O
+    int part_perm;                // 1: partial O in the 4-bit kernels' slot order: slot s of a
+                                  // row holds head dim 8 (s / 8) + pi(s % 8), pi = 0,4,2,6,1,5,3,7
     int window;                   // > 0: only the last `window` key rows of each sequence
     unsigned int *err;            // precondition word (SV_DEBUG builds), else nullptr
 };
