@@ -66,19 +66,31 @@ __device__ int walk_sequence(const AcceptParams &p, int b, int lane, int *am_s, 
     __builtin_amdgcn_s_waitcnt(0);           // the LDS writes of all lanes (one wave: no barrier)
     __builtin_amdgcn_wave_barrier();
 
-    // node `lane`: accepted iff every edge of its root path is accepted
-    int acc = 0, depth = 0;
-    if (lane < N) {
-        acc = 1;
-        int j = lane;
-#pragma unroll 1
-        for (int step = 0; step < 64 && j > 0; ++step) {
-            const int pj = par_s[j];
-            if (pj < 0 || pj >= j) { acc = 0; break; }
-            if (dr_s[j] != am_s[pj]) acc = 0;
-            ++depth;
-            j = pj;
-        }
+    // node `lane`: accepted iff every edge of its root path is accepted (the
+    // edge parent -> i: a valid parent, parent[i] < i, whose argmax is the
+    // draft of i).  The root paths are combined by pointer doubling instead of
+    // walked one step at a time: after round k each node knows the AND of its
+    // edges' acceptance, its depth and its ancestor set over its first 2^k
+    // ancestors; six rounds cover the 63 edges of the deepest tree.  An
+    // invalid edge ends its node's path at the root and rejects the node.
+    const bool node = lane < N;
+    const int pj = node ? par_s[lane] : 0;
+    const bool valid = node && lane > 0 && pj >= 0 && pj < lane;
+    const int am_parent = __shfl(node ? am_s[lane] : 0, valid ? pj : 0, 64);
+    int up = valid ? pj : 0;
+    int acc = !node ? 0 : (lane == 0 ? 1 : (valid && dr_s[lane] == am_parent ? 1 : 0));
+    int depth = valid ? 1 : 0;
+    unsigned long long anc = node ? (1ull << lane) : 0ull;
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+        const int acc_u = __shfl(acc, up, 64);
+        const int dep_u = __shfl(depth, up, 64);
+        const unsigned long long anc_u = __shfl(anc, up, 64);
+        const int up_u = __shfl(up, up, 64);
+        acc &= acc_u;
+        depth += dep_u;
+        anc |= anc_u;
+        up = up_u;
     }
     // deepest accepted node, ties to the smallest index (node 0 always qualifies)
     unsigned int key = acc ? (((unsigned)depth << 8) | (unsigned)(255 - lane)) : 0u;
@@ -87,16 +99,17 @@ __device__ int walk_sequence(const AcceptParams &p, int b, int lane, int *am_s, 
     const int best_node = 255 - (int)(key & 255u);
     const int a = (int)(key >> 8);
 
+    // the path: the ancestors of the best node (itself included), each at its
+    // depth; the tokens: their drafts, then the best node's argmax
+    const unsigned long long on_path = __shfl(anc, best_node, 64);
     int32_t *path = p.path + (int64_t)b * N;
     int32_t *tok = p.tokens + (int64_t)b * N;
+    if (node && ((on_path >> lane) & 1ull)) {
+        path[depth] = lane;
+        if constexpr (PATH_LDS) path_s[depth] = lane;
+        if (depth > 0) tok[depth - 1] = dr_s[lane];
+    }
     if (lane == 0) {
-        int j = best_node;
-        for (int d = a; d >= 0; --d) {
-            path[d] = j;
-            if constexpr (PATH_LDS) path_s[d] = j;
-            if (d > 0) tok[d - 1] = dr_s[j];
-            j = (j > 0) ? par_s[j] : 0;
-        }
         tok[a] = am_s[best_node];
         p.accept_len[b] = a;
     }
