@@ -190,42 +190,28 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
 
 // Split merge: one block of 256 threads per output row.  Thread t covers the 4
 // columns 4 (t % (D/4)) .. +3 of the splits s = t / (D/4) (mod NSG), NSG =
-// 1024 / D split groups, with 16-byte loads.  The first OB partial rows of each
-// thread go out together with the (m, l) loads; the block then finds
-// M = max_s m_s and the weights 2^(m_s - M) (kept in LDS), every thread
-// accumulates its weighted partials, and the split groups add up through LDS.
-// Slots past the sequence's splits (not written by this call) are never read.
+// 1024 / D split groups, with 16-byte loads.  Each wavefront loads the (m, l)
+// pairs of all splits, then the first OB partial rows of each thread; it finds
+// M = max_s m_s and the weights 2^(m_s - M) (kept in its own LDS copy) by lane
+// shuffles while the rows land, every thread accumulates its weighted
+// partials, and the split groups add up through LDS (the one block barrier).
+// Slots past the sequence's splits (not written by this call) are never used.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
     constexpr int CG = D / 4;               // column groups of one row
     constexpr int NSG = 256 / CG;           // split groups
     constexpr int OB = 16;                  // partial rows in flight per thread
-    __shared__ float w_s[kMaxSplits];
-    __shared__ float red[8];
+    __shared__ float w_s[4][kMaxSplits];            // split weights, one copy per wavefront
     __shared__ f32x4 acc_s[NSG - 1][CG];
     const int tid = threadIdx.x;
     const int c = tid % CG, sg = tid / CG;
+    const int lane = tid & 63, wave = tid >> 6;
     const int row = blockIdx.x;
     const int h = row % p.Hq;
     const int n = (row / p.Hq) % p.N;
     const int b = row / (p.Hq * p.N);
     const int kvh = h / p.G, g = h % p.G;
     const int r = n * p.G + g;
-    // block-wide reduction (max or sum)
-    auto block_reduce = [&](float v, bool is_max) -> float {
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-            const float o = __shfl_xor(v, m, 64);
-            v = is_max ? fmaxf(v, o) : v + o;
-        }
-        __syncthreads();                             // red[] free again
-        if ((tid & 63) == 0) red[tid >> 6] = v;
-        __syncthreads();
-        float a = red[0];
-#pragma unroll
-        for (int k = 1; k < 4; ++k) a = is_max ? fmaxf(a, red[k]) : a + red[k];
-        return a;
-    };
     // first partial slot and split count of (b, kvh); the static schedule
     // knows the slots without the context length, so the loads start together
     // with the ctx_lens load
@@ -241,6 +227,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
         const int L = (int)key_range(p, ctx_of(p.ctx_lens, b, p.max_ctx, p.err));
         ns = min(p.n_splits, (L + p.split_len - 1) / p.split_len);
     }
+    // every wavefront reads all (m, l) pairs itself (one per lane up to 64
+    // splits), before the partial rows: the maximum and the weights are then
+    // formed while the rows are still in flight, with no workgroup barrier
+    const float2 *ml = (const float2 *)p.part_ml + base * p.R + r;
+    const float2 ml0 = lane < ns_cap ? ml[(int64_t)lane * p.R] : make_float2(-INFINITY, 0.f);
     const float *op = p.part_o + (base * p.R + r) * D + 4 * c;
     const int64_t sstride = (int64_t)p.R * D;
     f32x4 ov[OB];
@@ -249,36 +240,36 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
         const int sp = sg + k * NSG;
         ov[k] = sp < ns_cap ? *(const f32x4 *)(op + sp * sstride) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const float2 *ml = (const float2 *)p.part_ml;
-    constexpr int MLR = kMaxSplits / 256;           // (m, l) pairs per thread (upper bound)
-    float2 mlv[MLR];
+    float M = lane < ns ? ml0.x : -INFINITY;
+    for (int j = 64 + lane; j < ns; j += 64) M = fmaxf(M, ml[(int64_t)j * p.R].x);
 #pragma unroll
-    for (int k = 0; k < MLR; ++k) {
-        const int sp = tid + k * 256;
-        mlv[k] = sp < ns_cap ? ml[(base + sp) * p.R + r] : make_float2(-INFINITY, 0.f);
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < MLR; ++k)
-        if (tid + k * 256 < ns) mx = fmaxf(mx, mlv[k].x);
-    const float M = block_reduce(mx, true);
+    for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
+    float *w_w = w_s[wave];
     float ls = 0.f;
-#pragma unroll
-    for (int k = 0; k < MLR; ++k) {
-        const int sp = tid + k * 256;
-        if (sp < ns) {
-            const float w = (mlv[k].x == -INFINITY) ? 0.f : exp2f(mlv[k].x - M);
-            w_s[sp] = w;
-            ls += w * mlv[k].y;
-        }
+    if (lane < ns) {
+        const float w = ml0.x == -INFINITY ? 0.f : exp2f(ml0.x - M);
+        w_w[lane] = w;
+        ls = w * ml0.y;
     }
-    const float lsum = block_reduce(ls, false);     // (its barriers also publish w_s)
+    for (int j = 64 + lane; j < ns; j += 64) {
+        const float2 t = ml[(int64_t)j * p.R];
+        const float w = t.x == -INFINITY ? 0.f : exp2f(t.x - M);
+        w_w[j] = w;
+        ls += w * t.y;
+    }
+    float lsum = ls;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) lsum += __shfl_xor(lsum, m, 64);
+    // the weights were written by other lanes of this wavefront
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < OB; ++k) {
         const int sp = sg + k * NSG;
-        if (sp < ns) acc += w_s[sp] * ov[k];
+        if (sp < ns) acc += w_w[sp] * ov[k];
     }
 #pragma unroll 1
     for (int s0 = OB * NSG; s0 < ns; s0 += OB * NSG) {
@@ -290,7 +281,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
 #pragma unroll
         for (int k = 0; k < OB; ++k) {
             const int sp = s0 + sg + k * NSG;
-            if (sp < ns) acc += w_s[sp] * ov[k];
+            if (sp < ns) acc += w_w[sp] * ov[k];
         }
     }
     if (sg > 0) acc_s[sg - 1][c] = acc;
