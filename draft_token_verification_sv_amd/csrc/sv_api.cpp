@@ -169,8 +169,9 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
         pl.occ = 2;
         pl.pg = std::min(pl.pg, std::max(1, std::min(2, 32768 / (128 * D))));
         // a batch and the regrouped blocks fill two workgroups per CU; a short
-        // single sequence keeps the one-per-CU grid
-        const bool keep_grid = planned && B == 1 && !single_pair;
+        // single sequence keeps the one-per-CU grid (regrouped blocks too:
+        // 24/4 heads, dim 256, 16-row chain at 4K keys 22.5 -> 18.8 us)
+        const bool keep_grid = planned && B == 1 && (!single_pair || single_short);
         if (tu.attn_target_wgs == 0 && !keep_grid) target = 512;
     };
 
@@ -242,6 +243,16 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
             const bool single_pair = pl.kind == kMfmaDma && !q4 && B == 1 && RT > 4 && L > 4096 && L <= 65536 &&
                                      tu.attn_rowblocks == 0 && tu.attn_occupancy != 1;
             if (single_pair) nrb = (RT + 3) / 4;
+            // One short sequence (<= 5K keys) of at most four row tiles: one
+            // tile per block, so each block's wavefront runs alone on its
+            // SIMD with the split's stages to itself and the splits stay long
+            // (24/4 heads, dim 256, 8-row chain: 1K 12.7 -> 11.4 us, 4K 15.2
+            // -> 14.8 us, but 6K 16.0 -> 16.3 us; 4-row chain at 4K 15.7 ->
+            // 12.7 us)
+            const bool single_short = B == 1 && L <= 6144;
+            if (pl.kind == kMfmaDma && !q4 && B == 1 && L <= 5120 && RT <= 4 && tu.attn_rowblocks == 0 &&
+                tu.attn_occupancy != 1)
+                nrb = RT;
             // More row blocks (each reads the same KV tiles, from L2 after the
             // first) shorten the per-split work but multiply the splits, whose
             // fp32 partials the merge reads back.  Added while the partials
@@ -267,7 +278,7 @@ AttnPlan plan_attn(int kv_dtype, int q_dtype, int D, int B, int N, int Hq, int H
                 const int pg_rows = tpb == 1 ? 4 : (tpb == 2 ? 2 : 1);
                 pl.pg = std::min(std::min(tu.attn_posgroups, pg_rows), std::min(4, 65536 / (128 * D)));
             }
-            occupancy2(single_pair, B == 1 && L <= 6144);
+            occupancy2(single_pair, single_short);
             splits_for(B * Hkv * pl.n_rowblocks, pl.split_len, pl.n_splits);
             whole_stages(B * Hkv * pl.n_rowblocks);
         }
