@@ -254,7 +254,10 @@ __global__ __launch_bounds__(256, OCC) void attn_dma_kernel(AttnParams p) {
                 }
             }
         } else {
+            // all page-id reads first: each DMA statement orders memory, so a
+            // read placed between two of them would be waited for alone
             const int ps = p.kv.page_size;
+            const uint8_t *src[C::LPW];
 #pragma unroll
             for (int j = 0; j < C::LPW; ++j) {
                 const int jj = Q4 ? j : 0;
@@ -273,9 +276,10 @@ __global__ __launch_bounds__(256, OCC) void attn_dma_kernel(AttnParams p) {
                 const int pg = pages_s[pq - first_page];
                 const int64_t ri = ((int64_t)pg * p.Hkv + kvh) * ps + pr;
                 // a page outside the pool reads the zero row
-                const uint8_t *src = pg < 0 ? zero_row + col : dma_gb[jj] + (ri << rsh) + col;
-                dma16(__builtin_amdgcn_readfirstlane(slot + (uint32_t)(j * 1024)), src);
+                src[j] = pg < 0 ? zero_row + col : dma_gb[jj] + (ri << rsh) + col;
             }
+#pragma unroll
+            for (int j = 0; j < C::LPW; ++j) dma16(__builtin_amdgcn_readfirstlane(slot + (uint32_t)(j * 1024)), src[j]);
         }
     };
     // instruction j of full stage st of a contiguous cache

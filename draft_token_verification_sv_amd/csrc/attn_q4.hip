@@ -156,7 +156,10 @@ __global__ __launch_bounds__(256, 1) void attn_q4c_kernel(AttnParams p) {
                 }
             }
         } else {
+            // all page-id reads first: each DMA statement orders memory, so a
+            // read placed between two of them would be waited for alone
             const int ps = p.kv.page_size;
+            const uint8_t *src[LPW];
 #pragma unroll
             for (int j = 0; j < LPW; ++j) {
                 const int rsh = dma_rsh[j];
@@ -166,8 +169,10 @@ __global__ __launch_bounds__(256, 1) void attn_q4c_kernel(AttnParams p) {
                 const int pq = pos / ps, pr = pos - pq * ps;
                 const int pg = pages_s[pq - first_page];
                 const int64_t ri = pg < 0 ? 0 : ((int64_t)pg * p.Hkv + kvh) * ps + pr;
-                dma16(__builtin_amdgcn_readfirstlane(slot + (uint32_t)(j * 1024)), dma_gb[j] + (ri << rsh) + col);
+                src[j] = dma_gb[j] + (ri << rsh) + col;
             }
+#pragma unroll
+            for (int j = 0; j < LPW; ++j) dma16(__builtin_amdgcn_readfirstlane(slot + (uint32_t)(j * 1024)), src[j]);
         }
     };
 

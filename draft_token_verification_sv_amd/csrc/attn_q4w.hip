@@ -208,20 +208,24 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_q4w_kernel(AttnParams p) {
                 }
             }
         } else {
+            // all page-id reads first: each DMA statement orders memory, so a
+            // read placed between two of them would be waited for alone
             const int ps = p.kv.page_size;
+            const uint8_t *src[WL];
 #pragma unroll
             for (int j = 0; j < WL; ++j) {
-                if (j >= n_dma) continue;
                 const int rsh = dma_rsh[j];
                 const int row = (int)(dma_off(j) >> rsh);
                 const uint32_t col = dma_off(j) & ((1u << rsh) - 1u);
                 const int pos = min(tb + row, p1 - 1);
                 const int pq = pos / ps, pr = pos - pq * ps;
-                const int pg = pages_s[pq - first_page];
+                const int pg = j < n_dma ? pages_s[pq - first_page] : 0;
                 const int64_t ri = pg < 0 ? 0 : ((int64_t)pg * p.Hkv + kvh) * ps + pr;
-                const uint8_t *src = (pg < 0 && rsh == 4) ? zero_scales : dma_gb[j] + (ri << rsh) + col;
-                dma16(__builtin_amdgcn_readfirstlane(slot + (uint32_t)(j * 1024)), src);
+                src[j] = (pg < 0 && rsh == 4) ? zero_scales : dma_gb[j] + (ri << rsh) + col;
             }
+#pragma unroll
+            for (int j = 0; j < WL; ++j)
+                if (j < n_dma) dma16(__builtin_amdgcn_readfirstlane(slot + (uint32_t)(j * 1024)), src[j]);
         }
     };
 
